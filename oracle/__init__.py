@@ -1,0 +1,133 @@
+"""Float64 CPU oracle for the BCQ product -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import or call this package.  The library and its Python
+binding never do: there is no CPU fallback anywhere in the product path.
+
+The arithmetic lives in ``bcq_oracle.c`` (plain C loops in float64, see its
+header for the definitions it follows and the page passages it cites).  This
+module compiles it with the host C compiler when no built copy is present and
+marshals NumPy arrays to it.  Inputs are converted to float64 exactly (every
+fp16 and fp32 value is a float64 value).
+
+Parity status: every function here is pinned by ``tests/test_oracle.py``
+(worked example from the BiLoCo page, dense dequantise-then-matmul, brute force
+over all sign patterns, closed forms, prefix invariant, linearity).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bcq_oracle.c")
+_LIB = os.path.join(_HERE, "libbcq_oracle.so")
+_lib: Optional[ctypes.CDLL] = None
+
+__all__ = ["build", "gemv", "gemv_requests", "dequant", "sign_at"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into ``oracle/libbcq_oracle.so`` and return its path."""
+    global _lib
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(
+            ["gcc", "-O2", "-std=c99", "-shared", "-fPIC", "-o", tmp, _SRC],
+            check=True,
+        )
+        os.replace(tmp, _LIB)
+        _lib = None
+    return _LIB
+
+
+def _load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        # BCQ_ORACLE_LIB points at a deliberately broken build of bcq_oracle.c;
+        # only the mutation test sets it, to prove the pins catch such mistakes.
+        path = os.environ.get("BCQ_ORACLE_LIB")
+        if path is None:
+            if not os.path.exists(_LIB):
+                build(force=False)
+            path = _LIB
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        lib.bcq_oracle_gemv.argtypes = [P, i, i, i, i, i, P, P, P, P]
+        lib.bcq_oracle_gemv.restype = None
+        lib.bcq_oracle_dequant.argtypes = [P, i, i, i, i, i, P, P, P]
+        lib.bcq_oracle_dequant.restype = None
+        lib.bcq_oracle_sign_at.argtypes = [P, i, i, i, i, i]
+        lib.bcq_oracle_sign_at.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _u32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.uint32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def gemv(signs, alpha, zero, x, p: int, g: int = 128) -> np.ndarray:
+    """One request at precision ``p``.
+
+    ``signs`` uint32 [P][M][ceil(K/32)]; ``alpha`` [>=p][M][G] (planes beyond p
+    are ignored); ``zero`` [M][G]; ``x`` [K].  Returns float64 ``y`` [M].
+    """
+    signs = _u32(signs)
+    P, M, _ = signs.shape
+    x = _f64(x).reshape(-1)
+    K = x.shape[0]
+    if K % g or not (1 <= p <= P):
+        raise ValueError("bad K/g or p")
+    a = _f64(np.asarray(alpha)[:p])
+    z = _f64(zero)
+    G = K // g
+    if a.shape != (p, M, G) or z.shape != (M, G):
+        raise ValueError("alpha/zero shapes do not match")
+    y = np.empty(M, dtype=np.float64)
+    _load().bcq_oracle_gemv(_ptr(signs), P, M, K, g, p, _ptr(a), _ptr(z), _ptr(x), _ptr(y))
+    return y
+
+
+def gemv_requests(signs, x, p_req: Sequence[int], alpha_for, zero_for, g: int = 128) -> np.ndarray:
+    """Several requests, each at its own precision.
+
+    ``x`` [b][K]; ``p_req`` [b]; ``alpha_for(p)`` / ``zero_for(p)`` return the
+    tables used at precision ``p``.  Returns float64 ``y`` [b][M].
+    """
+    x = np.asarray(x)
+    out = [gemv(signs, alpha_for(int(p)), zero_for(int(p)), x[r], int(p), g)
+           for r, p in enumerate(p_req)]
+    return np.stack(out)
+
+
+def dequant(signs, alpha, zero, p: int, K: int, g: int = 128) -> np.ndarray:
+    """Dense float64 reconstruction ``[M][K]`` at precision ``p``."""
+    signs = _u32(signs)
+    P, M, _ = signs.shape
+    a = _f64(np.asarray(alpha)[:p])
+    z = _f64(zero)
+    w = np.empty((M, K), dtype=np.float64)
+    _load().bcq_oracle_dequant(_ptr(signs), P, M, K, g, p, _ptr(a), _ptr(z), _ptr(w))
+    return w
+
+
+def sign_at(signs, i: int, m: int, k: int, K: int) -> int:
+    """+1 or -1: the sign the oracle reads for plane ``i``, row ``m``, column ``k``."""
+    signs = _u32(signs)
+    _, M, _ = signs.shape
+    return int(_load().bcq_oracle_sign_at(_ptr(signs), M, K, i, m, k))
