@@ -1,0 +1,252 @@
+"""Python binding of the MI355X BCQ library (``libbcq.so``, C ABI in ``include/bcq.h``).
+
+Argument marshalling only: every step of every product runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  There
+is no CPU fallback: if the library is missing or fails to load, every entry
+point raises.
+
+Functions carry the C names (``bcq_pack_planes``, ``bcq_gemv``,
+``bcq_gemm_skinny``, ``bcq_gemv_mixed_p``, ...) and take torch tensors on the
+GPU.  :class:`Store` holds a packed weight (planes + per-precision scale tables)
+and the ``bcq_store`` descriptor that points at it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbcq.so")
+
+BCQ_OK = 0
+BCQ_ERR_INVALID_ARG = -1
+BCQ_ERR_UNSUPPORTED = -2
+BCQ_ERR_ALIGNMENT = -3
+BCQ_ERR_HIP = -4
+BCQ_F16 = 1
+BCQ_F32 = 2
+BCQ_MAX_PLANES = 4
+BCQ_GROUP = 128
+BCQ_TILE_ROWS = 16
+BCQ_MAX_BATCH = 256
+
+# Every symbol include/bcq.h declares.
+EXPORTS = (
+    "bcq_packed_bytes",
+    "bcq_pack_planes",
+    "bcq_unpack_planes",
+    "bcq_gemv",
+    "bcq_gemm_skinny",
+    "bcq_workspace_bytes",
+    "bcq_gemv_mixed_p",
+    "bcq_status_string",
+)
+
+
+class BCQError(RuntimeError):
+    """A library call returned a status other than BCQ_OK."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s" % (fn, bcq_status_string(status)))
+
+
+class _Store(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int32),
+        ("K", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+        ("planes", ctypes.c_int32),
+        ("bits", ctypes.c_void_p),
+        ("scale_dtype", ctypes.c_int),
+        ("alpha", ctypes.c_void_p * (BCQ_MAX_PLANES + 1)),
+        ("zero", ctypes.c_void_p * (BCQ_MAX_PLANES + 1)),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(build_if_missing: bool = True) -> ctypes.CDLL:
+    """Load ``libbcq.so`` (building it first only if no built copy exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise RuntimeError("libbcq.so is not built: run binary_coded_precision_amd.build")
+        from . import build as _build
+
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    st = ctypes.POINTER(_Store)
+    sig = {
+        "bcq_packed_bytes": (sz, [i32, i32, i32]),
+        "bcq_pack_planes": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
+        "bcq_unpack_planes": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
+        "bcq_gemv": (ctypes.c_int, [st, i32, vp, ctypes.c_int, vp, ctypes.c_int, vp]),
+        "bcq_gemm_skinny": (ctypes.c_int, [st, i32, vp, i32, i32, ctypes.c_int, vp, i32,
+                                           ctypes.c_int, vp, sz, vp]),
+        "bcq_workspace_bytes": (sz, [st, i32]),
+        "bcq_gemv_mixed_p": (ctypes.c_int, [st, vp, vp, i32, i32, ctypes.c_int, vp, i32,
+                                            ctypes.c_int, vp]),
+        "bcq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != BCQ_OK:
+        raise BCQError(fn, status)
+
+
+def _stream(stream=None):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float16:
+        return BCQ_F16
+    if t.dtype == torch.float32:
+        return BCQ_F32
+    raise TypeError("BCQ tensors must be float16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+# ----------------------------------------------------------------------------- C names
+
+
+def bcq_status_string(status: int) -> str:
+    return load().bcq_status_string(int(status)).decode()
+
+
+def bcq_packed_bytes(P: int, M: int, K: int) -> int:
+    return int(load().bcq_packed_bytes(P, M, K))
+
+
+def bcq_pack_planes(signs, P: int, M: int, K: int, packed, stream=None) -> None:
+    """``signs``: int32/uint32 device tensor [P][M][K/32]; ``packed``: device tensor of
+    ``bcq_packed_bytes(P, M, K)`` bytes."""
+    _check("bcq_pack_planes",
+           load().bcq_pack_planes(_ptr(signs), P, M, K, _ptr(packed), _stream(stream)))
+
+
+def bcq_unpack_planes(packed, P: int, M: int, K: int, signs, stream=None) -> None:
+    _check("bcq_unpack_planes",
+           load().bcq_unpack_planes(_ptr(packed), P, M, K, _ptr(signs), _stream(stream)))
+
+
+def bcq_gemv(store: "Store", p: int, x, y, stream=None) -> None:
+    """``y[M] = product at precision p`` of the device vector ``x[K]``."""
+    _check("bcq_gemv", load().bcq_gemv(store.ref(), p, _ptr(x), _dtype_code(x), _ptr(y),
+                                       _dtype_code(y), _stream(stream)))
+
+
+def bcq_workspace_bytes(store: "Store", b: int) -> int:
+    return int(load().bcq_workspace_bytes(store.ref(), b))
+
+
+def bcq_gemm_skinny(store: "Store", p: int, X, Y, workspace=None, stream=None) -> None:
+    """``Y[r] = product at precision p`` of ``X[r]`` for each row r of the [b][K] tensor X."""
+    b = X.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bcq_gemm_skinny",
+           load().bcq_gemm_skinny(store.ref(), p, _ptr(X), b, X.stride(0), _dtype_code(X),
+                                  _ptr(Y), Y.stride(0), _dtype_code(Y), _ptr(workspace),
+                                  ws_bytes, _stream(stream)))
+
+
+def bcq_gemv_mixed_p(store: "Store", p_host: Sequence[int], X, Y, stream=None) -> None:
+    """Request r at its own precision ``p_host[r]``."""
+    b = X.shape[0]
+    ps = (ctypes.c_int32 * b)(*[int(v) for v in p_host])
+    _check("bcq_gemv_mixed_p",
+           load().bcq_gemv_mixed_p(store.ref(), ps, _ptr(X), b, X.stride(0), _dtype_code(X),
+                                   _ptr(Y), Y.stride(0), _dtype_code(Y), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- store
+
+
+class Store:
+    """A packed BCQ weight on the GPU and its ``bcq_store`` descriptor.
+
+    ``bits`` is the packed device layout; ``alpha[p]`` / ``zero[p]`` are the
+    tables used at precision p (tensors, possibly the same tensor for every p).
+    """
+
+    def __init__(self, M: int, K: int, planes: int, bits, alpha: Dict[int, object],
+                 zero: Dict[int, object]):
+        self.M, self.K, self.planes = M, K, planes
+        self.bits = bits
+        self.alpha = dict(alpha)
+        self.zero = dict(zero)
+        dt = None
+        for t in list(self.alpha.values()) + list(self.zero.values()):
+            d = _dtype_code(t)
+            if dt is not None and d != dt:
+                raise TypeError("all scale tables must share one dtype")
+            dt = d
+        self.scale_dtype = dt
+        st = _Store()
+        st.M, st.K, st.group_size, st.planes = M, K, BCQ_GROUP, planes
+        st.bits = bits.data_ptr()
+        st.scale_dtype = dt
+        for p in range(BCQ_MAX_PLANES + 1):
+            st.alpha[p] = self.alpha[p].data_ptr() if p in self.alpha else None
+            st.zero[p] = self.zero[p].data_ptr() if p in self.zero else None
+        self._st = st
+
+    def ref(self):
+        return ctypes.byref(self._st)
+
+    @classmethod
+    def from_host(cls, signs: np.ndarray, alpha: np.ndarray, zero: np.ndarray, *,
+                  alpha_p: Optional[Dict[int, np.ndarray]] = None,
+                  zero_p: Optional[Dict[int, np.ndarray]] = None, device="cuda",
+                  stream=None) -> "Store":
+        """Upload canonical host arrays and pack the planes with ``bcq_pack_planes``.
+
+        ``signs`` uint32 [P][M][K/32]; ``alpha`` [P][M][K/128]; ``zero`` [M][K/128].
+        Without ``alpha_p``/``zero_p`` every precision shares ``alpha``'s leading
+        planes and ``zero``.
+        """
+        import torch
+
+        P, M, W = signs.shape
+        K = W * 32
+        nbytes = bcq_packed_bytes(P, M, K)
+        if nbytes == 0:
+            raise BCQError("bcq_packed_bytes", BCQ_ERR_INVALID_ARG)
+        dsigns = torch.from_numpy(np.ascontiguousarray(signs).view(np.int32)).to(device)
+        packed = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
+        bcq_pack_planes(dsigns, P, M, K, packed, stream)
+        if alpha_p is None:
+            a = torch.from_numpy(np.ascontiguousarray(alpha)).to(device)
+            z = torch.from_numpy(np.ascontiguousarray(zero)).to(device)
+            at = {p: a for p in range(1, P + 1)}
+            zt = {p: z for p in range(1, P + 1)}
+        else:
+            at = {p: torch.from_numpy(np.ascontiguousarray(alpha_p[p])).to(device)
+                  for p in range(1, P + 1)}
+            zt = {p: torch.from_numpy(np.ascontiguousarray(zero_p[p])).to(device)
+                  for p in range(1, P + 1)}
+        return cls(M, K, P, packed, at, zt)

@@ -1,0 +1,165 @@
+/*
+ * bcq.h -- C ABI of the MI355X (gfx950) binary-coded quantization (BCQ) library.
+ *
+ * The operation (AnyBCQ paper notes, "Method / key designs", and the AnyBCQ
+ * abstract on the mlsanity page): a weight matrix W [M][K] is held as P binary
+ * planes B_1..B_P with entries in {-1,+1}, a scale per plane and per
+ * (row, group of g = 128 columns), and one offset z per (row, group)
+ * (asymmetric, group-wise BCQ: AnyBCQ paper notes, "Training strategy").  A
+ * product at precision p <= P uses only the first p planes:
+ *
+ *     y[m] = sum_j [ sum_{i<p} alpha_p[i][m][j] * (sum_{k in group j} s_i[m][k] x[k])
+ *                    + zero_p[m][j] * (sum_{k in group j} x[k]) ]
+ *
+ * One stored set of planes serves every precision, and the precision may be
+ * chosen per call or per request (AnyBCQ paper notes, "overall framework" and
+ * "progressive precision expansion"; abstract: per-request precision).  Reading
+ * the first p planes must not touch the others, so each plane is a separate
+ * contiguous array in device memory.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless the parameter name ends in _host.
+ *    The caller allocates and owns all memory; the library allocates nothing
+ *    and keeps no state between calls.
+ *  - Calls that take a stream validate their arguments on the host first.  A
+ *    failed check returns an error and enqueues nothing.  A passing call
+ *    enqueues its kernels on `stream` and returns without synchronising.
+ *    BCQ_ERR_HIP reports a launch failure (hipGetLastError after the launch).
+ *  - Calls on different streams are independent.  Calls that share output
+ *    buffers must be ordered by the caller.
+ *  - Dtypes: scales, activations and outputs use one dtype per call
+ *    (BCQ_F16 or BCQ_F32); other pairings return BCQ_ERR_UNSUPPORTED.
+ *    Products accumulate in fp32 and round once (to nearest even) at writeback.
+ *  - Shapes: K must be a positive multiple of 128 (group_size must be 128),
+ *    M >= 1, 1 <= p <= planes <= 4.
+ */
+#ifndef BCQ_H_
+#define BCQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BCQ_MAX_PLANES 4
+#define BCQ_GROUP 128
+/* Rows per tile of the packed device layout (see bcq_pack_planes). */
+#define BCQ_TILE_ROWS 16
+/* Largest batch accepted by bcq_gemm_skinny / bcq_gemv_mixed_p in one call. */
+#define BCQ_MAX_BATCH 256
+
+typedef enum {
+  BCQ_OK = 0,
+  BCQ_ERR_INVALID_ARG = -1, /* null pointer, bad shape, p out of range, bad leading dim */
+  BCQ_ERR_UNSUPPORTED = -2, /* valid but not implemented: dtype pairing, group size != 128 */
+  BCQ_ERR_ALIGNMENT = -3,   /* a pointer or leading dimension breaks the alignment rules */
+  BCQ_ERR_HIP = -4          /* the HIP runtime reported an error for a launch */
+} bcq_status;
+
+typedef enum { BCQ_F16 = 1, BCQ_F32 = 2 } bcq_dtype;
+
+/*
+ * A packed store: the planes in device layout plus the scale tables.
+ *
+ * bits:  written by bcq_pack_planes for (planes, M, K); 16-byte aligned.
+ * alpha[p], zero[p] for p = 1..planes: the tables used at precision p.
+ *   alpha[p] -> [p][M][K/128] scales, zero[p] -> [M][K/128] offsets, dtype
+ *   scale_dtype, row-major, element aligned.  AnyBCQ refits every scale when it
+ *   adds a plane, so each precision may have its own tables; when one table is
+ *   shared, alpha[p] for every p may point at the same [planes][M][K/128]
+ *   buffer (its first p planes are the table for precision p) and all zero[p]
+ *   may alias.  alpha[0] and zero[0] are ignored.  Only the entries for the
+ *   precisions a call uses must be non-null.
+ */
+typedef struct {
+  int32_t M;
+  int32_t K;
+  int32_t group_size; /* must be 128 */
+  int32_t planes;     /* P stored planes, 1..4 */
+  const uint32_t *bits;
+  bcq_dtype scale_dtype;
+  const void *alpha[BCQ_MAX_PLANES + 1];
+  const void *zero[BCQ_MAX_PLANES + 1];
+} bcq_store;
+
+/*
+ * Bytes of the packed device layout for (P, M, K), or 0 if the shape is
+ * invalid.  Layout: plane-major; within a plane, rows in tiles of 16 (the last
+ * tile padded with clear bits); within a tile, group-major; within a group, the
+ * 16 rows' 128 bits (16 bytes each, canonical bit order) are contiguous.  So
+ * word index = (((i*MT + t)*G + j)*16 + r)*4 + q with MT = ceil(M/16),
+ * G = K/128, row m = 16t + r, columns 128j + 32q .. 128j + 32q + 31.
+ * The first p planes are a contiguous prefix of p * (bytes / P) bytes.
+ */
+size_t bcq_packed_bytes(int32_t P, int32_t M, int32_t K);
+
+/*
+ * Pack canonical sign planes into the device layout.
+ * signs:  [P][M][K/32] uint32; column k of plane i, row m is bit (k mod 32),
+ *         least significant first, of word [i][m][k/32]; set = +1, clear = -1.
+ *         4-byte aligned.
+ * packed: bcq_packed_bytes(P, M, K) bytes, 16-byte aligned; fully overwritten.
+ * The round trip through bcq_unpack_planes is bit-exact.
+ */
+bcq_status bcq_pack_planes(const uint32_t *signs, int32_t P, int32_t M, int32_t K,
+                           uint32_t *packed, hipStream_t stream);
+
+/* Inverse of bcq_pack_planes (for tests and inspection). */
+bcq_status bcq_unpack_planes(const uint32_t *packed, int32_t P, int32_t M, int32_t K,
+                             uint32_t *signs, hipStream_t stream);
+
+/*
+ * y = BCQ product at precision p for one activation vector (batch 1).
+ * x: [K], 16-byte aligned.  y: [M], element aligned; every element written.
+ */
+bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype x_dtype,
+                    void *y, bcq_dtype y_dtype, hipStream_t stream);
+
+/*
+ * Y[r] = BCQ product at precision p for each of b activation rows X[r].
+ * X: [b][ldx] (row r starts at X + r*ldx elements), 16-byte aligned, so ldx*size
+ * must be a multiple of 16 bytes; ldx >= K.  Y: [b][ldy], ldy >= M, element
+ * aligned.  1 <= b <= BCQ_MAX_BATCH.
+ * Batch 1 runs the batch-1 kernel.  Batches below 16 (and every fp32 batch) run
+ * on the vector ALUs with sign-combination tables shared by up to 8 requests.
+ * fp16 batches of 16 and more dequantise tiles of W to fp16 and contract them
+ * on the matrix cores; that path splits K over workgroups and needs
+ * bcq_workspace_bytes(store, b) bytes of device workspace (4-byte aligned,
+ * contents need no initialisation, clobbered by the call).  workspace may be
+ * NULL when that size is 0; a smaller workspace gives BCQ_ERR_INVALID_ARG.
+ */
+bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int32_t b,
+                           int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,
+                           bcq_dtype y_dtype, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * Device workspace bcq_gemm_skinny needs for a batch of b (0 when none), or 0
+ * for an invalid store.
+ */
+size_t bcq_workspace_bytes(const bcq_store *store, int32_t b);
+
+/*
+ * Per-request precision: Y[r] = BCQ product of X[r] at precision p_host[r],
+ * using alpha[p_host[r]] and zero[p_host[r]].  Every plane up to the largest
+ * requested precision is read once for the whole batch.
+ * p_host: [b] in HOST memory; every entry must lie in [1, planes], otherwise
+ * BCQ_ERR_INVALID_ARG and nothing is enqueued.  1 <= b <= BCQ_MAX_BATCH.
+ * X, Y, ldx, ldy as in bcq_gemm_skinny.
+ */
+bcq_status bcq_gemv_mixed_p(const bcq_store *store, const int32_t *p_host, const void *X,
+                            int32_t b, int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,
+                            bcq_dtype y_dtype, hipStream_t stream);
+
+/* Static text for a status code (never null). */
+const char *bcq_status_string(bcq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BCQ_H_ */

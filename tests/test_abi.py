@@ -1,0 +1,156 @@
+"""The C-ABI library loads, exports every symbol include/bcq.h declares, and
+rejects invalid arguments on the host before any HIP call (no GPU needed:
+every call below fails validation, so nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import binary_coded_precision_amd as bcq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bcq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bcq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(bcq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bcq.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        s = bcq.bcq_status_string(code)
+        assert s.startswith("BCQ_")
+    assert "unknown" in bcq.bcq_status_string(7)
+
+
+def test_packed_bytes():
+    # P planes x 16-row tiles x K/8 bytes per row
+    assert bcq.bcq_packed_bytes(4, 4096, 4096) == 4 * 4096 * 512
+    assert bcq.bcq_packed_bytes(2, 256, 512) == 2 * 256 * 64
+    assert bcq.bcq_packed_bytes(3, 17, 128) == 3 * 32 * 16  # ragged rows pad to a full tile
+    assert bcq.bcq_packed_bytes(4, 14336, 4096) // 4 == 14336 * 4096 // 8  # one plane
+    for bad in [(0, 16, 128), (5, 16, 128), (1, 0, 128), (1, 16, 0), (1, 16, 100), (1, 16, 96)]:
+        assert bcq.bcq_packed_bytes(*bad) == 0
+
+
+# ---------------------------------------------------------------- validation
+
+FAKE = 0x100000  # aligned, never dereferenced (validation fails before any launch)
+
+
+def make_store(M=64, K=256, planes=4, dtype=bcq.BCQ_F16, bits=FAKE, group=128, tables=True):
+    st = bcq._Store()
+    st.M, st.K, st.group_size, st.planes = M, K, group, planes
+    st.bits = bits
+    st.scale_dtype = dtype
+    for p in range(1, 5):
+        st.alpha[p] = FAKE if tables else None
+        st.zero[p] = FAKE if tables else None
+    return st
+
+
+def gemv(st, p=2, x=FAKE, y=FAKE, xdt=bcq.BCQ_F16, ydt=bcq.BCQ_F16):
+    ref = None if st is None else ctypes.byref(st)
+    return bcq.load().bcq_gemv(ref, p, x, xdt, y, ydt, None)
+
+
+def skinny(st, p=2, X=FAKE, b=4, ldx=None, Y=FAKE, ldy=None, dt=bcq.BCQ_F16, ws=None, wsb=0):
+    ldx = st.K if ldx is None else ldx
+    ldy = st.M if ldy is None else ldy
+    return bcq.load().bcq_gemm_skinny(ctypes.byref(st), p, X, b, ldx, dt, Y, ldy, dt, ws, wsb,
+                                      None)
+
+
+def mixed(st, ps, X=FAKE, ldx=None, Y=FAKE, ldy=None, dt=bcq.BCQ_F16):
+    ldx = st.K if ldx is None else ldx
+    ldy = st.M if ldy is None else ldy
+    arr = (ctypes.c_int32 * len(ps))(*ps)
+    return bcq.load().bcq_gemv_mixed_p(ctypes.byref(st), arr, X, len(ps), ldx, dt, Y, ldy, dt,
+                                       None)
+
+
+E_ARG, E_UNS, E_ALN = bcq.BCQ_ERR_INVALID_ARG, bcq.BCQ_ERR_UNSUPPORTED, bcq.BCQ_ERR_ALIGNMENT
+
+
+@pytest.mark.parametrize("case,expect", [
+    (lambda: gemv(None), E_ARG),
+    (lambda: gemv(make_store(bits=0)), E_ARG),
+    (lambda: gemv(make_store(group=64)), E_UNS),
+    (lambda: gemv(make_store(K=100)), E_ARG),
+    (lambda: gemv(make_store(K=192)), E_ARG),
+    (lambda: gemv(make_store(M=0)), E_ARG),
+    (lambda: gemv(make_store(planes=0)), E_ARG),
+    (lambda: gemv(make_store(planes=5)), E_ARG),
+    (lambda: gemv(make_store(), p=0), E_ARG),
+    (lambda: gemv(make_store(planes=2), p=3), E_ARG),
+    (lambda: gemv(make_store(tables=False)), E_ARG),
+    (lambda: gemv(make_store(), x=0), E_ARG),
+    (lambda: gemv(make_store(), y=0), E_ARG),
+    (lambda: gemv(make_store(bits=FAKE + 4)), E_ALN),
+    (lambda: gemv(make_store(), x=FAKE + 8), E_ALN),
+    (lambda: gemv(make_store(), y=FAKE + 1), E_ALN),
+    (lambda: gemv(make_store(), xdt=bcq.BCQ_F32), E_UNS),
+    (lambda: gemv(make_store(), ydt=bcq.BCQ_F32), E_UNS),
+    (lambda: gemv(make_store(), xdt=3), E_ARG),
+    (lambda: gemv(make_store(dtype=9)), E_ARG),
+    (lambda: skinny(make_store(), b=0), E_ARG),
+    (lambda: skinny(make_store(), b=257), E_ARG),
+    (lambda: skinny(make_store(), ldx=255), E_ARG),
+    (lambda: skinny(make_store(), ldy=63), E_ARG),
+    (lambda: skinny(make_store(), ldx=260), E_ALN),  # 260 halves = 520 B, not a multiple of 16
+    (lambda: skinny(make_store(), X=FAKE + 2), E_ALN),
+    (lambda: skinny(make_store(), p=5), E_ARG),
+    (lambda: skinny(make_store(M=4096, K=4096), b=16), E_ARG),  # needs a workspace
+    (lambda: skinny(make_store(M=4096, K=4096), b=16, ws=FAKE, wsb=16), E_ARG),
+    (lambda: mixed(make_store(), [2, 3, 0, 4]), E_ARG),
+    (lambda: mixed(make_store(), [2, 3, 5, 4]), E_ARG),
+    (lambda: mixed(make_store(planes=3), [2, 3, 4]), E_ARG),
+    (lambda: mixed(make_store(), []), E_ARG),
+    (lambda: mixed(make_store(), [2, 3], X=0), E_ARG),
+])
+def test_validation_rejects_before_launch(case, expect):
+    assert case() == expect
+
+
+def test_null_precision_array_rejected():
+    st = make_store()
+    r = bcq.load().bcq_gemv_mixed_p(ctypes.byref(st), None, FAKE, 2, st.K, bcq.BCQ_F16, FAKE,
+                                    st.M, bcq.BCQ_F16, None)
+    assert r == E_ARG
+
+
+def test_pack_validation():
+    lib = bcq.load()
+    assert lib.bcq_pack_planes(None, 1, 16, 128, FAKE, None) == E_ARG
+    assert lib.bcq_pack_planes(FAKE, 1, 16, 100, FAKE, None) == E_ARG
+    assert lib.bcq_pack_planes(FAKE + 2, 1, 16, 128, FAKE, None) == E_ALN
+    assert lib.bcq_pack_planes(FAKE, 1, 16, 128, FAKE + 4, None) == E_ALN
+    assert lib.bcq_unpack_planes(FAKE, 0, 16, 128, FAKE, None) == E_ARG
+
+
+def test_workspace_sizes():
+    lib = bcq.load()
+    st = make_store(M=4096, K=4096)
+    assert lib.bcq_workspace_bytes(ctypes.byref(st), 1) == 0
+    assert lib.bcq_workspace_bytes(ctypes.byref(st), 8) == 0
+    need16 = lib.bcq_workspace_bytes(ctypes.byref(st), 16)
+    need64 = lib.bcq_workspace_bytes(ctypes.byref(st), 64)
+    assert need16 > 0 and need64 == 4 * need16
+    assert lib.bcq_workspace_bytes(ctypes.byref(st), 256) == need64  # launched 64 at a time
+    f32 = make_store(M=4096, K=4096, dtype=bcq.BCQ_F32)
+    assert lib.bcq_workspace_bytes(ctypes.byref(f32), 64) == 0  # fp32 uses the table path
+    assert lib.bcq_workspace_bytes(None, 16) == 0

@@ -1,0 +1,367 @@
+"""HIP path vs the float64 oracle, element by element, through the C ABI.
+
+Bars (relative L2 over all outputs of a call, float64): 2e-3 for fp16 outputs,
+1e-5 for fp32 outputs.  Packing and sign recovery are bit-exact.  Small cases
+span several row tiles, several K windows and ragged tails; full-size cases use
+the configured shapes and compare sampled rows (rows are independent, so the
+oracle runs on the sampled rows only).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import bcq_synth
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import binary_coded_precision_amd as bcq  # noqa: E402
+
+TOL = {np.dtype(np.float16): 2e-3, np.dtype(np.float32): 1e-5}
+
+
+def say(*a):
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def store_of(w, independent=False):
+    if independent:
+        return bcq.Store.from_host(w.signs, w.alpha, w.zero, alpha_p=w.alpha_p, zero_p=w.zero_p)
+    return bcq.Store.from_host(w.signs, w.alpha, w.zero)
+
+
+def sub_rows(w, rows):
+    """The same problem restricted to some rows (rows are independent)."""
+    class V:
+        pass
+    v = V()
+    v.signs = w.signs[:, rows]
+    v.alpha_for = lambda p: w.alpha_for(p)[:, rows]
+    v.zero_for = lambda p: w.zero_for(p)[rows]
+    return v
+
+
+def oracle_y(w, x, p_req, rows=None):
+    v = w if rows is None else sub_rows(w, rows)
+    return oracle.gemv_requests(v.signs, x, p_req, v.alpha_for, v.zero_for)
+
+
+def sample_rows(M, n=384, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    rows |= {0, 1, 15, 16, M - 1, M - 17 if M > 17 else 0}
+    return np.array(sorted(r for r in rows if 0 <= r < M))
+
+
+# ---------------------------------------------------------------- packing
+
+@pytest.mark.parametrize("P,M,K", [(2, 256, 512), (4, 4096, 4096), (3, 37, 384), (1, 1, 128),
+                                   (4, 14336, 4096)])
+def test_pack_unpack_round_trip_bit_exact(P, M, K):
+    say("pack/unpack", P, M, K)
+    w = bcq_synth.make(M, K, P, seed=M + K)
+    d = dev(w.signs.view(np.int32))
+    packed = torch.empty(bcq.bcq_packed_bytes(P, M, K) // 4, dtype=torch.int32, device="cuda")
+    bcq.bcq_pack_planes(d, P, M, K, packed)
+    back = torch.full_like(d, -1)
+    bcq.bcq_unpack_planes(packed, P, M, K, back)
+    torch.cuda.synchronize()
+    assert np.array_equal(back.cpu().numpy().view(np.uint32), w.signs)
+
+
+def test_packed_layout_matches_documented_index():
+    """Word (((i*MT + t)*G + j)*16 + r)*4 + q holds row 16t+r, columns 128j+32q.."""
+    P, M, K = 2, 40, 384
+    w = bcq_synth.make(M, K, P, seed=3)
+    packed = torch.empty(bcq.bcq_packed_bytes(P, M, K) // 4, dtype=torch.int32, device="cuda")
+    bcq.bcq_pack_planes(dev(w.signs.view(np.int32)), P, M, K, packed)
+    got = packed.cpu().numpy().view(np.uint32)
+    MT, G = 3, 3
+    for i in range(P):
+        for t in range(MT):
+            for j in range(G):
+                for r in range(16):
+                    for q in range(4):
+                        m = 16 * t + r
+                        want = w.signs[i, m, 4 * j + q] if m < M else 0
+                        assert got[(((i * MT + t) * G + j) * 16 + r) * 4 + q] == want
+
+
+# ---------------------------------------------------------------- batch 1
+
+def test_worked_example_on_gpu():
+    """The BiLoCo page's v.x = 3.4 through one 128-column group (fp32)."""
+    say("gemv worked example")
+    K = 128
+    signs = np.zeros((2, 1, 4), np.uint32)
+    signs[0, 0, 0] = 0b0101
+    alpha = np.array([[[1.0]], [[0.0]]], np.float32)
+    zero = np.zeros((1, 1), np.float32)
+    st = bcq.Store.from_host(signs, alpha, zero)
+    x = np.zeros(K, np.float32)
+    x[:4] = [0.5, -1.2, 2.0, 0.3]
+    y = torch.empty(1, dtype=torch.float32, device="cuda")
+    bcq.bcq_gemv(st, 2, dev(x), y)
+    assert abs(float(y.item()) - 3.4) <= 4e-7
+
+
+@pytest.mark.parametrize("p", [2, 3, 4])
+def test_config2_qproj_each_precision(p):
+    w = bcq_synth.config(2)
+    say("gemv cfg2", p)
+    st = store_of(w)
+    y = torch.empty(w.M, dtype=torch.float16, device="cuda")
+    bcq.bcq_gemv(st, p, dev(w.x[0]), y)
+    ref = oracle.gemv(w.signs, w.alpha, w.zero, w.x[0], p)
+    assert rel_l2(y.cpu().numpy(), ref) <= 2e-3
+
+
+def test_config1_tiny_fp32():
+    w = bcq_synth.config(1)
+    say("gemv cfg1")
+    st = store_of(w)
+    y = torch.empty(w.M, dtype=torch.float32, device="cuda")
+    bcq.bcq_gemv(st, 2, dev(w.x[0]), y)
+    ref = oracle.gemv(w.signs, w.alpha, w.zero, w.x[0], 2)
+    assert rel_l2(y.cpu().numpy(), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("M,K,P,dt", [
+    (1, 128, 1, np.float32), (15, 128, 2, np.float16), (17, 256, 4, np.float32),
+    (100, 384, 3, np.float16), (48, 2048, 4, np.float32), (33, 2176, 2, np.float16),
+    (64, 4224, 4, np.float16), (20, 16384 + 2048, 2, np.float32), (8, 40960, 1, np.float16),
+])
+def test_gemv_ragged_and_windowed_shapes(M, K, P, dt):
+    """Ragged row tiles, partial K windows, more windows than one prefetch batch."""
+    say("gemv shape", M, K, P, dt)
+    w = bcq_synth.make(M, K, P, dtype=dt, seed=M * 7 + K, outlier_frac=0.01)
+    st = store_of(w)
+    for p in range(1, P + 1):
+        y = torch.empty(M, dtype=torch.from_numpy(np.zeros(1, dt)).dtype, device="cuda")
+        bcq.bcq_gemv(st, p, dev(w.x[0]), y)
+        ref = oracle.gemv(w.signs, w.alpha, w.zero, w.x[0], p)
+        assert rel_l2(y.cpu().numpy(), ref) <= TOL[np.dtype(dt)], (M, K, P, p)
+
+
+def test_unit_vectors_recover_sign_bits_on_gpu():
+    """x = e_k with scales 1, 1/2, 1/4, 1/8 and z = 1/32: y is column k of W exactly."""
+    M, K, P = 40, 512, 4
+    w = bcq_synth.make(M, K, P, dtype=np.float32, seed=21)
+    alpha = np.zeros_like(w.alpha)
+    for i in range(P):
+        alpha[i] = 2.0 ** -i
+    zero = np.full_like(w.zero, 1.0 / 32)
+    st = bcq.Store.from_host(w.signs, alpha, zero)
+    cols = [0, 1, 31, 32, 33, 127, 128, 200, 255, 256, 300, 511]
+    X = np.zeros((len(cols), K), np.float32)
+    for n, k in enumerate(cols):
+        X[n, k] = 1.0
+    say("gemv unit vectors")
+    for n, k in enumerate(cols):
+        y = torch.empty(M, dtype=torch.float32, device="cuda")
+        bcq.bcq_gemv(st, P, dev(X[n]), y)
+        col = y.cpu().numpy().astype(np.float64) - 1.0 / 32
+        for i in range(P):
+            s = np.where(col > 0, 1, -1)
+            bit = (w.signs[i, :, k // 32] >> np.uint32(k % 32)) & 1
+            assert np.array_equal(s, bit.astype(int) * 2 - 1), (i, k)
+            col -= s * 2.0 ** -i
+        assert np.max(np.abs(col)) == 0.0
+
+
+def test_prefix_invariant_on_gpu():
+    M, K, P = 256, 1024, 4
+    w = bcq_synth.make(M, K, P, dtype=np.float32, seed=22)
+    st = store_of(w)
+    x = dev(w.x[0])
+    ys = {}
+    say("gemv prefix invariant")
+    for p in range(1, P + 1):
+        y = torch.empty(M, dtype=torch.float32, device="cuda")
+        bcq.bcq_gemv(st, p, x, y)
+        ys[p] = y.cpu().numpy().astype(np.float64)
+    for p in range(2, P + 1):
+        a = w.alpha.copy()
+        a[: p - 1] = 0
+        term = oracle.gemv(w.signs, a, np.zeros_like(w.zero), w.x[0], p)  # alpha_p (B_p x) only
+        assert rel_l2(ys[p] - ys[p - 1], term) <= 1e-5
+
+
+def test_deterministic():
+    w = bcq_synth.config(2)
+    st = store_of(w)
+    x = dev(w.x[0])
+    outs = []
+    for _ in range(3):
+        y = torch.empty(w.M, dtype=torch.float16, device="cuda")
+        bcq.bcq_gemv(st, 3, x, y)
+        outs.append(y.cpu().numpy().view(np.uint16))
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+@pytest.mark.parametrize("M,K", [(14336, 4096), (4096, 14336), (1024, 4096)])
+def test_full_size_shapes_sampled_rows(M, K):
+    w = bcq_synth.make(M, K, 4, dtype=np.float16, seed=M + 3 * K)
+    st = store_of(w)
+    rows = sample_rows(M)
+    for p in (2, 3, 4):
+        say("gemv full", M, K, p)
+        y = torch.empty(M, dtype=torch.float16, device="cuda")
+        bcq.bcq_gemv(st, p, dev(w.x[0]), y)
+        ref = oracle_y(w, w.x[:1], [p], rows)[0]
+        assert rel_l2(y.cpu().numpy()[rows], ref) <= 2e-3
+        assert torch.isfinite(y.float()).all()
+
+
+# ---------------------------------------------------------------- small batches
+
+@pytest.mark.parametrize("b", [2, 3, 4, 5, 8, 12, 15])
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+def test_skinny_small_batches(b, dt):
+    M, K, P = 72, 896, 4
+    w = bcq_synth.make(M, K, P, b=b, dtype=dt, seed=b * 13, outlier_frac=0.01)
+    st = store_of(w)
+    tdt = torch.float16 if dt == np.float16 else torch.float32
+    for p in (1, 3, 4):
+        say("skinny", b, dt, p)
+        Y = torch.empty((b, M), dtype=tdt, device="cuda")
+        bcq.bcq_gemm_skinny(st, p, dev(w.x), Y)
+        ref = oracle_y(w, w.x, [p] * b)
+        for r in range(b):
+            assert rel_l2(Y[r].cpu().numpy(), ref[r]) <= TOL[np.dtype(dt)], (b, p, r)
+
+
+@pytest.mark.parametrize("shape,b", [("gate_up", 4), ("gate_up", 8), ("down", 4), ("down", 8)])
+def test_config3_mlp_sampled(shape, b):
+    M, K = bcq_synth.MLP_SHAPES[shape]
+    w = bcq_synth.make(M, K, 4, b=b, p=3, seed=3, dtype=np.float16)
+    st = store_of(w)
+    say("skinny cfg3", shape, b)
+    Y = torch.empty((b, M), dtype=torch.float16, device="cuda")
+    bcq.bcq_gemm_skinny(st, 3, dev(w.x), Y)
+    rows = sample_rows(M, 256)
+    ref = oracle_y(w, w.x, [3] * b, rows)
+    got = Y.cpu().numpy()[:, rows]
+    for r in range(b):
+        assert rel_l2(got[r], ref[r]) <= 2e-3
+
+
+def test_strided_batch_rows():
+    """Leading dimensions larger than the row lengths."""
+    M, K, b = 40, 512, 5
+    w = bcq_synth.make(M, K, 3, b=b, dtype=np.float16, seed=31)
+    st = store_of(w)
+    Xb = torch.zeros((b, K + 64), dtype=torch.float16, device="cuda")
+    Xb[:, :K] = dev(w.x)
+    Yb = torch.full((b, M + 9), 7.0, dtype=torch.float16, device="cuda")
+    say("skinny strided")
+    bcq.bcq_gemm_skinny(st, 3, Xb[:, :K], Yb[:, :M])
+    ref = oracle_y(w, w.x, [3] * b)
+    for r in range(b):
+        assert rel_l2(Yb[r, :M].cpu().numpy(), ref[r]) <= 2e-3
+    assert (Yb[:, M:].float() == 7.0).all()  # nothing written past ldy's row
+
+
+# ---------------------------------------------------------------- per-request precision
+
+def test_config4_mixed_precision():
+    w = bcq_synth.config(4)
+    st = store_of(w)
+    say("mixed cfg4", list(w.p_req))
+    Y = torch.empty((w.b, w.M), dtype=torch.float16, device="cuda")
+    bcq.bcq_gemv_mixed_p(st, w.p_req, dev(w.x), Y)
+    ref = oracle_y(w, w.x, w.p_req)
+    for r in range(w.b):
+        assert rel_l2(Y[r].cpu().numpy(), ref[r]) <= 2e-3, r
+    # the same requests one by one through bcq_gemv agree with the oracle too
+    for r in range(w.b):
+        y = torch.empty(w.M, dtype=torch.float16, device="cuda")
+        bcq.bcq_gemv(st, int(w.p_req[r]), dev(w.x[r]), y)
+        assert rel_l2(y.cpu().numpy(), ref[r]) <= 2e-3
+
+
+@pytest.mark.parametrize("b", [1, 3, 8, 11])
+def test_mixed_precision_independent_tables(b):
+    """Each request uses alpha[p_r] / zero[p_r]: independently drawn per-precision tables."""
+    w = bcq_synth.independent_tables(
+        bcq_synth.make(96, 640, 4, b=b, dtype=np.float32, seed=40 + b, p_choices=(1, 2, 3, 4)))
+    st = store_of(w, independent=True)
+    say("mixed independent", b, list(w.p_req))
+    Y = torch.empty((b, w.M), dtype=torch.float32, device="cuda")
+    bcq.bcq_gemv_mixed_p(st, w.p_req, dev(w.x), Y)
+    ref = oracle_y(w, w.x, w.p_req)
+    for r in range(b):
+        assert rel_l2(Y[r].cpu().numpy(), ref[r]) <= 1e-5, r
+
+
+def test_mixed_rejects_bad_entry_and_writes_nothing():
+    w = bcq_synth.make(32, 256, 4, b=3, seed=5)
+    st = store_of(w)
+    Y = torch.full((3, 32), 5.0, dtype=torch.float16, device="cuda")
+    with pytest.raises(bcq.BCQError):
+        bcq.bcq_gemv_mixed_p(st, [2, 7, 3], dev(w.x), Y)
+    torch.cuda.synchronize()
+    assert (Y.float() == 5.0).all()
+
+
+# ---------------------------------------------------------------- matrix-core path
+
+@pytest.mark.parametrize("M,K,b", [(64, 512, 16), (100, 640, 17), (48, 1024, 32), (80, 2048, 64),
+                                   (33, 384, 80), (4096, 4096, 16)])
+def test_mfma_batches(M, K, b):
+    w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=M + b, outlier_frac=0.01)
+    st = store_of(w)
+    ws_bytes = bcq.bcq_workspace_bytes(st, b)
+    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda")
+    rows = sample_rows(M, 256)
+    for p in (2, 4):
+        say("mfma", M, K, b, p)
+        Y = torch.empty((b, M), dtype=torch.float16, device="cuda")
+        bcq.bcq_gemm_skinny(st, p, dev(w.x), Y, workspace=ws)
+        ref = oracle_y(w, w.x, [p] * b, rows)
+        got = Y.cpu().numpy()[:, rows]
+        for r in range(b):
+            assert rel_l2(got[r], ref[r]) <= 2e-3, (p, r)
+
+
+@pytest.mark.parametrize("shape", ["q_o", "k_v", "gate_up", "down"])
+@pytest.mark.parametrize("b", [16, 64])
+def test_config5_layer_sweep_sampled(shape, b):
+    M, K = bcq_synth.LAYER_SHAPES[shape]
+    w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=5)
+    st = store_of(w)
+    ws = torch.empty(max(bcq.bcq_workspace_bytes(st, b) // 4, 1), dtype=torch.float32,
+                     device="cuda")
+    say("mfma cfg5", shape, b)
+    Y = torch.empty((b, M), dtype=torch.float16, device="cuda")
+    bcq.bcq_gemm_skinny(st, 4, dev(w.x), Y, workspace=ws)
+    rows = sample_rows(M, 128)
+    ref = oracle_y(w, w.x, [4] * b, rows)
+    got = Y.cpu().numpy()[:, rows]
+    for r in range(b):
+        assert rel_l2(got[r], ref[r]) <= 2e-3
+
+
+def test_fp32_large_batch_uses_exact_tables():
+    M, K, b = 64, 512, 20
+    w = bcq_synth.make(M, K, 2, b=b, dtype=np.float32, seed=77)
+    st = store_of(w)
+    say("fp32 b20")
+    Y = torch.empty((b, M), dtype=torch.float32, device="cuda")
+    bcq.bcq_gemm_skinny(st, 2, dev(w.x), Y)
+    ref = oracle_y(w, w.x, [2] * b)
+    for r in range(b):
+        assert rel_l2(Y[r].cpu().numpy(), ref[r]) <= 1e-5
