@@ -40,12 +40,25 @@ constexpr int kXStride = kGroup * 2 + 16;  // bytes per staged request row
 __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 __device__ __forceinline__ uint32_t as_u(half2v h) { return __builtin_bit_cast(uint32_t, h); }
 
-template <int NT>
+// Operands of one K group, double-buffered across the group loop.
+template <int NT, int P>
+struct MfOperands {
+  uint4 x[NT];         // this thread's share of the staged activations
+  uint4 bits[P];       // this lane's row: 128 sign bits per plane
+  uint32_t alpha2[P];  // (alpha, alpha) as packed fp16
+  uint32_t zero2;      // (z, z)
+};
+
+// P (the precision) is a template argument and the load phase has no branches:
+// request rows past b, rows past M and tiles past MT read clamped in-range
+// addresses whose values are never stored.
+template <int NT, int P>
 __global__ __launch_bounds__(kMfThreads) void gemm_mfma_kernel(
     const uint4 *__restrict__ bits, const half_t *__restrict__ alpha,
     const half_t *__restrict__ zero, const half_t *__restrict__ X, int ldx, int b,
-    half_t *__restrict__ Y, int ldy, float *__restrict__ ws, int M, int G, int MT, int p,
+    half_t *__restrict__ Y, int ldy, float *__restrict__ ws, int M, int G, int MT,
     int groups_per_slice) {
+  using Ops = MfOperands<NT, P>;
   __shared__ __attribute__((aligned(16))) char xt[2][NT * 16 * kXStride];
   __shared__ __attribute__((aligned(16))) uint2 pm1[16];  // +-1.0 for the 4 bits of a nibble
 
@@ -55,14 +68,13 @@ __global__ __launch_bounds__(kMfThreads) void gemm_mfma_kernel(
   const int r = lane & 15;
   const int kb = lane >> 4;
   const int t = blockIdx.x * kMfWaves + wave;
-  const bool tile_ok = t < MT;
-  const int m = t * kTileRows + r;
-  const bool row_ok = m < M;
+  const int t_safe = min(t, MT - 1);
+  const int m_safe = min(t * kTileRows + r, M - 1);
   const int s = blockIdx.y;
   const int j0 = s * groups_per_slice;
   const int j1 = min(G, j0 + groups_per_slice);
   const size_t plane_stride = (size_t)MT * G * kTileRows;
-  const uint4 *tbits = bits + (size_t)t * G * kTileRows + r;
+  const uint4 *tbits = bits + (size_t)t_safe * G * kTileRows + r;
   const size_t MG = (size_t)M * G;
 
   if (tid < 16) {
@@ -76,77 +88,51 @@ __global__ __launch_bounds__(kMfThreads) void gemm_mfma_kernel(
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // per-group operands, prefetched one group ahead
-  uint4 xr[NT];            // this thread's share of the staged activations
-  uint4 bw[BCQ_MAX_PLANES];
-  uint32_t al2[BCQ_MAX_PLANES];  // (alpha, alpha) as packed fp16
-  uint32_t z2;
-  auto fetch = [&](int j, uint4 (&xv)[NT], uint4 (&bv)[BCQ_MAX_PLANES],
-                   uint32_t (&av)[BCQ_MAX_PLANES], uint32_t &zv) {
-    const bool jok = j < j1;
+  auto fetch = [&](int j_in, Ops &o) {
+    const int j = min(j_in, j1 - 1);
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
       const int c = tid + q * kMfThreads;  // 16-byte chunk: request c/16, columns 8*(c%16)..
-      const int n = c >> 4;
-      xv[q] = (jok && n < b)
-                  ? *reinterpret_cast<const uint4 *>(X + (size_t)n * ldx + (size_t)j * kGroup +
-                                                     (c & 15) * 8)
-                  : make_uint4(0u, 0u, 0u, 0u);
+      const int n = min(c >> 4, b - 1);
+      o.x[q] = *reinterpret_cast<const uint4 *>(X + (size_t)n * ldx + (size_t)j * kGroup +
+                                                (c & 15) * 8);
     }
 #pragma unroll
-    for (int i = 0; i < BCQ_MAX_PLANES; ++i) {
-      bv[i] = (jok && tile_ok && i < p) ? tbits[i * plane_stride + (size_t)j * kTileRows]
-                                        : make_uint4(0u, 0u, 0u, 0u);
-      const unsigned short a =
-          (jok && row_ok && i < p)
-              ? __builtin_bit_cast(unsigned short, alpha[i * MG + (size_t)m * G + j])
-              : (unsigned short)0;
-      av[i] = a | ((uint32_t)a << 16);
+    for (int i = 0; i < P; ++i) {
+      o.bits[i] = tbits[i * plane_stride + (size_t)j * kTileRows];
+      const uint32_t a =
+          *reinterpret_cast<const unsigned short *>(alpha + i * MG + (size_t)m_safe * G + j);
+      o.alpha2[i] = a | (a << 16);
     }
-    const unsigned short zz =
-        (jok && row_ok) ? __builtin_bit_cast(unsigned short, zero[(size_t)m * G + j])
-                        : (unsigned short)0;
-    zv = zz | ((uint32_t)zz << 16);
+    const uint32_t zz = *reinterpret_cast<const unsigned short *>(zero + (size_t)m_safe * G + j);
+    o.zero2 = zz | (zz << 16);
   };
 
-  fetch(j0, xr, bw, al2, z2);
-  int buf = 0;
-  for (int j = j0; j < j1; ++j) {
+  auto consume = [&](int buf, const Ops &o) {
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
       const int c = tid + q * kMfThreads;
-      *reinterpret_cast<uint4 *>(xt[buf] + (c >> 4) * kXStride + (c & 15) * 16) = xr[q];
+      *reinterpret_cast<uint4 *>(xt[buf] + (c >> 4) * kXStride + (c & 15) * 16) = o.x[q];
     }
-    uint4 cb[BCQ_MAX_PLANES];
-    uint32_t ca[BCQ_MAX_PLANES];
-#pragma unroll
-    for (int i = 0; i < BCQ_MAX_PLANES; ++i) {
-      cb[i] = bw[i];
-      ca[i] = al2[i];
-    }
-    const uint32_t cz = z2;
-    fetch(j + 1, xr, bw, al2, z2);
     __syncthreads();
-
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       // dequantise 8 weights: row r, columns 128j + 32*s4 + 8*kb .. +7
       half2v w2[4] = {as_h2(0u), as_h2(0u), as_h2(0u), as_h2(0u)};
 #pragma unroll
-      for (int i = BCQ_MAX_PLANES - 1; i >= 0; --i) {
-        if (i < p) {
-          const uint32_t word = s4 == 0 ? cb[i].x : (s4 == 1 ? cb[i].y : (s4 == 2 ? cb[i].z : cb[i].w));
-          const uint32_t byte = (word >> (8 * kb)) & 0xFFu;
-          const uint2 lo = pm1[byte & 15u];
-          const uint2 hi = pm1[byte >> 4];
-          const half2v a2 = as_h2(ca[i]);
-          w2[0] = __builtin_elementwise_fma(a2, as_h2(lo.x), w2[0]);
-          w2[1] = __builtin_elementwise_fma(a2, as_h2(lo.y), w2[1]);
-          w2[2] = __builtin_elementwise_fma(a2, as_h2(hi.x), w2[2]);
-          w2[3] = __builtin_elementwise_fma(a2, as_h2(hi.y), w2[3]);
-        }
+      for (int i = P - 1; i >= 0; --i) {
+        const uint32_t word =
+            s4 == 0 ? o.bits[i].x : (s4 == 1 ? o.bits[i].y : (s4 == 2 ? o.bits[i].z : o.bits[i].w));
+        const uint32_t byte = (word >> (8 * kb)) & 0xFFu;
+        const uint2 lo = pm1[byte & 15u];
+        const uint2 hi = pm1[byte >> 4];
+        const half2v a2 = as_h2(o.alpha2[i]);
+        w2[0] = __builtin_elementwise_fma(a2, as_h2(lo.x), w2[0]);
+        w2[1] = __builtin_elementwise_fma(a2, as_h2(lo.y), w2[1]);
+        w2[2] = __builtin_elementwise_fma(a2, as_h2(hi.x), w2[2]);
+        w2[3] = __builtin_elementwise_fma(a2, as_h2(hi.y), w2[3]);
       }
-      const half2v zz = as_h2(cz);
+      const half2v zz = as_h2(o.zero2);
       half8 a;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -161,7 +147,20 @@ __global__ __launch_bounds__(kMfThreads) void gemm_mfma_kernel(
         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop, acc[nt], 0, 0, 0);
       }
     }
-    buf ^= 1;
+  };
+
+  // ping-pong: group j+1 loads while group j computes; the staged x tile is
+  // double-buffered in LDS, so one barrier per group suffices
+  if (j0 < j1) {
+    Ops A, B;
+    fetch(j0, A);
+    for (int j = j0; j < j1; j += 2) {
+      fetch(j + 1, B);
+      consume(0, A);
+      if (j + 1 >= j1) break;  // uniform
+      fetch(j + 2, A);
+      consume(1, B);
+    }
   }
 
   // D layout: lane holds rows 4*kb .. 4*kb+3 of the tile for request column r
@@ -229,24 +228,24 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
   float *w = S > 1 ? static_cast<float *>(ws) : nullptr;
   dim3 grid((MT + kMfWaves - 1) / kMfWaves, S), block(kMfThreads);
   const int NT = (b + 15) / 16;
-  switch (NT) {
-    case 1:
-      hipLaunchKernelGGL(gemm_mfma_kernel<1>, grid, block, 0, s, b4, a, z, X, ldx, b, Y, ldy, w,
-                         M, G, MT, p, gps);
-      break;
-    case 2:
-      hipLaunchKernelGGL(gemm_mfma_kernel<2>, grid, block, 0, s, b4, a, z, X, ldx, b, Y, ldy, w,
-                         M, G, MT, p, gps);
-      break;
-    case 3:
-      hipLaunchKernelGGL(gemm_mfma_kernel<3>, grid, block, 0, s, b4, a, z, X, ldx, b, Y, ldy, w,
-                         M, G, MT, p, gps);
-      break;
-    default:
-      hipLaunchKernelGGL(gemm_mfma_kernel<4>, grid, block, 0, s, b4, a, z, X, ldx, b, Y, ldy, w,
-                         M, G, MT, p, gps);
-      break;
+#define BCQ_MF(NTV, PV)                                                                    \
+  hipLaunchKernelGGL((gemm_mfma_kernel<NTV, PV>), grid, block, 0, s, b4, a, z, X, ldx, b, Y, \
+                     ldy, w, M, G, MT, gps)
+#define BCQ_MF_NT(NTV)              \
+  switch (p) {                      \
+    case 1: BCQ_MF(NTV, 1); break;  \
+    case 2: BCQ_MF(NTV, 2); break;  \
+    case 3: BCQ_MF(NTV, 3); break;  \
+    default: BCQ_MF(NTV, 4); break; \
   }
+  switch (NT) {
+    case 1: BCQ_MF_NT(1) break;
+    case 2: BCQ_MF_NT(2) break;
+    case 3: BCQ_MF_NT(3) break;
+    default: BCQ_MF_NT(4) break;
+  }
+#undef BCQ_MF_NT
+#undef BCQ_MF
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S <= 1) return e;
   const size_t n = (size_t)b * M;

@@ -74,6 +74,26 @@ struct Act<half_t> {
   }
 };
 
+// Scales and offsets are loaded as raw bits into a full 32-bit register and
+// converted at their use.  (Loading fp16 values straight into _Float16
+// variables lets the compiler pack two into one register, which forces a wait
+// on each load before the pack and serialises the loads.)
+template <typename T>
+__device__ __forceinline__ uint32_t load_raw(const T *p) {
+  if constexpr (sizeof(T) == 2)
+    return (uint32_t)(*reinterpret_cast<const unsigned short *>(p));
+  else
+    return *reinterpret_cast<const uint32_t *>(p);
+}
+
+template <typename T>
+__device__ __forceinline__ float raw_to_float(uint32_t v) {
+  if constexpr (sizeof(T) == 2)
+    return (float)__builtin_bit_cast(half_t, (unsigned short)v);
+  else
+    return __builtin_bit_cast(float, v);
+}
+
 // The 16 signed sums of one chunk, entry e at float index e (bit t of e selects
 // +x_t).  lo(e & 3) is -A, D, -D, A and hi(e >> 2) is -C, E, -E, C.
 __device__ __forceinline__ void chunk_entries(const float (&f)[4], float4 (&v)[4]) {
@@ -168,10 +188,16 @@ __device__ __forceinline__ float g1_plane_sum(const uint4 bw, uint32_t base) {
   return (s[0] + s[1]) + (s[2] + s[3]);
 }
 
-template <typename T, int WMAX>
+// The load phase has no branches at all: the precision P is a template
+// argument, and lanes or windows past the end read clamped in-range addresses
+// whose values are never used.  LOOP = false: the whole of K fits one batch of
+// WMAX windows and the body runs once, so no register is loop-carried.  With
+// both, the compiler keeps every load of a batch in flight and waits only at
+// first use.
+template <typename T, int WMAX, bool LOOP, int P>
 __global__ __launch_bounds__(kG1Threads) void gemv_lut_kernel(
     const uint4 *__restrict__ bits, const T *__restrict__ alpha, const T *__restrict__ zero,
-    const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT, int p) {
+    const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT) {
   __shared__ __attribute__((aligned(16))) char lut[kG1WindowBytes];
   __shared__ float gsum[kG1Ksub];
   __shared__ float part[kG1Threads / 64][kTileRows];
@@ -183,7 +209,7 @@ __global__ __launch_bounds__(kG1Threads) void gemv_lut_kernel(
   const int ks = wave * 4 + (lane >> 4);
   const int tile = blockIdx.x;
   const int m = tile * kTileRows + r;
-  const bool row_ok = m < M;
+  const int m_safe = min(m, M - 1);  // padding rows read row M-1's scales, never stored
   const int nwin = (G + kG1Ksub - 1) / kG1Ksub;
   const size_t plane_stride = (size_t)MT * G * kTileRows;  // in uint4
   const uint4 *tbits = bits + (size_t)tile * G * kTileRows + r;
@@ -191,37 +217,33 @@ __global__ __launch_bounds__(kG1Threads) void gemv_lut_kernel(
 
   float acc = 0.f;
 
-  for (int w0 = 0; w0 < nwin; w0 += WMAX) {
+  for (int w0 = 0; w0 < (LOOP ? nwin : 1); w0 += WMAX) {
     // ---- issue every load of this batch of windows: x for the tables first,
-    // then per window the sign words, scales and offsets
+    // then per window the sign words, scales and offsets.
     typename Act<T>::raw xr[WMAX][2];
-    uint4 bw[WMAX][BCQ_MAX_PLANES];
-    T al[WMAX][BCQ_MAX_PLANES];
-    T zz[WMAX];
+    uint4 bw[WMAX][P];
+    uint32_t al[WMAX][P];
+    uint32_t zz[WMAX];
 #pragma unroll
     for (int u = 0; u < WMAX; ++u) {
-      const int w = w0 + u;
+      const int w = min(w0 + u, nwin - 1);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int c = tid + h * kG1Threads;
-        const int j = w * kG1Ksub + c / kChunksPerGroup;
-        xr[u][h] = (w < nwin && j < G)
-                       ? Act<T>::load(x + ((size_t)w * kG1WindowChunks + c) * 4)
-                       : Act<T>::zero();
+        const int j = min(w * kG1Ksub + c / kChunksPerGroup, G - 1);
+        xr[u][h] = Act<T>::load(x + (size_t)j * kGroup + (c % kChunksPerGroup) * 4);
       }
     }
 #pragma unroll
     for (int u = 0; u < WMAX; ++u) {
-      const int w = w0 + u;
-      const int j = w * kG1Ksub + ks;
-      const bool ok = (w < nwin) && (j < G);
+      const int w = min(w0 + u, nwin - 1);
+      const int js = min(w * kG1Ksub + ks, G - 1);
 #pragma unroll
-      for (int i = 0; i < BCQ_MAX_PLANES; ++i) {
-        bw[u][i] = (ok && i < p) ? tbits[i * plane_stride + (size_t)j * kTileRows]
-                                 : make_uint4(0u, 0u, 0u, 0u);
-        al[u][i] = (ok && row_ok && i < p) ? alpha[i * MG + (size_t)m * G + j] : T(0);
+      for (int i = 0; i < P; ++i) {
+        bw[u][i] = tbits[i * plane_stride + (size_t)js * kTileRows];
+        al[u][i] = load_raw(alpha + i * MG + (size_t)m_safe * G + js);
       }
-      zz[u] = (ok && row_ok) ? zero[(size_t)m * G + j] : T(0);
+      zz[u] = load_raw(zero + (size_t)m_safe * G + js);
     }
 
 #pragma unroll
@@ -262,10 +284,9 @@ __global__ __launch_bounds__(kG1Threads) void gemv_lut_kernel(
       if (j < G) {
         const uint32_t base = lds_addr(lut + ks * kG1GroupStride);
 #pragma unroll
-        for (int i = 0; i < BCQ_MAX_PLANES; ++i) {
-          if (i < p) acc = fmaf((float)al[u][i], g1_plane_sum(bw[u][i], base), acc);
-        }
-        acc = fmaf((float)zz[u], gsum[ks], acc);
+        for (int i = 0; i < P; ++i)
+          acc = fmaf(raw_to_float<T>(al[u][i]), g1_plane_sum(bw[u][i], base), acc);
+        acc = fmaf(raw_to_float<T>(zz[u]), gsum[ks], acc);
       }
     }
   }
@@ -282,6 +303,272 @@ __global__ __launch_bounds__(kG1Threads) void gemv_lut_kernel(
   }
 }
 
+// ------------------------------------------------ batch 1, whole-K tables
+//
+// For K <= 6144 the tables of all of K fit in LDS (NW windows of 16 groups).
+// A workgroup of 512 lanes (two wavefronts per SIMD, so one hides the other's
+// LDS latency) builds them once, then walks its row tiles (tile blockIdx.x +
+// k * gridDim.x), loading the next tile's sign words, scales and offsets while
+// it looks up the current one, and reduces all its tiles at the end.  With
+// grid = min(row tiles, CUs) every CU holds one workgroup that streams several
+// tiles, so table builds are amortised and loads overlap lookups.
+//
+// Lane (r, hs): row r of the tile, half-group slot hs = 0..31 of the window
+// (group hs/2, columns 64*(hs%2) .. +63).  A wavefront's four slots are two
+// groups x two halves; in LDS the second half of a group sits 16 banks after
+// the first and consecutive groups 32 banks apart, so the four slots read
+// disjoint quarters of the 64 banks.
+
+constexpr int kRThreads = 512;
+constexpr int kRWaves = kRThreads / 64;
+constexpr int kRSlots = 32;                          // half-group slots per row
+constexpr int kRHalfPad = 64;                        // bytes between the two halves
+constexpr int kRGroupStride = kChunksPerGroup * kG1ChunkStride + kRHalfPad + 64;  // 2688
+constexpr int kRWindowBytes = kG1Ksub * kRGroupStride;                           // 43008
+
+__device__ __forceinline__ int r_chunk_offset(int c) {  // chunk c (0..31) within its group
+  return c * kG1ChunkStride + (c >= 16 ? kRHalfPad : 0);
+}
+
+// Sum over the 16 chunks of one half group of T_c[nibble].  base is the LDS
+// byte offset of the half's first table; the second 8 chunks follow the
+// first 8 at the same stride.
+__device__ __forceinline__ float r_half_sum(const uint2 bw, uint32_t base) {
+  constexpr int S = kG1ChunkStride / 4;  // chunk stride in floats
+  const uint32_t wd[2] = {bw.x, bw.y};
+  float s[4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t ev = (wd[q] << 2) & 0x3C3C3C3Cu;
+    const uint32_t od = (wd[q] >> 2) & 0x3C3C3C3Cu;
+    const int c = q * 8;
+    const float t0 = lds_at<0>(base, ev)[(c + 0) * S] + lds_at<0>(base, od)[(c + 1) * S];
+    const float t1 = lds_at<1>(base, ev)[(c + 2) * S] + lds_at<1>(base, od)[(c + 3) * S];
+    const float t2 = lds_at<2>(base, ev)[(c + 4) * S] + lds_at<2>(base, od)[(c + 5) * S];
+    const float t3 = lds_at<3>(base, ev)[(c + 6) * S] + lds_at<3>(base, od)[(c + 7) * S];
+    if (q == 0) {
+      s[0] = t0;
+      s[1] = t1;
+      s[2] = t2;
+      s[3] = t3;
+    } else {
+      s[0] += t0;
+      s[1] += t1;
+      s[2] += t2;
+      s[3] += t3;
+    }
+  }
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
+template <int NW, int P>
+struct G1Tile {
+  uint2 bits[NW][P];
+};
+
+// Scales and offsets of a tile are staged through LDS: in the caller's
+// [p][M][G] layout the 16 rows of a tile are one contiguous run of 16*G
+// values per plane, so consecutive threads load consecutive elements
+// (coalesced), and each lane then reads its own (row, group) values from
+// LDS.  Loading them per lane straight from memory instead touches one
+// cache line per row for every 2-byte value and more than doubles the
+// kernel's time.
+template <typename T, int NW, int P, int TMAX>
+__global__ __launch_bounds__(kRThreads) void gemv_res_kernel(
+    const uint4 *__restrict__ bits, const T *__restrict__ alpha, const T *__restrict__ zero,
+    const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT) {
+  constexpr int kMaxG = NW * kG1Ksub;
+  __shared__ __attribute__((aligned(16))) char lut[NW * kRWindowBytes];
+  __shared__ float gsum[NW * kG1Ksub];
+  __shared__ float part[kRWaves][TMAX][kTileRows];
+  // staged scales: [tile][plane P = offsets][row][group]; rows padded to an
+  // odd number of words so the 16 rows x 2 groups one wavefront reads hit
+  // distinct banks
+  __shared__ uint32_t scl[TMAX][P + 1][kTileRows][kMaxG + 1];
+  using Tile = G1Tile<NW, P>;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int hs = wave * 4 + (lane >> 4);  // half-group slot 0..31
+  const int gw = hs >> 1;                 // group within a window
+  const int half = hs & 1;
+  const int nt = (MT - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // my tiles
+  const size_t plane_stride = (size_t)MT * G * kTileRows;  // in uint4
+  const size_t MG = (size_t)M * G;
+  const uint2 *bits2 = reinterpret_cast<const uint2 *>(bits);
+
+  // ---- activations for every window's tables: thread tid builds chunk tid
+  typename Act<T>::raw xr[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int j = min(w * kG1Ksub + tid / kChunksPerGroup, G - 1);
+    xr[w] = Act<T>::load(x + (size_t)j * kGroup + (tid % kChunksPerGroup) * 4);
+  }
+
+  // ---- scales and offsets first (they are small and the staging below waits
+  // for them); element e of a tile's (plane, 16 x G) run
+  constexpr int kScl = (P + 1) * kTileRows * kMaxG;           // per tile, upper bound
+  constexpr int kSclPerThread = (kScl + kRThreads - 1) / kRThreads;
+  uint32_t sv[TMAX][kSclPerThread];
+  const int run = kTileRows * G;  // values per plane per tile
+#pragma unroll
+  for (int k = 0; k < TMAX; ++k) {
+    const int m0 = ((int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x) * kTileRows;
+#pragma unroll
+    for (int u = 0; u < kSclPerThread; ++u) {
+      const int e = min(tid + u * kRThreads, (P + 1) * run - 1);
+      const int b = e / run;  // plane, or P for the offsets
+      const int rem = e - b * run;
+      const int row = min(m0 + rem / G, M - 1);
+      const int g = rem % G;
+      const T *src = b < P ? alpha + b * MG : zero;
+      sv[k][u] = load_raw(src + (size_t)row * G + g);
+    }
+  }
+
+  // ---- then the sign words, tile by tile, so tile k's lookups wait only for
+  // the loads up to tile k (past my last tile: my last tile again,
+  // lines already in flight, so the load phase stays branch-free)
+  Tile tiles[TMAX];
+#pragma unroll
+  for (int k = 0; k < TMAX; ++k) {
+    const int t = (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int js = min(w * kG1Ksub + gw, G - 1);
+      const size_t q = (((size_t)t * G + js) * kTileRows + r) * 2 + half;  // uint2 index
+#pragma unroll
+      for (int i = 0; i < P; ++i) tiles[k].bits[w][i] = bits2[i * plane_stride * 2 + q];
+    }
+  }
+
+  // ---- build every window's tables and group sums
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    float f[4];
+    Act<T>::cvt(xr[w], f);
+    float4 v[4];
+    chunk_entries(f, v);
+    float4 *dst = reinterpret_cast<float4 *>(lut + w * kRWindowBytes +
+                                             (tid / kChunksPerGroup) * kRGroupStride +
+                                             r_chunk_offset(tid % kChunksPerGroup));
+    dst[0] = v[0];
+    dst[1] = v[1];
+    dst[2] = v[2];
+    dst[3] = v[3];
+    float cs = (f[0] + f[1]) + (f[2] + f[3]);
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) cs += __shfl_xor(cs, off);
+    if ((tid & 31) == 0) gsum[w * kG1Ksub + tid / 32] = cs;
+  }
+#pragma unroll
+  for (int k = 0; k < TMAX; ++k)
+#pragma unroll
+    for (int u = 0; u < kSclPerThread; ++u) {
+      const int e = tid + u * kRThreads;
+      if (e < (P + 1) * run) {
+        const int b = e / run;
+        const int rem = e - b * run;
+        scl[k][b][rem / G][rem % G] = sv[k][u];
+      }
+    }
+  __syncthreads();
+
+  auto consume = [&](int k, const Tile &o) -> float {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int j = w * kG1Ksub + gw;
+      if (j < G) {
+        const uint32_t base = lds_addr(lut + w * kRWindowBytes + gw * kRGroupStride +
+                                       r_chunk_offset(16 * half));
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+          a = fmaf(raw_to_float<T>(scl[k][i][r][j]), r_half_sum(o.bits[w][i], base), a);
+        if (half == 0) a = fmaf(raw_to_float<T>(scl[k][P][r][j]), gsum[j], a);
+      }
+    }
+    return a;
+  };
+
+  float acc[TMAX];
+#pragma unroll
+  for (int k = 0; k < TMAX; ++k) {
+    acc[k] = 0.f;
+    if (k < nt) acc[k] = consume(k, tiles[k]);
+  }
+
+  // ---- reduce the 32 slot partials of each row of each tile, fixed order
+#pragma unroll
+  for (int k = 0; k < TMAX; ++k) {
+    acc[k] += __shfl_xor(acc[k], 16);
+    acc[k] += __shfl_xor(acc[k], 32);
+    if (lane < 16) part[wave][k][lane] = acc[k];
+  }
+  __syncthreads();
+  if (tid < TMAX * kTileRows) {
+    const int k = tid / kTileRows;
+    const int rr = tid % kTileRows;
+    const int mm = ((int)blockIdx.x + k * (int)gridDim.x) * kTileRows + rr;
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kRWaves; ++v) sum += part[v][k][rr];
+    if (k < nt && mm < M) y[mm] = (T)sum;
+  }
+}
+
+int compute_units() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+template <typename T, int NW, int TMAX>
+void gemv_res_launch(dim3 grid, hipStream_t s, const uint4 *b4, const T *a, const T *z,
+                     const T *xx, T *yy, int M, int G, int MT, int p) {
+  switch (p) {
+    case 1:
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 1, TMAX>), grid, dim3(kRThreads), 0, s, b4, a,
+                         z, xx, yy, M, G, MT);
+      break;
+    case 2:
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 2, TMAX>), grid, dim3(kRThreads), 0, s, b4, a,
+                         z, xx, yy, M, G, MT);
+      break;
+    case 3:
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 3, TMAX>), grid, dim3(kRThreads), 0, s, b4, a,
+                         z, xx, yy, M, G, MT);
+      break;
+    default:
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 4, TMAX>), grid, dim3(kRThreads), 0, s, b4, a,
+                         z, xx, yy, M, G, MT);
+      break;
+  }
+}
+
+template <typename T, int NW>
+void gemv_res_tiles(hipStream_t s, const uint4 *b4, const T *a, const T *z, const T *xx, T *yy,
+                    int M, int G, int MT, int p) {
+  const int cus = compute_units();
+  const int tmax = (MT + cus - 1) / cus;
+  if (tmax <= 1)
+    gemv_res_launch<T, NW, 1>(dim3(MT), s, b4, a, z, xx, yy, M, G, MT, p);
+  else if (tmax <= 2)
+    gemv_res_launch<T, NW, 2>(dim3((MT + 1) / 2), s, b4, a, z, xx, yy, M, G, MT, p);
+  else
+    gemv_res_launch<T, NW, 4>(dim3((MT + 3) / 4 > cus ? (MT + 3) / 4 : cus), s, b4, a, z, xx, yy,
+                              M, G, MT, p);
+}
+
 template <typename T>
 hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *alpha,
                          const void *zero, const void *x, void *y, hipStream_t s) {
@@ -293,15 +580,33 @@ hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *
   const T *z = static_cast<const T *>(zero);
   const T *xx = static_cast<const T *>(x);
   T *yy = static_cast<T *>(y);
+  if (nwin <= 1) {
+    gemv_res_tiles<T, 1>(s, b4, a, z, xx, yy, M, G, MT, p);
+    return hipGetLastError();
+  }
+  if (nwin <= 2) {
+    gemv_res_tiles<T, 2>(s, b4, a, z, xx, yy, M, G, MT, p);
+    return hipGetLastError();
+  }
+  // larger K: one tile per workgroup, tables built window by window
   dim3 grid(MT), block(kG1Threads);
-  if (nwin <= 1)
-    hipLaunchKernelGGL((gemv_lut_kernel<T, 1>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT, p);
-  else if (nwin <= 2)
-    hipLaunchKernelGGL((gemv_lut_kernel<T, 2>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT, p);
-  else if (nwin <= 4)
-    hipLaunchKernelGGL((gemv_lut_kernel<T, 4>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT, p);
+#define BCQ_G1P(W, L, PP)                                                                 \
+  hipLaunchKernelGGL((gemv_lut_kernel<T, W, L, PP>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT)
+#define BCQ_G1(W, L)            \
+  switch (p) {                  \
+    case 1: BCQ_G1P(W, L, 1); break; \
+    case 2: BCQ_G1P(W, L, 2); break; \
+    case 3: BCQ_G1P(W, L, 3); break; \
+    default: BCQ_G1P(W, L, 4); break; \
+  }
+  if (nwin <= 4)
+    BCQ_G1(4, false)
+  else if (nwin <= 8)
+    BCQ_G1(8, false)
   else
-    hipLaunchKernelGGL((gemv_lut_kernel<T, 8>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT, p);
+    BCQ_G1(8, true)
+#undef BCQ_G1P
+#undef BCQ_G1
   return hipGetLastError();
 }
 
@@ -382,11 +687,25 @@ __device__ __forceinline__ void sk_plane_sums(const uint4 bw, uint32_t base, flo
   }
 }
 
-template <typename T, int NB>
+// Operands of one window, double-buffered across the window loop.
+template <typename T, int NB, int P>
+struct SkOperands {
+  uint4 bits[P];
+  typename Act<T>::raw x[2][NB];  // this lane's two chunks of every request's activations
+  uint32_t alpha[NB][P];
+  uint32_t zero[NB];
+};
+
+// P is the largest precision of the launch (a template argument, so the plane
+// loops are compile-time).  The load phase has no branches: lanes past the last
+// group or row, windows past the end and planes beyond a request's precision
+// read clamped in-range addresses whose values are never used.
+template <typename T, int NB, int P>
 __global__ __launch_bounds__(kSkThreads) void skinny_lut_kernel(
-    const uint4 *__restrict__ bits, ReqTables tabs, int nreq, int p_max,
-    const T *__restrict__ x, int ldx, T *__restrict__ y, int ldy, int M, int G, int MT) {
+    const uint4 *__restrict__ bits, ReqTables tabs, int nreq, const T *__restrict__ x, int ldx,
+    T *__restrict__ y, int ldy, int M, int G, int MT) {
   using Gm = SkGeom<NB>;
+  using Ops = SkOperands<T, NB, P>;
   __shared__ __attribute__((aligned(16))) char lut[Gm::window_bytes];
   __shared__ float gsum[kSkKsub][NB];
 
@@ -396,6 +715,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_lut_kernel(
   const int tile = blockIdx.x;
   const int m = tile * kTileRows + r;
   const bool row_ok = m < M;
+  const int m_safe = min(m, M - 1);
   const int nwin = (G + kSkKsub - 1) / kSkKsub;
   const size_t plane_stride = (size_t)MT * G * kTileRows;
   const uint4 *tbits = bits + (size_t)tile * G * kTileRows + r;
@@ -405,49 +725,33 @@ __global__ __launch_bounds__(kSkThreads) void skinny_lut_kernel(
 #pragma unroll
   for (int q = 0; q < NB; ++q) acc[q] = 0.f;
 
-  // registers for the window being consumed; the next window is prefetched
-  uint4 bw[BCQ_MAX_PLANES];
-  typename Act<T>::raw xr[2][NB];
-
-  auto load_window = [&](int w, uint4 (&b)[BCQ_MAX_PLANES], typename Act<T>::raw (&xv)[2][NB]) {
-    const int j = w * kSkKsub + ks;
+  auto fetch = [&](int w_in, Ops &o) {
+    const int w = min(w_in, nwin - 1);
+    const int js = min(w * kSkKsub + ks, G - 1);
 #pragma unroll
-    for (int i = 0; i < BCQ_MAX_PLANES; ++i)
-      b[i] = (w < nwin && j < G && i < p_max) ? tbits[i * plane_stride + (size_t)j * kTileRows]
-                                               : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < P; ++i) o.bits[i] = tbits[i * plane_stride + (size_t)js * kTileRows];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = lane + h * kSkThreads;
-      const int jc = w * kSkKsub + c / kChunksPerGroup;
+      const int jc = min(w * kSkKsub + c / kChunksPerGroup, G - 1);
 #pragma unroll
-      for (int q = 0; q < NB; ++q)
-        xv[h][q] = (w < nwin && jc < G && q < nreq)
-                       ? Act<T>::load(x + (size_t)q * ldx + ((size_t)w * Gm::window_chunks + c) * 4)
-                       : Act<T>::zero();
+      for (int q = 0; q < NB; ++q) {
+        const int qs = min(q, nreq - 1);
+        o.x[h][q] = Act<T>::load(x + (size_t)qs * ldx + (size_t)jc * kGroup + (c % kChunksPerGroup) * 4);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int pq = max(tabs.p[q], 1);
+      const T *a = static_cast<const T *>(tabs.alpha[q]);
+#pragma unroll
+      for (int i = 0; i < P; ++i)
+        o.alpha[q][i] = load_raw(a + min(i, pq - 1) * MG + (size_t)m_safe * G + js);
+      o.zero[q] = load_raw(static_cast<const T *>(tabs.zero[q]) + (size_t)m_safe * G + js);
     }
   };
 
-  load_window(0, bw, xr);
-  for (int w = 0; w < nwin; ++w) {
-    const int j = w * kSkKsub + ks;
-    const bool gok = j < G && row_ok;
-    // this window's scales and offsets: issued now, consumed after the lookups
-    T al[NB][BCQ_MAX_PLANES];
-    T zz[NB];
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-#pragma unroll
-      for (int i = 0; i < BCQ_MAX_PLANES; ++i)
-        al[q][i] = (gok && i < tabs.p[q])
-                       ? static_cast<const T *>(tabs.alpha[q])[i * MG + (size_t)m * G + j]
-                       : T(0);
-      zz[q] = (gok && tabs.p[q] > 0) ? static_cast<const T *>(tabs.zero[q])[(size_t)m * G + j]
-                                     : T(0);
-    }
-    uint4 nbw[BCQ_MAX_PLANES];
-    typename Act<T>::raw nxr[2][NB];
-    load_window(w + 1, nbw, nxr);  // prefetch (all-zero past the end)
-
+  auto consume = [&](int w, const Ops &o) {
     __syncthreads();  // the previous window's lookups are done with lut[]
     // ---- build tables for the 128 chunks of the window, NB requests each
     float cs[2][NB];
@@ -463,7 +767,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_lut_kernel(
 #pragma unroll
         for (int q = 0; q < L; ++q) {
           float f[4];
-          Act<T>::cvt(xr[h][hf * L + q], f);
+          Act<T>::cvt(o.x[h][hf * L + q], f);
           chunk_entries(f, v[q]);
           cs[h][hf * L + q] = (f[0] + f[1]) + (f[2] + f[3]);
         }
@@ -499,26 +803,36 @@ __global__ __launch_bounds__(kSkThreads) void skinny_lut_kernel(
     __syncthreads();
 
     // ---- lookups, then per-request scale and offset
-    if (gok) {
+    const int j = w * kSkKsub + ks;
+    if (j < G && row_ok) {
       const uint32_t base = lds_addr(lut + ks * Gm::group_stride);
 #pragma unroll
-      for (int i = 0; i < BCQ_MAX_PLANES; ++i) {
-        if (i < p_max) {
-          float ps[NB];
-          sk_plane_sums<NB>(bw[i], base, ps);
+      for (int i = 0; i < P; ++i) {
+        float ps[NB];
+        sk_plane_sums<NB>(o.bits[i], base, ps);
 #pragma unroll
-          for (int q = 0; q < NB; ++q) acc[q] = fmaf((float)al[q][i], ps[q], acc[q]);
+        for (int q = 0; q < NB; ++q) {
+          const float a = i < tabs.p[q] ? raw_to_float<T>(o.alpha[q][i]) : 0.f;
+          acc[q] = fmaf(a, ps[q], acc[q]);
         }
       }
 #pragma unroll
-      for (int q = 0; q < NB; ++q) acc[q] = fmaf((float)zz[q], gsum[ks][q], acc[q]);
+      for (int q = 0; q < NB; ++q) {
+        const float z = tabs.p[q] > 0 ? raw_to_float<T>(o.zero[q]) : 0.f;
+        acc[q] = fmaf(z, gsum[ks][q], acc[q]);
+      }
     }
-#pragma unroll
-    for (int i = 0; i < BCQ_MAX_PLANES; ++i) bw[i] = nbw[i];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int q = 0; q < NB; ++q) xr[h][q] = nxr[h][q];
+  };
+
+  // ping-pong over two operand buffers: window w+1 loads while window w computes
+  Ops A, B;
+  fetch(0, A);
+  for (int w = 0; w < nwin; w += 2) {
+    fetch(w + 1, B);
+    consume(w, A);
+    if (w + 1 >= nwin) break;  // uniform
+    fetch(w + 2, A);
+    consume(w + 1, B);
   }
 
   // ---- reduce the 4 K-sub partials of each row (lanes r, r+16, r+32, r+48)
@@ -534,6 +848,30 @@ __global__ __launch_bounds__(kSkThreads) void skinny_lut_kernel(
   }
 }
 
+template <typename T, int NB>
+void skinny_launch_p(dim3 grid, dim3 block, hipStream_t s, const uint4 *b4, const ReqTables &t,
+                     int nreq, const T *xx, int ldx, T *yy, int ldy, int M, int G, int MT,
+                     int p_max) {
+  switch (p_max) {
+    case 1:
+      hipLaunchKernelGGL((skinny_lut_kernel<T, NB, 1>), grid, block, 0, s, b4, t, nreq, xx, ldx,
+                         yy, ldy, M, G, MT);
+      break;
+    case 2:
+      hipLaunchKernelGGL((skinny_lut_kernel<T, NB, 2>), grid, block, 0, s, b4, t, nreq, xx, ldx,
+                         yy, ldy, M, G, MT);
+      break;
+    case 3:
+      hipLaunchKernelGGL((skinny_lut_kernel<T, NB, 3>), grid, block, 0, s, b4, t, nreq, xx, ldx,
+                         yy, ldy, M, G, MT);
+      break;
+    default:
+      hipLaunchKernelGGL((skinny_lut_kernel<T, NB, 4>), grid, block, 0, s, b4, t, nreq, xx, ldx,
+                         yy, ldy, M, G, MT);
+      break;
+  }
+}
+
 template <typename T>
 hipError_t skinny_dispatch(const uint32_t *bits, int M, int K, int p_max, const ReqTables &t,
                            int nreq, const void *x, int ldx, void *y, int ldy, hipStream_t s) {
@@ -544,14 +882,11 @@ hipError_t skinny_dispatch(const uint32_t *bits, int M, int K, int p_max, const 
   T *yy = static_cast<T *>(y);
   dim3 grid(MT), block(kSkThreads);
   if (nreq <= 2)
-    hipLaunchKernelGGL((skinny_lut_kernel<T, 2>), grid, block, 0, s, b4, t, nreq, p_max, xx, ldx,
-                       yy, ldy, M, G, MT);
+    skinny_launch_p<T, 2>(grid, block, s, b4, t, nreq, xx, ldx, yy, ldy, M, G, MT, p_max);
   else if (nreq <= 4)
-    hipLaunchKernelGGL((skinny_lut_kernel<T, 4>), grid, block, 0, s, b4, t, nreq, p_max, xx, ldx,
-                       yy, ldy, M, G, MT);
+    skinny_launch_p<T, 4>(grid, block, s, b4, t, nreq, xx, ldx, yy, ldy, M, G, MT, p_max);
   else
-    hipLaunchKernelGGL((skinny_lut_kernel<T, 8>), grid, block, 0, s, b4, t, nreq, p_max, xx, ldx,
-                       yy, ldy, M, G, MT);
+    skinny_launch_p<T, 8>(grid, block, s, b4, t, nreq, xx, ldx, yy, ldy, M, G, MT, p_max);
   return hipGetLastError();
 }
 
