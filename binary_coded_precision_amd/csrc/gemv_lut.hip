@@ -373,7 +373,7 @@ struct G1Tile {
 // LDS.  Loading them per lane straight from memory instead touches one
 // cache line per row for every 2-byte value and more than doubles the
 // kernel's time.
-template <typename T, int NW, int P, int TMAX>
+template <typename T, int NW, int P, int TMAX, int AHEAD = 1>
 __global__ __launch_bounds__(kRThreads) void gemv_res_kernel(
     const uint4 *__restrict__ bits, const T *__restrict__ alpha, const T *__restrict__ zero,
     const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT) {
@@ -408,41 +408,44 @@ __global__ __launch_bounds__(kRThreads) void gemv_res_kernel(
   }
 
   // ---- scales and offsets first (they are small and the staging below waits
-  // for them); element e of a tile's (plane, 16 x G) run
-  constexpr int kScl = (P + 1) * kTileRows * kMaxG;           // per tile, upper bound
-  constexpr int kSclPerThread = (kScl + kRThreads - 1) / kRThreads;
-  uint32_t sv[TMAX][kSclPerThread];
-  const int run = kTileRows * G;  // values per plane per tile
+  // for them).  Thread (row tid / 32, group tid % 32) owns one position of
+  // each tile's 16 x G run per plane: consecutive threads read consecutive
+  // groups of a row, so the loads are coalesced, and no index needs a division.
+  static_assert(kRThreads >= kTileRows * kMaxG, "one staging position per thread");
+  const bool sok = tid < kTileRows * kMaxG;  // threads past the 16 x kMaxG positions idle
+  const int srow = min(tid / kMaxG, kTileRows - 1);
+  const int sg = tid % kMaxG;
+  const int sgc = min(sg, G - 1);
+  uint32_t sv[TMAX][P + 1];
 #pragma unroll
   for (int k = 0; k < TMAX; ++k) {
-    const int m0 = ((int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x) * kTileRows;
+    const int row = min(((int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x) * kTileRows + srow,
+                        M - 1);
 #pragma unroll
-    for (int u = 0; u < kSclPerThread; ++u) {
-      const int e = min(tid + u * kRThreads, (P + 1) * run - 1);
-      const int b = e / run;  // plane, or P for the offsets
-      const int rem = e - b * run;
-      const int row = min(m0 + rem / G, M - 1);
-      const int g = rem % G;
-      const T *src = b < P ? alpha + b * MG : zero;
-      sv[k][u] = load_raw(src + (size_t)row * G + g);
-    }
+    for (int i = 0; i < P; ++i) sv[k][i] = load_raw(alpha + i * MG + (size_t)row * G + sgc);
+    sv[k][P] = load_raw(zero + (size_t)row * G + sgc);
   }
 
-  // ---- then the sign words, tile by tile, so tile k's lookups wait only for
-  // the loads up to tile k (past my last tile: my last tile again,
-  // lines already in flight, so the load phase stays branch-free)
-  Tile tiles[TMAX];
-#pragma unroll
-  for (int k = 0; k < TMAX; ++k) {
+  // ---- then tile 0's sign words.  Later tiles are requested only after the
+  // barrier below, AHEAD tiles in front of the one being looked up: the small
+  // loads the barrier waits for (x, scales) are otherwise queued behind every
+  // tile's sign words and the whole workgroup idles for most of the stream.
+  // (Past my last tile a fetch re-reads my own last tile: lines already in
+  // flight, so the load phase stays branch-free.)
+  constexpr int kAhead = AHEAD < TMAX - 1 ? AHEAD : TMAX - 1;
+  constexpr int kRing = kAhead + 1;
+  Tile tiles[kRing];
+  auto fetch = [&](int k, Tile &o) {
     const int t = (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const int js = min(w * kG1Ksub + gw, G - 1);
       const size_t q = (((size_t)t * G + js) * kTileRows + r) * 2 + half;  // uint2 index
 #pragma unroll
-      for (int i = 0; i < P; ++i) tiles[k].bits[w][i] = bits2[i * plane_stride * 2 + q];
+      for (int i = 0; i < P; ++i) o.bits[w][i] = bits2[i * plane_stride * 2 + q];
     }
-  }
+  };
+  fetch(0, tiles[0]);
 
   // ---- build every window's tables and group sums
 #pragma unroll
@@ -463,18 +466,15 @@ __global__ __launch_bounds__(kRThreads) void gemv_res_kernel(
     for (int off = 16; off >= 1; off >>= 1) cs += __shfl_xor(cs, off);
     if ((tid & 31) == 0) gsum[w * kG1Ksub + tid / 32] = cs;
   }
+  if (sok) {
 #pragma unroll
-  for (int k = 0; k < TMAX; ++k)
+    for (int k = 0; k < TMAX; ++k)
 #pragma unroll
-    for (int u = 0; u < kSclPerThread; ++u) {
-      const int e = tid + u * kRThreads;
-      if (e < (P + 1) * run) {
-        const int b = e / run;
-        const int rem = e - b * run;
-        scl[k][b][rem / G][rem % G] = sv[k][u];
-      }
-    }
+      for (int i = 0; i <= P; ++i) scl[k][i][srow][sg] = sv[k][i];
+  }
   __syncthreads();
+#pragma unroll
+  for (int k = 1; k <= kAhead; ++k) fetch(k, tiles[k]);
 
   auto consume = [&](int k, const Tile &o) -> float {
     float a = 0.f;
@@ -497,7 +497,8 @@ __global__ __launch_bounds__(kRThreads) void gemv_res_kernel(
 #pragma unroll
   for (int k = 0; k < TMAX; ++k) {
     acc[k] = 0.f;
-    if (k < nt) acc[k] = consume(k, tiles[k]);
+    if (k < nt) acc[k] = consume(k, tiles[k % kRing]);
+    if (k + kRing < TMAX) fetch(k + kRing, tiles[k % kRing]);  // refill the slot just read
   }
 
   // ---- reduce the 32 slot partials of each row of each tile, fixed order
