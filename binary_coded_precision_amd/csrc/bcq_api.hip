@@ -11,6 +11,7 @@ using bcq::kGroup;
 
 constexpr int32_t kMaxM = 1 << 24;
 constexpr int32_t kMaxK = 1 << 20;
+constexpr int32_t kDqMinBatch = 5;  // smallest fp16 batch sent to the decode kernel
 
 size_t dtype_size(bcq_dtype d) { return d == BCQ_F16 ? 2 : 4; }
 bool dtype_valid(bcq_dtype d) { return d == BCQ_F16 || d == BCQ_F32; }
@@ -74,32 +75,87 @@ bcq_status check_batch(const bcq_store *st, const void *X, int32_t b, int32_t ld
 bcq_status run_table_batches(const bcq_store *st, const int32_t *p_of, const char *X, int32_t b,
                              int32_t ldx, char *Y, int32_t ldy, hipStream_t stream) {
   const size_t es = dtype_size(st->scale_dtype);
+  const size_t mg = (size_t)st->M * (st->K / kGroup) * es;  // bytes of one [M][G] plane
   for (int32_t r0 = 0; r0 < b; r0 += bcq::kMaxReq) {
     const int n = (b - r0) < bcq::kMaxReq ? (b - r0) : bcq::kMaxReq;
-    bcq::ReqTables t{};
     int pmax = 0;
-    for (int q = 0; q < n; ++q) {
-      const int p = p_of[r0 + q];
-      t.p[q] = p;
-      t.alpha[q] = st->alpha[p];
-      t.zero[q] = st->zero[p];
-      pmax = p > pmax ? p : pmax;
+    for (int q = 0; q < n; ++q) pmax = p_of[r0 + q] > pmax ? p_of[r0 + q] : pmax;
+    // one staged array per plane of each distinct precision, plus its offsets
+    bcq::ReqTables t{};
+    for (int p = 1; p <= BCQ_MAX_PLANES; ++p) {
+      uint32_t mask = 0;
+      for (int q = 0; q < n; ++q)
+        if (p_of[r0 + q] == p) mask |= 1u << q;
+      if (mask == 0) continue;
+      for (int i = 0; i <= p; ++i) {
+        const char *base = static_cast<const char *>(i < p ? st->alpha[p] : st->zero[p]);
+        t.arr[t.n] = i < p ? base + i * mg : base;
+        t.slot[t.n] = i < p ? i : bcq::sk_zero_slot(pmax);
+        t.mask[t.n] = mask;
+        ++t.n;
+      }
     }
-    for (int q = n; q < bcq::kMaxReq; ++q) {
-      t.p[q] = 0;
-      t.alpha[q] = st->alpha[p_of[r0]];
-      t.zero[q] = st->zero[p_of[r0]];
-    }
+    for (int k = t.n; k < bcq::kMaxStage; ++k) t.arr[k] = t.arr[0];
     const char *xr = X + (size_t)r0 * ldx * es;
     char *yr = Y + (size_t)r0 * ldy * es;
     hipError_t e;
     if (n == 1)
-      e = bcq::launch_gemv_lut(st->bits, st->M, st->K, t.p[0], t.alpha[0], t.zero[0], xr, yr,
-                               st->scale_dtype, stream);
+      e = bcq::launch_gemv_lut(st->bits, st->M, st->K, pmax, st->alpha[pmax], st->zero[pmax], xr,
+                               yr, st->scale_dtype, stream);
     else
       e = bcq::launch_skinny_lut(st->bits, st->M, st->K, pmax, t, n, xr, ldx, yr, ldy,
                                  st->scale_dtype, stream);
     if (e != hipSuccess) return BCQ_ERR_HIP;
+  }
+  return BCQ_OK;
+}
+
+// fp16 requests through the decode kernel, up to kDqMaxReq per launch.  When
+// every precision used reads the same scale chain (alpha[p] and zero[p] alias
+// those of the largest p -- the shared-store layout), one launch serves all its
+// requests and the planes are read once; each request takes the weight after
+// its own p planes.  Otherwise the requests are grouped by precision and each
+// group reads its own tables.  A group of one request goes to the batch-1
+// kernel.
+bcq_status run_dq_batches(const bcq_store *st, const int32_t *p_of, const char *X, int32_t b,
+                          int32_t ldx, char *Y, int32_t ldy, hipStream_t stream) {
+  const size_t es = 2;
+  int pmax = 0;
+  for (int32_t r = 0; r < b; ++r) pmax = p_of[r] > pmax ? p_of[r] : pmax;
+  bool shared = true, uniform = true;
+  for (int32_t r = 0; r < b; ++r) {
+    shared = shared && st->alpha[p_of[r]] == st->alpha[pmax] && st->zero[p_of[r]] == st->zero[pmax];
+    uniform = uniform && p_of[r] == pmax;
+  }
+  // a launch mixing precisions holds fewer requests (see kDqMaxMixedReq)
+  const int cap = (shared && !uniform) ? bcq::kDqMaxMixedReq : bcq::kDqMaxReq;
+  // groups: one (chain precision, request subset) per launch
+  for (int chain = shared ? pmax : 1; chain <= pmax; ++chain) {
+    bcq::DqRequests rq{};
+    int p0 = 0;  // precision of the first request of the pending launch
+    auto flush = [&]() -> bcq_status {
+      if (rq.n == 0) return BCQ_OK;
+      hipError_t e;
+      if (rq.n == 1)
+        e = bcq::launch_gemv_lut(st->bits, st->M, st->K, p0, st->alpha[p0], st->zero[p0],
+                                 X + (size_t)rq.row[0] * ldx * es,
+                                 Y + (size_t)rq.row[0] * ldy * es, st->scale_dtype, stream);
+      else
+        e = bcq::launch_skinny_dq(st->bits, st->M, st->K, st->alpha[chain], st->zero[chain], rq,
+                                  X, ldx, Y, ldy, stream);
+      rq = bcq::DqRequests{};
+      p0 = 0;
+      return e == hipSuccess ? BCQ_OK : BCQ_ERR_HIP;
+    };
+    for (int32_t r = 0; r < b; ++r) {
+      if (!shared && p_of[r] != chain) continue;
+      if (rq.n == 0) p0 = p_of[r];
+      rq.row[rq.n] = r;
+      rq.at[p_of[r] - 1] |= 1u << rq.n;
+      ++rq.n;
+      if (rq.n == cap) BCQ_TRY(flush());
+    }
+    BCQ_TRY(flush());
   }
   return BCQ_OK;
 }
@@ -173,6 +229,11 @@ bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int
   }
   int32_t ps[BCQ_MAX_BATCH];
   for (int32_t r = 0; r < b; ++r) ps[r] = p;
+  // fp16 batches of 5..15 decode each weight once for all requests; below
+  // that the per-request table lookups cost less than the decode (measured on
+  // gfx950 at 4096 and 14336 rows)
+  if (store->scale_dtype == BCQ_F16 && b >= kDqMinBatch)
+    return run_dq_batches(store, ps, Xc, b, ldx, Yc, ldy, stream);
   return run_table_batches(store, ps, Xc, b, ldx, Yc, ldy, stream);
 }
 

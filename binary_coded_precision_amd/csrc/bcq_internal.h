@@ -16,13 +16,34 @@ constexpr int kGroup = BCQ_GROUP;
 
 inline int row_tiles(int M) { return (M + kTileRows - 1) / kTileRows; }
 
-// Per-request description used by the batched kernels: each request has its
-// own precision and its own scale/offset tables (AnyBCQ per-request precision).
-constexpr int kMaxReq = 8;  // requests handled by one launch of a batched kernel
+// Scale description used by the batched table kernel.  Each request of a
+// launch has its own precision and reads the scale/offset tables of that
+// precision (AnyBCQ per-request precision).  The host lists every distinct
+// [M][G] array the launch needs -- one per plane of each distinct alpha[p],
+// plus zero[p] -- with the slot it fills and the requests that read it; the
+// kernel stages each array once per window and fans it out to those requests.
+constexpr int kMaxReq = 8;     // requests handled by one launch of the batched kernel
+constexpr int kMaxStage = 16;  // distinct arrays per launch (at most 4+3+2+1 + 4 offsets)
 struct ReqTables {
-  const void *alpha[kMaxReq];  // [p_r][M][G]
-  const void *zero[kMaxReq];   // [M][G]
-  int p[kMaxReq];              // precision of each request (0 for padding slots)
+  const void *arr[kMaxStage];  // [M][G] array: one plane of some alpha[p], or zero[p]
+  int slot[kMaxStage];         // 0..pmax-1: plane index; pmax: offsets
+  uint32_t mask[kMaxStage];    // bit q set: request q of the launch reads this array
+  int n;                       // arrays in use, 1..kMaxStage
+};
+// The batched kernel works on planes in pairs, so it reserves an even number
+// of plane slots; the offsets go in the slot after them.
+constexpr int sk_zero_slot(int pmax) { return 2 * ((pmax + 1) / 2); }
+
+// Requests of one launch of the fp16 decode kernel.  All requests read one
+// scale chain (alpha [P][M][G], zero [M][G]); request q takes the weight
+// decoded from the first p[q] planes of it.  A launch holds up to kDqMaxReq
+// requests of one precision, or up to kDqMaxMixedReq of several.
+constexpr int kDqMaxReq = 16;
+constexpr int kDqMaxMixedReq = 8;
+struct DqRequests {
+  int row[kDqMaxReq];           // row of X and of Y holding request q
+  uint32_t at[BCQ_MAX_PLANES];  // bit q of at[i] set: request q has precision i + 1
+  int n;                        // requests in use, 1..kDqMaxReq
 };
 
 // ---- launchers (return hipGetLastError() after the launch) ----
@@ -41,6 +62,12 @@ hipError_t launch_gemv_lut(const uint32_t *bits, int M, int K, int p, const void
 hipError_t launch_skinny_lut(const uint32_t *bits, int M, int K, int p_max, const ReqTables &t,
                              int nreq, const void *x, int ldx, void *y, int ldy, bcq_dtype dt,
                              hipStream_t s);
+
+// Batched fp16 products with 2..16 requests per launch: weights decoded once
+// per launch on the vector ALUs and reused by every request.
+hipError_t launch_skinny_dq(const uint32_t *bits, int M, int K, const void *alpha,
+                            const void *zero, const DqRequests &rq, const void *x, int ldx,
+                            void *y, int ldy, hipStream_t s);
 
 // Batched products with >= 16 requests at one precision: fp16 dequantised
 // tiles on the matrix cores.

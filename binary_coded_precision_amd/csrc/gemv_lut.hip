@@ -148,6 +148,19 @@ __device__ __forceinline__ lds_float *lds_at(uint32_t base, uint32_t v) {
   return (lds_float *)(size_t)add_byte<B>(base, v);
 }
 
+// Sum over the 8 consecutive lanes of an aligned block, returned in all 8 (DPP
+// lane moves within quad and half-row, no LDS traffic).  The additions run in
+// the same pairwise order in every lane, so all 8 hold identical bits.
+__device__ __forceinline__ float sum8_lanes(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF,
+                                                         0xF, true));  // quad_perm 1,0,3,2
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF,
+                                                         0xF, true));  // quad_perm 2,3,0,1
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF,
+                                                         0xF, true));  // row_half_mirror
+  return v;
+}
+
 // ---------------------------------------------------------------- batch 1
 
 constexpr int kG1Threads = 256;
@@ -613,264 +626,387 @@ hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *
 
 // ---------------------------------------------------------------- batches of 2..8
 //
-// One wavefront per workgroup: 16 rows x 4 groups per window.  Table entries
-// hold NB fp32 values (one per request) side by side, so one address serves NB
-// requests.  Requests carry their own precision and scale tables, which is
-// how per-request precision costs nothing extra: planes up to the largest
-// precision are read once, and a request simply stops accumulating after its
-// own p (AnyBCQ paper notes, per-request precision; abstract: negligible
-// overhead for per-request selection).
+// A workgroup of four wavefronts owns a tile of 16 rows and walks K in
+// windows of 4 groups; wavefront v handles group v of the window.  Lane
+// (r, k, c) takes row r, plane 2u + k of each plane pair u, and the 64-column
+// half c of the group (two 32-bit sign words per plane).  Table entries hold
+// the sums of up to 4 requests side by side, so one lookup address serves
+// every request of the launch.
+//
+// Why planes and not column quarters across the lanes: a 16-byte LDS read is
+// conflict-free only when the 32 lanes of each half-wavefront read within one
+// 256-byte table (measured on gfx950: four tables per wavefront cost 46% bank
+// conflicts and 1.85x the cycles per read).  Lanes of a half-wavefront here
+// share the column half, so at every lookup they read the same chunk's table,
+// two planes x 16 rows at random entries.
+//
+// Per-request precision (AnyBCQ paper notes, per-request precision; the
+// abstract's negligible-overhead selection): planes up to the largest
+// precision are read once for all requests, and a request whose precision is
+// lower gets a zero scale for the planes it does not use.  Scales are staged
+// per window through LDS: each distinct [M][G] array of the launch (a plane
+// of alpha[p], or zero[p]) is loaded once and written into the slots of the
+// requests that read it; slots that nothing writes stay zero from the start.
+//
+// The offset term z * S_j is split over the four lanes of a row: each adds z
+// times one quarter's activation sum, so no lane needs a branch (the four
+// quarter terms sum to z * S_j).  With an odd largest precision the last pair
+// has one plane; its other lanes read a clamped plane and a zero scale.
 
-constexpr int kSkThreads = 64;
-constexpr int kSkKsub = 4;  // groups per window
+constexpr int kSkThreads = 256;
+constexpr int kSkGroups = 4;                                // groups per window
+constexpr int kSkChunks = kSkGroups * kChunksPerGroup;      // 128 tables per window
+constexpr int kSkQuarters = kGroup / 32;                    // 32-column quarters per group
+constexpr int kSkConcurrent = 2;                            // windows in flight per workgroup
+constexpr int kSkDepth = 2;                                 // operand sets in the prefetch ring
 
 // Table geometry for NB requests.  An entry holds up to 4 requests' fp32 sums
-// side by side (16 B); with 8 requests a chunk holds two such 16-entry halves,
-// so the byte offset of an entry is always nibble * entry_bytes and fits the
-// byte-select add.  Chunks sit at a stride of (halves * 16 entries + 1) x 16 B
-// so 16-byte writes by consecutive chunks spread over the banks.
+// side by side; with 8 requests a chunk holds two 16-entry halves, so the
+// byte offset of an entry is nibble * entry_bytes and always fits the
+// byte-select add.  The chunk stride staggers consecutive chunks over the LDS
+// banks for the writes of the build.
 template <int NB>
 struct SkGeom {
-  static constexpr int lanes = NB < 4 ? NB : 4;                      // requests per entry
-  static constexpr int halves = NB / lanes;                          // 1 or 2
-  static constexpr int entry_bytes = lanes * 4;                      // 8 or 16
-  static constexpr int half_bytes = kEntries * entry_bytes;          // 128 or 256
-  static constexpr int chunk_stride = halves * half_bytes + 16;
+  static constexpr int per_entry = NB < 4 ? NB : 4;              // requests per entry
+  static constexpr int entry_bytes = per_entry * 4;              // 8 or 16
+  static constexpr int half_bytes = kEntries * entry_bytes;      // 128 or 256
+  static constexpr int halves = NB / per_entry;                  // 1 or 2
+  static constexpr int chunk_stride = halves * half_bytes + (NB == 2 ? 8 : 16);
   static constexpr int group_stride = kChunksPerGroup * chunk_stride;
-  static constexpr int window_bytes = kSkKsub * group_stride;
-  static constexpr int window_chunks = kSkKsub * kChunksPerGroup;    // 128
+  static constexpr int lut_bytes = kSkGroups * group_stride;
+  static constexpr int rpt = NB / 2;                             // requests built per thread
 };
 
-// Per-request plane sums over one group: s[q] += T_c[nibble c] for request q.
 template <int NB>
-__device__ __forceinline__ void sk_plane_sums(const uint4 bw, uint32_t base, float (&s)[NB]) {
-  using Gm = SkGeom<NB>;
+__device__ __forceinline__ void sk_read(uint32_t addr, float *v) {
+  if constexpr (NB == 2) {
+    const f32x2 a = *(lds_float2 *)(size_t)addr;
+    v[0] = a.x;
+    v[1] = a.y;
+  } else {
 #pragma unroll
-  for (int q = 0; q < NB; ++q) s[q] = 0.f;
-  const uint32_t wd[4] = {bw.x, bw.y, bw.z, bw.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t ev, od;  // nibble * entry_bytes, one per byte (even nibbles, odd nibbles)
-    if constexpr (Gm::entry_bytes == 8) {
-      ev = (wd[q] << 3) & 0x78787878u;
-      od = (wd[q] >> 1) & 0x78787878u;
-    } else {
-      ev = (wd[q] << 4) & 0xF0F0F0F0u;
-      od = wd[q] & 0xF0F0F0F0u;
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int c = q * 8 + 2 * b + e;
-        uint32_t a;
-        if (b == 0) a = add_byte<0>(base, e ? od : ev);
-        else if (b == 1) a = add_byte<1>(base, e ? od : ev);
-        else if (b == 2) a = add_byte<2>(base, e ? od : ev);
-        else a = add_byte<3>(base, e ? od : ev);
-        const uint32_t off = c * Gm::chunk_stride;
-        if constexpr (Gm::lanes == 2) {
-          const f32x2 v = *(lds_float2 *)(size_t)(a + off);
-          s[0] += v.x;
-          s[1] += v.y;
-        } else {
-#pragma unroll
-          for (int h = 0; h < Gm::halves; ++h) {
-            const f32x4 v = *(lds_float4 *)(size_t)(a + off + h * Gm::half_bytes);
-            s[4 * h + 0] += v.x;
-            s[4 * h + 1] += v.y;
-            s[4 * h + 2] += v.z;
-            s[4 * h + 3] += v.w;
-          }
-        }
-      }
+    for (int h = 0; h < NB / 4; ++h) {
+      const f32x4 a = *(lds_float4 *)(size_t)(addr + h * SkGeom<NB>::half_bytes);
+      v[4 * h + 0] = a.x;
+      v[4 * h + 1] = a.y;
+      v[4 * h + 2] = a.z;
+      v[4 * h + 3] = a.w;
     }
   }
 }
 
+// The table entries of one 32-column quarter: t[c] = T_c[nibble c] for its 8
+// chunks c, all requests.  base is the LDS byte offset of the quarter's first
+// table.  All 8 reads are issued before any is used.
+template <int NB>
+__device__ __forceinline__ void sk_quarter_reads(uint32_t wd, uint32_t base, float (&t)[8][NB]) {
+  using Gm = SkGeom<NB>;
+  uint32_t ev, od;  // nibble * entry_bytes, one per byte (even nibbles, odd nibbles)
+  if constexpr (Gm::entry_bytes == 8) {
+    ev = (wd << 3) & 0x78787878u;
+    od = (wd >> 1) & 0x78787878u;
+  } else {
+    ev = (wd << 4) & 0xF0F0F0F0u;
+    od = wd & 0xF0F0F0F0u;
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t v = e ? od : ev;
+      uint32_t a;
+      if (b == 0) a = add_byte<0>(base, v);
+      else if (b == 1) a = add_byte<1>(base, v);
+      else if (b == 2) a = add_byte<2>(base, v);
+      else a = add_byte<3>(base, v);
+      sk_read<NB>(a + (2 * b + e) * Gm::chunk_stride, t[2 * b + e]);
+    }
+  }
+}
+
+// Per-request plane sums over the quarter, in a fixed pairwise order.
+template <int NB>
+__device__ __forceinline__ float sk_quarter_sum(const float (&t)[8][NB], int q) {
+  return ((t[0][q] + t[1][q]) + (t[2][q] + t[3][q])) + ((t[4][q] + t[5][q]) + (t[6][q] + t[7][q]));
+}
+
 // Operands of one window, double-buffered across the window loop.
-template <typename T, int NB, int P>
+template <typename T, int NB, int P, int UMAX>
 struct SkOperands {
-  uint4 bits[P];
-  typename Act<T>::raw x[2][NB];  // this lane's two chunks of every request's activations
-  uint32_t alpha[NB][P];
-  uint32_t zero[NB];
+  uint2 bits[(P + 1) / 2];                    // this lane's two sign words, per plane pair
+  typename Act<T>::raw x[SkGeom<NB>::rpt];    // the chunk this thread builds, per request
+  uint32_t sc[UMAX];                          // staged scale values (raw)
 };
 
-// P is the largest precision of the launch (a template argument, so the plane
-// loops are compile-time).  The load phase has no branches: lanes past the last
-// group or row, windows past the end and planes beyond a request's precision
-// read clamped in-range addresses whose values are never used.
-template <typename T, int NB, int P>
-__global__ __launch_bounds__(kSkThreads) void skinny_lut_kernel(
-    const uint4 *__restrict__ bits, ReqTables tabs, int nreq, const T *__restrict__ x, int ldx,
-    T *__restrict__ y, int ldy, int M, int G, int MT) {
+// P is the largest precision of the launch; UMAX * 4 >= the number of staged
+// arrays.  NH windows are processed at once, each by its own 256-lane half of
+// the workgroup with its own tables, so every step has NH windows of work to
+// cover the loads of the next step.  The load phase has no branches: windows
+// past the end, groups past G, rows past M and requests past nreq read clamped
+// in-range addresses whose values are never used.
+template <typename T, int NB, int P, int UMAX, int NH, bool UNI>
+__global__ __launch_bounds__(kSkThreads * NH) __attribute__((amdgpu_waves_per_eu(1, 2))) void
+skinny_lut_kernel(const uint32_t *__restrict__ bits, ReqTables st, int nreq,
+                  const T *__restrict__ x, int ldx, T *__restrict__ y, int ldy, int M, int G,
+                  int MT) {
   using Gm = SkGeom<NB>;
-  using Ops = SkOperands<T, NB, P>;
-  __shared__ __attribute__((aligned(16))) char lut[Gm::window_bytes];
-  __shared__ float gsum[kSkKsub][NB];
+  using Ops = SkOperands<T, NB, P, UMAX>;
+  constexpr int kPairs = (P + 1) / 2;
+  constexpr int kZSlot = sk_zero_slot(P);  // plane slots (an even number), then offsets
+  constexpr int kSlots = kZSlot + 1;
+  // With one precision for every request (UNI) all requests share one scale
+  // per (row, group, plane): one float per record.  Otherwise each request
+  // has its own slot, per_entry requests side by side in a record.
+  constexpr int kQB = UNI ? 1 : Gm::halves;         // request blocks
+  constexpr int kSR = UNI ? 4 : Gm::entry_bytes;    // bytes of one (slot, block, row) record
+  constexpr int kStageBytes = kSkGroups * kSlots * kQB * kTileRows * kSR;
+  constexpr int kWaves = kSkGroups * NH;
+  __shared__ __attribute__((aligned(16))) char lut_all[NH][Gm::lut_bytes];
+  __shared__ __attribute__((aligned(16))) char stage_all[NH][kStageBytes];
+  __shared__ __attribute__((aligned(16))) float qsum_all[NH][kSkGroups][kSkQuarters][NB];
+  static_assert(kWaves * kTileRows * NB * 4 <= Gm::lut_bytes, "partials fit the tables");
 
-  const int lane = threadIdx.x;
-  const int r = lane & 15;
-  const int ks = lane >> 4;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave / kSkGroups;      // which of the NH concurrent windows
+  const int wl = wave % kSkGroups;        // group of the window
+  const int tl = tid % kSkThreads;        // thread within the half
+  char *lut = lut_all[half];
+  char *stage = stage_all[half];
+  float(*qsum)[kSkQuarters][NB] = qsum_all[half];
+  const int r = lane & 15;         // row of the tile (lookups and staging)
+  const int k = (lane >> 4) & 1;   // plane within a pair (lookups)
+  const int c = lane >> 5;         // 64-column half of the group (lookups)
+  const int h = lane >> 4;         // group of the window (staging)
   const int tile = blockIdx.x;
-  const int m = tile * kTileRows + r;
-  const bool row_ok = m < M;
-  const int m_safe = min(m, M - 1);
-  const int nwin = (G + kSkKsub - 1) / kSkKsub;
-  const size_t plane_stride = (size_t)MT * G * kTileRows;
-  const uint4 *tbits = bits + (size_t)tile * G * kTileRows + r;
-  const size_t MG = (size_t)M * G;
+  const int nwin = (G + kSkGroups - 1) / kSkGroups;
+  const int nstep = (nwin + NH - 1) / NH;
+  const size_t plane_words = (size_t)MT * G * kTileRows * 4;
+  const uint2 *tb = reinterpret_cast<const uint2 *>(bits + ((size_t)tile * G * kTileRows + r) * 4) + c;
+  // build role: chunk bc of the window, requests q0 .. q0 + rpt - 1.  Lane bits
+  // 3 and 4 are swapped in the chunk index so that the 16-byte table writes of
+  // lanes l and l + 16 (serviced together) land 32 banks apart.
+  const int bc = ((tl & 0x67) | ((tl & 8) << 1) | ((tl & 16) >> 1)) & (kSkChunks - 1);
+  const int bg = bc / kChunksPerGroup;
+  const int bcl = bc % kChunksPerGroup;
+  const int q0 = (tl / kSkChunks) * Gm::rpt;
+  // staging role: row r, window group h, arrays wl + 4u (their descriptors are
+  // wave-uniform and read once, before the loop)
+  const int srow = min(tile * kTileRows + r, M - 1);
+  const T *sptr[UMAX];
+  int sslot[UMAX];
+  uint32_t smask[UMAX];
+#pragma unroll
+  for (int u = 0; u < UMAX; ++u) {
+    const int a = wl + 4 * u;
+    const int ac = min(a, st.n - 1);
+    sptr[u] = static_cast<const T *>(st.arr[ac]) + (size_t)srow * G;
+    sslot[u] = __builtin_amdgcn_readfirstlane(st.slot[ac]);
+    smask[u] = __builtin_amdgcn_readfirstlane(a < st.n ? st.mask[ac] : 0u);
+  }
+
+  // slots no array writes (planes past a request's precision, padding
+  // requests) must read as zero
+  for (int o = tid * 16; o < NH * kStageBytes; o += kSkThreads * NH * 16)
+    *reinterpret_cast<float4 *>(&stage_all[0][0] + o) = make_float4(0.f, 0.f, 0.f, 0.f);
 
   float acc[NB];
 #pragma unroll
   for (int q = 0; q < NB; ++q) acc[q] = 0.f;
 
-  auto fetch = [&](int w_in, Ops &o) {
-    const int w = min(w_in, nwin - 1);
-    const int js = min(w * kSkKsub + ks, G - 1);
+  auto fetch = [&](int step, Ops &o) {
+    const int w = min(step * NH + half, nwin - 1);
+    const int j = min(w * kSkGroups + wl, G - 1);
 #pragma unroll
-    for (int i = 0; i < P; ++i) o.bits[i] = tbits[i * plane_stride + (size_t)js * kTileRows];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = lane + h * kSkThreads;
-      const int jc = min(w * kSkKsub + c / kChunksPerGroup, G - 1);
-#pragma unroll
-      for (int q = 0; q < NB; ++q) {
-        const int qs = min(q, nreq - 1);
-        o.x[h][q] = Act<T>::load(x + (size_t)qs * ldx + (size_t)jc * kGroup + (c % kChunksPerGroup) * 4);
-      }
+    for (int u = 0; u < kPairs; ++u) {
+      const int i = min(2 * u + k, P - 1);
+      o.bits[u] = tb[(i * plane_words + (size_t)j * kTileRows * 4) / 2];
     }
+    const int jx = min(w * kSkGroups + bg, G - 1);
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int pq = max(tabs.p[q], 1);
-      const T *a = static_cast<const T *>(tabs.alpha[q]);
-#pragma unroll
-      for (int i = 0; i < P; ++i)
-        o.alpha[q][i] = load_raw(a + min(i, pq - 1) * MG + (size_t)m_safe * G + js);
-      o.zero[q] = load_raw(static_cast<const T *>(tabs.zero[q]) + (size_t)m_safe * G + js);
+    for (int u = 0; u < Gm::rpt; ++u) {
+      const int qs = min(q0 + u, nreq - 1);
+      o.x[u] = Act<T>::load(x + (size_t)qs * ldx + (size_t)jx * kGroup + bcl * 4);
     }
+    const int js = min(w * kSkGroups + h, G - 1);
+#pragma unroll
+    for (int u = 0; u < UMAX; ++u) o.sc[u] = load_raw(sptr[u] + js);
   };
 
-  auto consume = [&](int w, const Ops &o) {
-    __syncthreads();  // the previous window's lookups are done with lut[]
-    // ---- build tables for the 128 chunks of the window, NB requests each
-    float cs[2][NB];
+  auto consume = [&](int step, const Ops &o) {
+    __syncthreads();  // the previous step's lookups are done with lut, stage, qsum
+    // ---- tables of chunk bc for this thread's requests
+    {
+      float A[Gm::rpt], D[Gm::rpt], C[Gm::rpt], E[Gm::rpt];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = lane + h * kSkThreads;
-      char *dst = lut + (c / kChunksPerGroup) * Gm::group_stride +
-                  (c % kChunksPerGroup) * Gm::chunk_stride;
+      for (int u = 0; u < Gm::rpt; ++u) {
+        float f[4];
+        Act<T>::cvt(o.x[u], f);
+        A[u] = f[0] + f[1];
+        D[u] = f[0] - f[1];
+        C[u] = f[2] + f[3];
+        E[u] = f[2] - f[3];
+      }
+      char *dst = lut + bg * Gm::group_stride + bcl * Gm::chunk_stride +
+                  (q0 / Gm::per_entry) * Gm::half_bytes + (q0 % Gm::per_entry) * 4;
 #pragma unroll
-      for (int hf = 0; hf < Gm::halves; ++hf) {
-        constexpr int L = Gm::lanes;
-        float4 v[L][4];
+      for (int e = 0; e < kEntries; ++e) {
+        // bit t of e selects +x_t: low two bits pick -A, D, -D, A; high two -C, E, -E, C
+        float v[Gm::rpt];
 #pragma unroll
-        for (int q = 0; q < L; ++q) {
-          float f[4];
-          Act<T>::cvt(o.x[h][hf * L + q], f);
-          chunk_entries(f, v[q]);
-          cs[h][hf * L + q] = (f[0] + f[1]) + (f[2] + f[3]);
+        for (int u = 0; u < Gm::rpt; ++u) {
+          const float lo = (e & 3) == 0 ? -A[u] : (e & 3) == 1 ? D[u] : (e & 3) == 2 ? -D[u] : A[u];
+          const float hi = (e >> 2) == 0 ? -C[u] : (e >> 2) == 1 ? E[u] : (e >> 2) == 2 ? -E[u] : C[u];
+          v[u] = lo + hi;
         }
-        char *hd = dst + hf * Gm::half_bytes;
+        char *ed = dst + e * Gm::entry_bytes;
+        if constexpr (Gm::rpt == 1)
+          *reinterpret_cast<float *>(ed) = v[0];
+        else if constexpr (Gm::rpt == 2)
+          *reinterpret_cast<float2 *>(ed) = make_float2(v[0], v[1]);
+        else
+          *reinterpret_cast<float4 *>(ed) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      // quarter sums: the 8 chunks of a quarter are 8 consecutive lanes
+      float cs[Gm::rpt];
 #pragma unroll
-        for (int e = 0; e < kEntries; ++e) {
-          char *ed = hd + e * Gm::entry_bytes;
-          if constexpr (L == 2) {
-            *reinterpret_cast<float2 *>(ed) =
-                make_float2(comp(v[0][e >> 2], e & 3), comp(v[1][e >> 2], e & 3));
-          } else {
-            *reinterpret_cast<float4 *>(ed) =
-                make_float4(comp(v[0][e >> 2], e & 3), comp(v[1][e >> 2], e & 3),
-                            comp(v[2][e >> 2], e & 3), comp(v[3][e >> 2], e & 3));
-          }
-        }
+      for (int u = 0; u < Gm::rpt; ++u) cs[u] = sum8_lanes(A[u] + C[u]);
+      if ((tid & 7) == 0) {
+#pragma unroll
+        for (int u = 0; u < Gm::rpt; ++u) qsum[bg][bcl / 8][q0 + u] = cs[u];
       }
     }
+    // ---- scales: array wl + 4u, position (row r, group h of the window)
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1)
+    for (int u = 0; u < UMAX; ++u) {
+      const float v = raw_to_float<T>(o.sc[u]);
+      if constexpr (UNI) {
+        if (smask[u] != 0u)
+          *reinterpret_cast<float *>(stage + ((h * kSlots + sslot[u]) * kTileRows + r) * kSR) = v;
+      } else {
 #pragma unroll
-      for (int q = 0; q < NB; ++q) {
-        cs[0][q] += __shfl_xor(cs[0][q], off);
-        cs[1][q] += __shfl_xor(cs[1][q], off);
-      }
-    if ((lane & 31) == 0) {
-#pragma unroll
-      for (int q = 0; q < NB; ++q) {
-        gsum[lane / 32][q] = cs[0][q];
-        gsum[lane / 32 + 2][q] = cs[1][q];
+        for (int q = 0; q < NB; ++q)
+          if ((smask[u] >> q) & 1u)
+            *reinterpret_cast<float *>(
+                stage + (((h * kSlots + sslot[u]) * kQB + q / Gm::per_entry) * kTileRows + r) * kSR +
+                (q % Gm::per_entry) * 4) = v;
       }
     }
     __syncthreads();
 
-    // ---- lookups, then per-request scale and offset
-    const int j = w * kSkKsub + ks;
-    if (j < G && row_ok) {
-      const uint32_t base = lds_addr(lut + ks * Gm::group_stride);
+    // ---- lookups for this lane's (plane, column half), then scales and offsets
+    const int j = (step * NH + half) * kSkGroups + wl;
+    if (j < G) {
+      const uint32_t base = lds_addr(lut + wl * Gm::group_stride + (16 * c) * Gm::chunk_stride);
+      const uint32_t sbase = lds_addr(stage + ((wl * kSlots) * kQB * kTileRows + r) * kSR);
+      constexpr int kSlotBytes = kQB * kTileRows * kSR;
+      // scale and offset slots first, then the sign words software-pipelined:
+      // the reads of word n + 1 are in flight while word n is summed
+      float al[kPairs][NB], zz[NB], qs[NB];
+      if constexpr (UNI) {
 #pragma unroll
-      for (int i = 0; i < P; ++i) {
-        float ps[NB];
-        sk_plane_sums<NB>(o.bits[i], base, ps);
+        for (int u = 0; u < kPairs; ++u) {
+          const float a = *(lds_float *)(size_t)(sbase + (2 * u + k) * kSlotBytes);
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-          const float a = i < tabs.p[q] ? raw_to_float<T>(o.alpha[q][i]) : 0.f;
-          acc[q] = fmaf(a, ps[q], acc[q]);
+          for (int q = 0; q < NB; ++q) al[u][q] = a;
         }
+        const float z = *(lds_float *)(size_t)(sbase + kZSlot * kSlotBytes);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) zz[q] = z;
+      } else {
+#pragma unroll
+        for (int u = 0; u < kPairs; ++u) sk_read<NB>(sbase + (2 * u + k) * kSlotBytes, al[u]);
+        sk_read<NB>(sbase + kZSlot * kSlotBytes, zz);
       }
 #pragma unroll
-      for (int q = 0; q < NB; ++q) {
-        const float z = tabs.p[q] > 0 ? raw_to_float<T>(o.zero[q]) : 0.f;
-        acc[q] = fmaf(z, gsum[ks][q], acc[q]);
+      for (int q = 0; q < NB; ++q) qs[q] = qsum[wl][2 * c + k][q];
+      constexpr int kWords = 2 * kPairs;
+      auto word = [&](int n) { return (n & 1) ? o.bits[n >> 1].y : o.bits[n >> 1].x; };
+      float t[2][8][NB];
+      sk_quarter_reads<NB>(word(0), base, t[0]);
+#pragma unroll
+      for (int n = 0; n < kWords; ++n) {
+        if (n + 1 < kWords)
+          sk_quarter_reads<NB>(word(n + 1), base + ((n + 1) & 1) * 8 * Gm::chunk_stride,
+                               t[(n + 1) & 1]);
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+          acc[q] = fmaf(al[n >> 1][q], sk_quarter_sum<NB>(t[n & 1], q), acc[q]);
       }
+#pragma unroll
+      for (int q = 0; q < NB; ++q) acc[q] = fmaf(zz[q], qs[q], acc[q]);
     }
   };
 
-  // ping-pong over two operand buffers: window w+1 loads while window w computes
-  Ops A, B;
-  fetch(0, A);
-  for (int w = 0; w < nwin; w += 2) {
-    fetch(w + 1, B);
-    consume(w, A);
-    if (w + 1 >= nwin) break;  // uniform
-    fetch(w + 2, A);
-    consume(w + 1, B);
+  // a ring of kSkDepth operand sets: the loads of step s + kSkDepth - 1 are
+  // issued before step s is computed, so memory latency (about 1.5 us under
+  // load, several steps' worth of work) is covered by the steps in between
+  constexpr int D = kSkDepth;
+  Ops ring[D];
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) fetch(d, ring[d]);
+  for (int s0 = 0; s0 < nstep; s0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (s0 + d >= nstep) break;  // uniform
+      fetch(s0 + d + D - 1, ring[(d + D - 1) % D]);
+      consume(s0 + d, ring[d]);
+    }
   }
 
-  // ---- reduce the 4 K-sub partials of each row (lanes r, r+16, r+32, r+48)
+  // ---- reduce: the 4 lanes of a row in the wavefront, then the groups
+  // (wavefronts) through LDS, in a fixed order
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
     acc[q] += __shfl_xor(acc[q], 16);
     acc[q] += __shfl_xor(acc[q], 32);
   }
-  if (ks == 0 && row_ok) {
+  __syncthreads();  // the tables are free: reuse them for the partials
+  float *part = reinterpret_cast<float *>(&lut_all[0][0]);  // [wave][row][request]
+  if (lane < kTileRows) {
 #pragma unroll
-    for (int q = 0; q < NB; ++q)
-      if (q < nreq) y[(size_t)q * ldy + m] = (T)acc[q];
+    for (int q = 0; q < NB; ++q) part[(wave * kTileRows + lane) * NB + q] = acc[q];
+  }
+  __syncthreads();
+  if (tid < kTileRows * NB) {
+    const int q = tid / kTileRows;
+    const int rr = tid % kTileRows;
+    const int m = tile * kTileRows + rr;
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) sum += part[(v * kTileRows + rr) * NB + q];
+    if (q < nreq && m < M) y[(size_t)q * ldy + m] = (T)sum;
   }
 }
 
-template <typename T, int NB>
-void skinny_launch_p(dim3 grid, dim3 block, hipStream_t s, const uint4 *b4, const ReqTables &t,
-                     int nreq, const T *xx, int ldx, T *yy, int ldy, int M, int G, int MT,
-                     int p_max) {
+template <typename T, int NB, int UMAX, bool UNI, int NH = kSkConcurrent>
+void skinny_launch_p(dim3 grid, hipStream_t s, const uint32_t *b, const ReqTables &t, int nreq,
+                     const T *xx, int ldx, T *yy, int ldy, int M, int G, int MT, int p_max) {
+  const dim3 block(kSkThreads * NH);
+#define BCQ_SKP(PP)                                                                          \
+  hipLaunchKernelGGL((skinny_lut_kernel<T, NB, PP, UMAX, NH, UNI>), grid, block, 0, s, b, t, \
+                     nreq, xx, ldx, yy, ldy, M, G, MT)
   switch (p_max) {
-    case 1:
-      hipLaunchKernelGGL((skinny_lut_kernel<T, NB, 1>), grid, block, 0, s, b4, t, nreq, xx, ldx,
-                         yy, ldy, M, G, MT);
-      break;
-    case 2:
-      hipLaunchKernelGGL((skinny_lut_kernel<T, NB, 2>), grid, block, 0, s, b4, t, nreq, xx, ldx,
-                         yy, ldy, M, G, MT);
-      break;
-    case 3:
-      hipLaunchKernelGGL((skinny_lut_kernel<T, NB, 3>), grid, block, 0, s, b4, t, nreq, xx, ldx,
-                         yy, ldy, M, G, MT);
-      break;
-    default:
-      hipLaunchKernelGGL((skinny_lut_kernel<T, NB, 4>), grid, block, 0, s, b4, t, nreq, xx, ldx,
-                         yy, ldy, M, G, MT);
-      break;
+    case 1: BCQ_SKP(1); break;
+    case 2: BCQ_SKP(2); break;
+    case 3: BCQ_SKP(3); break;
+    default: BCQ_SKP(4); break;
   }
+#undef BCQ_SKP
+}
+
+// One precision for every request: the host lists exactly p + 1 arrays (the
+// planes and offsets of that precision), each read by every request.
+template <typename T, int NB>
+void skinny_launch_u(dim3 grid, hipStream_t s, const uint32_t *b, const ReqTables &t, int nreq,
+                     const T *xx, int ldx, T *yy, int ldy, int M, int G, int MT, int p_max) {
+  if (t.n == p_max + 1)
+    skinny_launch_p<T, NB, 2, true>(grid, s, b, t, nreq, xx, ldx, yy, ldy, M, G, MT, p_max);
+  else if (t.n <= 8)
+    skinny_launch_p<T, NB, 2, false>(grid, s, b, t, nreq, xx, ldx, yy, ldy, M, G, MT, p_max);
+  else
+    skinny_launch_p<T, NB, 4, false>(grid, s, b, t, nreq, xx, ldx, yy, ldy, M, G, MT, p_max);
 }
 
 template <typename T>
@@ -878,16 +1014,15 @@ hipError_t skinny_dispatch(const uint32_t *bits, int M, int K, int p_max, const 
                            int nreq, const void *x, int ldx, void *y, int ldy, hipStream_t s) {
   const int G = K / kGroup;
   const int MT = row_tiles(M);
-  const uint4 *b4 = reinterpret_cast<const uint4 *>(bits);
   const T *xx = static_cast<const T *>(x);
   T *yy = static_cast<T *>(y);
-  dim3 grid(MT), block(kSkThreads);
+  const dim3 grid(MT);
   if (nreq <= 2)
-    skinny_launch_p<T, 2>(grid, block, s, b4, t, nreq, xx, ldx, yy, ldy, M, G, MT, p_max);
+    skinny_launch_u<T, 2>(grid, s, bits, t, nreq, xx, ldx, yy, ldy, M, G, MT, p_max);
   else if (nreq <= 4)
-    skinny_launch_p<T, 4>(grid, block, s, b4, t, nreq, xx, ldx, yy, ldy, M, G, MT, p_max);
+    skinny_launch_u<T, 4>(grid, s, bits, t, nreq, xx, ldx, yy, ldy, M, G, MT, p_max);
   else
-    skinny_launch_p<T, 8>(grid, block, s, b4, t, nreq, xx, ldx, yy, ldy, M, G, MT, p_max);
+    skinny_launch_u<T, 8>(grid, s, bits, t, nreq, xx, ldx, yy, ldy, M, G, MT, p_max);
   return hipGetLastError();
 }
 
