@@ -187,19 +187,11 @@ def headline(args, bcq, torch, bcq_synth):
     achieved = algorithmic_bytes(M, K, 4) / (dur[4] * 1e-3) / 1e9
     traffic = stored_traffic()
 
-    # warm-cache context: one store, repeated
-    warm = {}
-    for p in ps:
-        d = time_calls(torch, lambda i, p=p: bcq.bcq_gemv(rot.stores[0], p, rot.x[0][0], ys[0]),
-                       args.steps, args.warmup)
-        warm[str(p)] = round(d * 1e3, 3)
-
     out = {
         "value": round(value, 1),
         "steps_timed": n_steps,
         "ms_per_step": round(region_ms / n_steps, 6),
         "per_p": per_p,
-        "warm_cache_us": warm,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -238,6 +230,17 @@ def secondary(args, bcq, torch, bcq_synth):
     rows["gemv_14336x4096_b1"] = r
     del rot, ys
 
+    # 4096x4096 at batch 1 with one store repeated (planes served from the
+    # Infinity Cache after the first call): context for the cold numbers
+    w = bcq_synth.config(2)
+    st = bcq.Store.from_host(w.signs, w.alpha, w.zero)
+    x = torch.from_numpy(np.ascontiguousarray(w.x[0])).cuda()
+    y = torch.empty(w.M, dtype=torch.float16, device="cuda")
+    rows["gemv_4096x4096_b1_warm_cache_us"] = {
+        str(p): round(time_calls(torch, lambda i, p=p: bcq.bcq_gemv(st, p, x, y), n, 10) * 1e3, 3)
+        for p in (2, 3, 4)}
+    del st, x, y
+
     # per-request precision, 8 requests on 4096x4096 vs the same call at uniform p = max
     w = bcq_synth.config(4)
     rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=w.b)
@@ -259,9 +262,12 @@ def secondary(args, bcq, torch, bcq_synth):
     del rot, Y
 
     # small batches (MLP shapes, p = 3) and matrix-core batches (p = 4)
-    for (M, K), b, p in [((14336, 4096), 4, 3), ((14336, 4096), 8, 3), ((4096, 14336), 8, 3),
+    for (M, K), b, p in [((4096, 4096), 2, 4), ((4096, 4096), 4, 4), ((4096, 4096), 8, 4),
+                         ((14336, 4096), 4, 3), ((14336, 4096), 8, 3), ((4096, 14336), 4, 3),
+                         ((4096, 14336), 8, 3),
                          ((4096, 4096), 16, 4), ((4096, 4096), 32, 4), ((4096, 4096), 64, 4),
                          ((14336, 4096), 64, 4)]:
+        print("[bench] secondary %dx%d b=%d p=%d" % (M, K, b, p), file=sys.stderr, flush=True)
         w = bcq_synth.make(M, K, 4, b=b, seed=5)
         rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
         Y = [torch.empty((b, M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
@@ -310,6 +316,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for HBM counter calibration)")
+    ap.add_argument("--counter-run", type=int, default=0, metavar="N",
+                    help="only run N cold eager calls of the batch-1 kernel at each of p=2,3,4 "
+                         "on the 4096x4096 store (for per-dispatch HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build's path runs on a single MI355X "
@@ -333,6 +342,18 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": src.numel() * 4, "copies": 5}))
+        return
+
+    if args.counter_run:
+        w = bcq_synth.config(2)
+        rot = Rotation(w, ROTATE_BYTES, bcq, torch)
+        ys = [torch.empty(w.M, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+        for p in (2, 3, 4):
+            for i in range(args.counter_run):
+                c = i % rot.n
+                bcq.bcq_gemv(rot.stores[c], p, rot.x[c][0], ys[c])
+        torch.cuda.synchronize()
+        print(json.dumps({"counter_run_calls_per_p": args.counter_run, "copies": rot.n}))
         return
 
     print("[bench] headline", file=sys.stderr, flush=True)
@@ -368,7 +389,6 @@ def main():
             "rotating_bytes": h["rotation"]["bytes"],
         },
         "per_p": h["per_p"],
-        "warm_cache_us": h["warm_cache_us"],
         "roofline": h["roofline"],
         "cpu_baseline": cpu,
         "secondary": sec,

@@ -124,10 +124,13 @@ bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype 
  * X: [b][ldx] (row r starts at X + r*ldx elements), 16-byte aligned, so ldx*size
  * must be a multiple of 16 bytes; ldx >= K.  Y: [b][ldy], ldy >= M, element
  * aligned.  1 <= b <= BCQ_MAX_BATCH.
- * Batch 1 runs the batch-1 kernel.  Batches below 16 (and every fp32 batch) run
- * on the vector ALUs with sign-combination tables shared by up to 8 requests.
- * fp16 batches of 16 and more dequantise tiles of W to fp16 and contract them
- * on the matrix cores; that path splits K over workgroups and needs
+ * Batch 1 runs the batch-1 kernel.  fp32 batches, and fp16 batches of 2..4,
+ * run on the vector ALUs with sign-combination tables shared by up to 8
+ * requests per launch.  fp16 batches of 5..15 decode each weight once per
+ * launch of up to 16 requests into fp16 and take one fp16 dot product per
+ * weight pair per request on the vector ALUs (the decoded weight is rounded to
+ * fp16).  fp16 batches of 16 and more dequantise tiles of W to fp16 and
+ * contract them on the matrix cores; that path splits K over workgroups and needs
  * bcq_workspace_bytes(store, b) bytes of device workspace (4-byte aligned,
  * contents need no initialisation, clobbered by the call).  workspace may be
  * NULL when that size is 0; a smaller workspace gives BCQ_ERR_INVALID_ARG.
@@ -145,8 +148,10 @@ size_t bcq_workspace_bytes(const bcq_store *store, int32_t b);
 
 /*
  * Per-request precision: Y[r] = BCQ product of X[r] at precision p_host[r],
- * using alpha[p_host[r]] and zero[p_host[r]].  Every plane up to the largest
- * requested precision is read once for the whole batch.
+ * using alpha[p_host[r]] and zero[p_host[r]].  Requests run in launches of up
+ * to 8; each launch reads every plane up to its largest requested precision
+ * once for all its requests (planes past a request's own precision get a zero
+ * scale for it), so mixing precisions costs no extra plane traffic.
  * p_host: [b] in HOST memory; every entry must lie in [1, planes], otherwise
  * BCQ_ERR_INVALID_ARG and nothing is enqueued.  1 <= b <= BCQ_MAX_BATCH.
  * X, Y, ldx, ldy as in bcq_gemm_skinny.
