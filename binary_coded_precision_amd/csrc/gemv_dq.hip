@@ -10,38 +10,36 @@
 // work grows with batch), so it is done once per weight and each request then
 // costs one fused multiply-add per weight.
 //
-// Decode on CDNA4.  Weights are handled as fp16 pairs (column t, column t+16)
-// of one 32-column sign word, so that one shift moves both sign bits (bits t
-// and t+16) to the two fp16 sign positions (bits 15 and 31).  For plane i:
-//   m   = (word' << (15 - t)) & 0x80008000        one shift, then a bit-field
-//   +-a = m | (|alpha_i| in both halves)           insert (v_bfi_b32)
-//   w  += +-a                                      v_pk_add_f16
-// where word' is the sign word inverted (or not, when alpha_i < 0) so that a
-// set bit yields +alpha_i.  The pair then meets each request's activation pair
-// in v_dot2_f32_f16 (exact fp16 products, fp32 accumulation).  The decoded
-// weight carries fp16 rounding (relative 2^-11 per addition), which is why
-// this path serves fp16 inputs only; fp32 batches use the exact table kernel.
+// The decode itself is in decode.h: per plane and fp16 pair one shift, one
+// bit-field insert and one packed add.  The pair then meets each request's
+// natural activation pair (columns 2t, 2t+1) in v_dot2_f32_f16 (exact fp16
+// products, fp32 accumulation).  The decoded weight carries fp16 rounding,
+// which is why this path serves fp16 inputs only; fp32 batches use the exact
+// table kernel.
 //
 // Lane mapping.  A workgroup owns a 16-row tile and walks K in windows of 4
 // groups; NH windows are in flight per step, one per 256-lane quarter of the
 // workgroup.  Wavefront v takes group v % 4 of its window, lane (r, h) row r
 // and the h-th 32-column word of that group, i.e. one packed sign word per
-// plane.  Activations of the step are staged in LDS in pair order
+// plane.  Activations of the step are staged in LDS
 // ([window][group][request][word][pair]) by the whole workgroup, double
 // buffered, so each step needs one barrier.  All 16 lanes of a word read the
 // same 64 bytes of a request's pairs (broadcast), and the two words of a
 // half-wavefront sit 64 bytes apart (distinct banks).
-#include "bcq_internal.h"
+#include "decode.h"
 
 namespace bcq {
 namespace {
 
 using half_t = _Float16;
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+using half2v = dq_half2;
+// 16-byte blocks as a native vector: HIP's uint4 is a struct copied with
+// memcpy, which keeps arrays of it out of registers (in scratch or LDS).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kDqGroups = 4;       // groups per window (one per wavefront)
+constexpr int kDqGroups = 4;           // groups per window (one per wavefront)
 constexpr int kDqWords = kGroup / 32;  // 32-column sign words per group
-constexpr int kDqPairs = 16;       // fp16 pairs per sign word
+
 // Windows in flight per workgroup: 4 (16 wavefronts, at most 128 VGPRs each)
 // while the requests' accumulators and activation reads fit that budget, 2
 // (8 wavefronts, up to 256 VGPRs) for more requests.  Mixed precisions keep
@@ -50,21 +48,6 @@ constexpr int kDqPairs = 16;       // fp16 pairs per sign word
 template <int NB, bool MIXED>
 constexpr int dq_concurrent() { return NB <= (MIXED ? 2 : 4) ? 4 : 2; }
 constexpr int kDqMaxMixed = kDqMaxMixedReq;
-
-__device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
-
-// One plane's contribution to the 16 pairs of a word: w[t] += +-alpha.
-// a16 is the raw fp16 scale in the low half of a register.
-__device__ __forceinline__ void dq_plane(half2v (&w)[kDqPairs], uint32_t word, uint32_t a16) {
-  const uint32_t mag = (a16 & 0x7FFFu) * 0x10001u;        // |alpha| in both halves
-  const uint32_t neg = (uint32_t)((int32_t)(a16 << 16) >> 31);  // all ones when alpha < 0
-  const uint32_t wp = ~(word ^ neg);  // a set sign bit must give +alpha: sign bit 0 iff alpha >= 0
-#pragma unroll
-  for (int t = 0; t < kDqPairs; ++t) {
-    const uint32_t m = wp << (15 - t);  // bits t, t+16 -> 15, 31
-    w[t] += as_h2((m & 0x80008000u) | mag);
-  }
-}
 
 // Operands of one step for one lane: the sign words, scales and offset of its
 // (row, group, word) position, and this thread's share of the activations to
@@ -78,7 +61,7 @@ struct DqW {
 template <int NB>
 struct DqX {
   static constexpr int kTasks = (NB + 3) / 4;  // 16-byte pair blocks this thread stages
-  uint2 lo[kTasks], hi[kTasks];                // columns 4b..4b+3 and 4b+16..4b+19
+  u32x4 v[kTasks];                             // columns 8b .. 8b+7 of a word: pairs 4b..4b+3
 };
 
 // P: planes decoded (the largest precision of the launch).  MIXED: requests
@@ -93,7 +76,7 @@ __global__ __launch_bounds__(256 * NH) __attribute__((amdgpu_waves_per_eu(NH, NH
   using OpsX = DqX<NB>;
   constexpr int kWaves = 4 * NH;
   // staged activations: [buffer][window][group][request][word][pair block] of 4 pairs
-  __shared__ uint4 xs[2][NH][kDqGroups][NB][kDqWords][4];
+  __shared__ u32x4 xs[2][NH][kDqGroups][NB][kDqWords][4];
   __shared__ float part[kWaves][kTileRows][NB];
 
   const int tid = threadIdx.x;
@@ -128,26 +111,15 @@ __global__ __launch_bounds__(256 * NH) __attribute__((amdgpu_waves_per_eu(NH, NH
   auto fetch_x = [&](int step, OpsX &o) {
     const int w = min(step * NH + half, nwin - 1);
     const int j = min(w * kDqGroups + sg, G - 1);
-    const int col = j * kGroup + sh * 32 + sb * 4;
+    const int col = j * kGroup + sh * 32 + sb * 8;
 #pragma unroll
-    for (int u = 0; u < OpsX::kTasks; ++u) {
-      o.lo[u] = *reinterpret_cast<const uint2 *>(xrow[u] + col);
-      o.hi[u] = *reinterpret_cast<const uint2 *>(xrow[u] + col + 16);
-    }
+    for (int u = 0; u < OpsX::kTasks; ++u) o.v[u] = *reinterpret_cast<const u32x4 *>(xrow[u] + col);
   };
   auto write_x = [&](const OpsX &o, int buf) {
 #pragma unroll
     for (int u = 0; u < OpsX::kTasks; ++u) {
       const int q = sq0 + 4 * u;
-      if (q < NB) {  // wave-uniform
-        // pair t = (x_t, x_{t+16}): low halves, then high halves, of each word
-        uint4 v;
-        v.x = __builtin_amdgcn_perm(o.hi[u].x, o.lo[u].x, 0x05040100u);
-        v.y = __builtin_amdgcn_perm(o.hi[u].x, o.lo[u].x, 0x07060302u);
-        v.z = __builtin_amdgcn_perm(o.hi[u].y, o.lo[u].y, 0x05040100u);
-        v.w = __builtin_amdgcn_perm(o.hi[u].y, o.lo[u].y, 0x07060302u);
-        xs[buf][half][sg][q][sh][sb] = v;
-      }
+      if (q < NB) xs[buf][half][sg][q][sh][sb] = o.v[u];  // wave-uniform
     }
   };
   auto fetch_w = [&](int step, OpsW &o) {
@@ -169,18 +141,16 @@ __global__ __launch_bounds__(256 * NH) __attribute__((amdgpu_waves_per_eu(NH, NH
     const int j = (step * NH + half) * kDqGroups + wl;
     if (j >= G) return;  // wave-uniform
     half2v w[kDqPairs];
-    const half2v z2 = as_h2((o.z & 0xFFFFu) * 0x10001u);
-#pragma unroll
-    for (int t = 0; t < kDqPairs; ++t) w[t] = z2;
+    dq_init(w, o.z);
     // the dot products of the requests in mask sel (bit q: request q), one
     // block of 4 pairs at a time: the block's activation reads of every
     // selected request are issued together, then the dot products follow, so
     // NB reads are in flight and consecutive dot2 feed different accumulators
-    const uint4 *xq = &xs[buf][half][wl][0][h][0];  // request q at xq + q * kDqWords * 4
+    const u32x4 *xq = &xs[buf][half][wl][0][h][0];  // request q at xq + q * kDqWords * 4
     auto dots = [&](uint32_t sel) {
 #pragma unroll
       for (int b4 = 0; b4 < 4; ++b4) {
-        uint4 xv[NB];
+        u32x4 xv[NB];
 #pragma unroll
         for (int q = 0; q < NB; ++q)
           if ((sel >> q) & 1u) xv[q] = xq[q * kDqWords * 4 + b4];
@@ -190,7 +160,7 @@ __global__ __launch_bounds__(256 * NH) __attribute__((amdgpu_waves_per_eu(NH, NH
           for (int q = 0; q < NB; ++q)
             if ((sel >> q) & 1u) {
               const uint32_t xu = u == 0 ? xv[q].x : u == 1 ? xv[q].y : u == 2 ? xv[q].z : xv[q].w;
-              acc[q] = __builtin_amdgcn_fdot2(w[4 * b4 + u], as_h2(xu), acc[q], false);
+              acc[q] = __builtin_amdgcn_fdot2(w[4 * b4 + u], dq_as_h2(xu), acc[q], false);
             }
       }
     };
@@ -206,27 +176,31 @@ __global__ __launch_bounds__(256 * NH) __attribute__((amdgpu_waves_per_eu(NH, NH
     if constexpr (!MIXED) dots(0xFFFFFFFFu);
   };
 
-  // pipeline: the activations of step s+1 are written to LDS while step s is
-  // computed from the other buffer; they were loaded a step earlier, and the
-  // sign words and scales of step s+1 load while step s computes
-  OpsX xa, xb;
+  // pipeline: step s computes from one LDS buffer and its sign words and
+  // scales (loaded two steps earlier); then the activations of step s+1
+  // (loaded a step earlier) go to the other buffer, and the loads of step s+2
+  // are issued last.  Issuing them at the end of the body, not its start,
+  // leaves the loop header with the same loads in flight on every path, so
+  // the waits there stay partial and the loads overlap a whole step.
+  OpsX xo;
   OpsW wa, wb;
-  fetch_x(0, xa);
+  fetch_x(0, xo);
   fetch_w(0, wa);
-  fetch_x(1, xb);
-  write_x(xa, 0);
+  write_x(xo, 0);
+  fetch_x(1, xo);
+  fetch_w(1, wb);
   __syncthreads();
   for (int s = 0; s < nstep; s += 2) {
-    write_x(xb, 1);
-    fetch_x(s + 2, xa);
-    fetch_w(s + 1, wb);
     compute(s, wa, 0);
+    write_x(xo, 1);
+    fetch_x(s + 2, xo);
+    fetch_w(s + 2, wa);
     __syncthreads();
     if (s + 1 >= nstep) break;  // uniform
-    write_x(xa, 0);
-    fetch_x(s + 3, xb);
-    fetch_w(s + 2, wa);
     compute(s + 1, wb, 1);
+    write_x(xo, 0);
+    fetch_x(s + 3, xo);
+    fetch_w(s + 3, wb);
     __syncthreads();
   }
 

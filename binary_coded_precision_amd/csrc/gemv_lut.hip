@@ -8,8 +8,9 @@
 // factor and accumulated, and the output is written after the p-th plane.
 //
 // Design for CDNA4 (gfx950):
-//  * Tables.  For every 4-column chunk c of x the workgroup builds the 16 sums
-//    T_c[e] = sum_t (bit t of e ? +x_{4c+t} : -x_{4c+t}) in fp32 in LDS.  One
+//  * Tables.  For every 4-column chunk c of x (the 4 columns one nibble of a
+//    packed sign word covers, see chunk_base) the workgroup builds the 16 sums
+//    T_c[e] = sum_t (bit t of e ? +x_{c,t} : -x_{c,t}) in fp32 in LDS.  One
 //    table read then replaces four signed adds: the 4 sign bits of one row in
 //    one plane are the table index.  (A 16-entry table per 4 columns keeps the
 //    build at 4 entries per column, cheap enough to repeat in every
@@ -40,18 +41,33 @@ constexpr int kChunksPerGroup = kGroup / 4;  // 32 four-column chunks per group
 constexpr int kEntries = 16;                 // table entries per chunk
 
 // ---------------------------------------------------------------- activations
+//
+// Table chunk c (0..31) of a group is nibble c % 8 of the group's packed sign
+// word c / 8.  The packed word holds the even columns of its 32 in the low half
+// and the odd columns in the high half (pack.hip), so the chunk's 4 columns are
+// 32*(c/8) + 8*(c%4) + par + {0, 2, 4, 6} with par = (c/4) % 2, and bit t of the
+// nibble is the column at offset 2t.  fp16 loads the 8 contiguous activations
+// from 32*(c/8) + 8*(c%4) (one 16-byte load) and keeps those of its parity;
+// fp32 loads the 4 it needs.
+
+__device__ __forceinline__ int chunk_base(int c) { return 32 * (c >> 3) + 8 * (c & 3); }
+__device__ __forceinline__ int chunk_parity(int c) { return (c >> 2) & 1; }
 
 template <typename T>
 struct Act;
 
+// Native vector types for values kept in registers (HIP's float4 / uint4 are
+// structs copied with memcpy, which can keep arrays of them in scratch memory).
+typedef float act_f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int act_u32x4 __attribute__((ext_vector_type(4)));
+
 template <>
 struct Act<float> {
-  using raw = float4;  // the 4 activations of one chunk
-  static __device__ __forceinline__ raw load(const float *p) {
-    return *reinterpret_cast<const float4 *>(p);
+  using raw = act_f32x4;  // the chunk's 4 activations (every other column)
+  static __device__ __forceinline__ raw load(const float *p, int par) {
+    return raw{p[par], p[par + 2], p[par + 4], p[par + 6]};
   }
-  static __device__ __forceinline__ raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
-  static __device__ __forceinline__ void cvt(const raw &v, float (&f)[4]) {
+  static __device__ __forceinline__ void cvt(const raw &v, int, float (&f)[4]) {
     f[0] = v.x;
     f[1] = v.y;
     f[2] = v.z;
@@ -61,16 +77,16 @@ struct Act<float> {
 
 template <>
 struct Act<half_t> {
-  using raw = uint2;
-  static __device__ __forceinline__ raw load(const half_t *p) {
-    return *reinterpret_cast<const uint2 *>(p);
+  using raw = act_u32x4;  // 8 contiguous fp16 activations; cvt keeps one parity
+  static __device__ __forceinline__ raw load(const half_t *p, int) {
+    return *reinterpret_cast<const act_u32x4 *>(p);
   }
-  static __device__ __forceinline__ raw zero() { return make_uint2(0u, 0u); }
-  static __device__ __forceinline__ void cvt(const raw &v, float (&f)[4]) {
-    f[0] = (float)__builtin_bit_cast(half_t, (unsigned short)(v.x & 0xFFFFu));
-    f[1] = (float)__builtin_bit_cast(half_t, (unsigned short)(v.x >> 16));
-    f[2] = (float)__builtin_bit_cast(half_t, (unsigned short)(v.y & 0xFFFFu));
-    f[3] = (float)__builtin_bit_cast(half_t, (unsigned short)(v.y >> 16));
+  static __device__ __forceinline__ void cvt(const raw &v, int par, float (&f)[4]) {
+    const int sh = 16 * par;
+    f[0] = (float)__builtin_bit_cast(half_t, (unsigned short)(v.x >> sh));
+    f[1] = (float)__builtin_bit_cast(half_t, (unsigned short)(v.y >> sh));
+    f[2] = (float)__builtin_bit_cast(half_t, (unsigned short)(v.z >> sh));
+    f[3] = (float)__builtin_bit_cast(half_t, (unsigned short)(v.w >> sh));
   }
 };
 
@@ -103,10 +119,6 @@ __device__ __forceinline__ void chunk_entries(const float (&f)[4], float4 (&v)[4
   v[1] = make_float4(-A + E, D + E, -D + E, A + E);
   v[2] = make_float4(-A - E, D - E, -D - E, A - E);
   v[3] = make_float4(-A + C, D + C, -D + C, A + C);
-}
-
-__device__ __forceinline__ float comp(const float4 &v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
 // LDS addressing.  Table addresses are 32-bit LDS byte offsets: a lane's table
@@ -168,7 +180,6 @@ constexpr int kG1Ksub = 16;                                   // groups per wind
 constexpr int kG1ChunkStride = 80;                            // bytes
 constexpr int kG1GroupStride = kChunksPerGroup * kG1ChunkStride + 64;  // 2624
 constexpr int kG1WindowBytes = kG1Ksub * kG1GroupStride;      // 41984
-constexpr int kG1WindowChunks = kG1Ksub * kChunksPerGroup;    // 512
 
 // Sum over the 32 chunks of one group of T_c[nibble c of the row's 128 bits].
 // base is the LDS byte offset of the group's first table.
@@ -244,7 +255,8 @@ __global__ __launch_bounds__(kG1Threads) void gemv_lut_kernel(
       for (int h = 0; h < 2; ++h) {
         const int c = tid + h * kG1Threads;
         const int j = min(w * kG1Ksub + c / kChunksPerGroup, G - 1);
-        xr[u][h] = Act<T>::load(x + (size_t)j * kGroup + (c % kChunksPerGroup) * 4);
+        xr[u][h] = Act<T>::load(x + (size_t)j * kGroup + chunk_base(c % kChunksPerGroup),
+                                chunk_parity(c % kChunksPerGroup));
       }
     }
 #pragma unroll
@@ -270,7 +282,7 @@ __global__ __launch_bounds__(kG1Threads) void gemv_lut_kernel(
       for (int h = 0; h < 2; ++h) {
         const int c = tid + h * kG1Threads;
         float f[4];
-        Act<T>::cvt(xr[u][h], f);
+        Act<T>::cvt(xr[u][h], chunk_parity(c % kChunksPerGroup), f);
         float4 v[4];
         chunk_entries(f, v);
         float4 *dst = reinterpret_cast<float4 *>(lut + (c / kChunksPerGroup) * kG1GroupStride +
@@ -334,7 +346,6 @@ __global__ __launch_bounds__(kG1Threads) void gemv_lut_kernel(
 
 constexpr int kRThreads = 512;
 constexpr int kRWaves = kRThreads / 64;
-constexpr int kRSlots = 32;                          // half-group slots per row
 constexpr int kRHalfPad = 64;                        // bytes between the two halves
 constexpr int kRGroupStride = kChunksPerGroup * kG1ChunkStride + kRHalfPad + 64;  // 2688
 constexpr int kRWindowBytes = kG1Ksub * kRGroupStride;                           // 43008
@@ -417,7 +428,8 @@ __global__ __launch_bounds__(kRThreads) void gemv_res_kernel(
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     const int j = min(w * kG1Ksub + tid / kChunksPerGroup, G - 1);
-    xr[w] = Act<T>::load(x + (size_t)j * kGroup + (tid % kChunksPerGroup) * 4);
+    xr[w] = Act<T>::load(x + (size_t)j * kGroup + chunk_base(tid % kChunksPerGroup),
+                         chunk_parity(tid % kChunksPerGroup));
   }
 
   // ---- scales and offsets first (they are small and the staging below waits
@@ -464,7 +476,7 @@ __global__ __launch_bounds__(kRThreads) void gemv_res_kernel(
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     float f[4];
-    Act<T>::cvt(xr[w], f);
+    Act<T>::cvt(xr[w], chunk_parity(tid % kChunksPerGroup), f);
     float4 v[4];
     chunk_entries(f, v);
     float4 *dst = reinterpret_cast<float4 *>(lut + w * kRWindowBytes +
@@ -827,7 +839,8 @@ skinny_lut_kernel(const uint32_t *__restrict__ bits, ReqTables st, int nreq,
 #pragma unroll
     for (int u = 0; u < Gm::rpt; ++u) {
       const int qs = min(q0 + u, nreq - 1);
-      o.x[u] = Act<T>::load(x + (size_t)qs * ldx + (size_t)jx * kGroup + bcl * 4);
+      o.x[u] = Act<T>::load(x + (size_t)qs * ldx + (size_t)jx * kGroup + chunk_base(bcl),
+                            chunk_parity(bcl));
     }
     const int js = min(w * kSkGroups + h, G - 1);
 #pragma unroll
@@ -842,7 +855,7 @@ skinny_lut_kernel(const uint32_t *__restrict__ bits, ReqTables st, int nreq,
 #pragma unroll
       for (int u = 0; u < Gm::rpt; ++u) {
         float f[4];
-        Act<T>::cvt(o.x[u], f);
+        Act<T>::cvt(o.x[u], chunk_parity(bcl), f);
         A[u] = f[0] + f[1];
         D[u] = f[0] - f[1];
         C[u] = f[2] + f[3];

@@ -90,9 +90,11 @@ typedef struct {
  * Bytes of the packed device layout for (P, M, K), or 0 if the shape is
  * invalid.  Layout: plane-major; within a plane, rows in tiles of 16 (the last
  * tile padded with clear bits); within a tile, group-major; within a group, the
- * 16 rows' 128 bits (16 bytes each, canonical bit order) are contiguous.  So
- * word index = (((i*MT + t)*G + j)*16 + r)*4 + q with MT = ceil(M/16),
- * G = K/128, row m = 16t + r, columns 128j + 32q .. 128j + 32q + 31.
+ * 16 rows' 128 bits (16 bytes each) are contiguous.  So word index =
+ * (((i*MT + t)*G + j)*16 + r)*4 + q with MT = ceil(M/16), G = K/128,
+ * row m = 16t + r, columns 128j + 32q .. 128j + 32q + 31; within that word,
+ * bit b holds column 128j + 32q + 2b for b < 16 and 128j + 32q + 2(b-16) + 1
+ * for b >= 16 (even columns in the low half, odd columns in the high half).
  * The first p planes are a contiguous prefix of p * (bytes / P) bytes.
  */
 size_t bcq_packed_bytes(int32_t P, int32_t M, int32_t K);

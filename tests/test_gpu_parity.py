@@ -82,8 +82,18 @@ def test_pack_unpack_round_trip_bit_exact(P, M, K):
     assert np.array_equal(back.cpu().numpy().view(np.uint32), w.signs)
 
 
+def packed_word(w):
+    """The documented in-word order: bit b holds column 2b (b < 16) or 2(b-16)+1."""
+    out = 0
+    for b in range(32):
+        col = 2 * b if b < 16 else 2 * (b - 16) + 1
+        out |= ((int(w) >> col) & 1) << b
+    return out
+
+
 def test_packed_layout_matches_documented_index():
-    """Word (((i*MT + t)*G + j)*16 + r)*4 + q holds row 16t+r, columns 128j+32q.."""
+    """Word (((i*MT + t)*G + j)*16 + r)*4 + q holds row 16t+r, columns 128j+32q..,
+    even columns in its low half and odd columns in its high half."""
     P, M, K = 2, 40, 384
     w = bcq_synth.make(M, K, P, seed=3)
     packed = torch.empty(bcq.bcq_packed_bytes(P, M, K) // 4, dtype=torch.int32, device="cuda")
@@ -96,7 +106,7 @@ def test_packed_layout_matches_documented_index():
                 for r in range(16):
                     for q in range(4):
                         m = 16 * t + r
-                        want = w.signs[i, m, 4 * j + q] if m < M else 0
+                        want = packed_word(w.signs[i, m, 4 * j + q]) if m < M else 0
                         assert got[(((i * MT + t) * G + j) * 16 + r) * 4 + q] == want
 
 
