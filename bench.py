@@ -271,8 +271,7 @@ def secondary(args, bcq, torch, bcq_synth):
         w = bcq_synth.make(M, K, 4, b=b, seed=5)
         rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
         Y = [torch.empty((b, M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
-        wsb = bcq.bcq_workspace_bytes(rot.stores[0], b)
-        ws = torch.empty(max(wsb // 4, 1), dtype=torch.float32, device="cuda")
+        ws = bcq.new_workspace(rot.stores[0], b)  # zeroed once; calls leave it zeroed
         d = time_calls(torch, lambda i: bcq.bcq_gemm_skinny(rot.stores[i % rot.n], p,
                                                            rot.x[i % rot.n], Y[i % rot.n],
                                                            workspace=ws), n, 10)

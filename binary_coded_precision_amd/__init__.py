@@ -164,6 +164,18 @@ def bcq_workspace_bytes(store: "Store", b: int) -> int:
     return int(load().bcq_workspace_bytes(store.ref(), b))
 
 
+def new_workspace(store: "Store", b: int):
+    """A device workspace of ``bcq_workspace_bytes(store, b)`` bytes for
+    ``bcq_gemm_skinny`` at batch b, or None when the call needs none.  Its
+    contents need no initialisation; calls that may overlap need separate ones."""
+    import torch
+
+    n = bcq_workspace_bytes(store, b)
+    if n == 0:
+        return None
+    return torch.empty((n + 3) // 4, dtype=torch.int32, device=store.bits.device)
+
+
 def bcq_gemm_skinny(store: "Store", p: int, X, Y, workspace=None, stream=None) -> None:
     """``Y[r] = product at precision p`` of ``X[r]`` for each row r of the [b][K] tensor X."""
     b = X.shape[0]

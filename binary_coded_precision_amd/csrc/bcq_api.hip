@@ -218,8 +218,8 @@ bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int
   const char *Xc = static_cast<const char *>(X);
   char *Yc = static_cast<char *>(Y);
   if (b >= 16 && store->scale_dtype == BCQ_F16) {
-    for (int32_t r0 = 0; r0 < b; r0 += 64) {
-      const int n = (b - r0) < 64 ? (b - r0) : 64;
+    for (int32_t r0 = 0; r0 < b; r0 += bcq::kMfMaxBatch) {
+      const int n = (b - r0) < bcq::kMfMaxBatch ? (b - r0) : bcq::kMfMaxBatch;
       hipError_t e = bcq::launch_gemm_mfma(store->bits, store->M, store->K, p, store->alpha[p],
                                            store->zero[p], Xc + (size_t)r0 * ldx * es, ldx, n,
                                            Yc + (size_t)r0 * ldy * es, ldy, workspace, stream);

@@ -70,12 +70,13 @@ hipError_t launch_skinny_dq(const uint32_t *bits, int M, int K, const void *alph
                             void *y, int ldy, hipStream_t s);
 
 // Batched products with >= 16 requests at one precision: fp16 dequantised
-// tiles on the matrix cores.
-// fp16 only, b <= 64 per launch; ws holds mfma_workspace_bytes(M, K, b) bytes.
+// tiles on the matrix cores.  fp16 only, b <= kMfMaxBatch per launch (a call
+// with more runs several launches in order); ws holds at least
+// mfma_workspace_bytes(M, K, b) bytes for the call's whole batch b.
+constexpr int kMfMaxBatch = 64;
 hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const void *alpha,
                             const void *zero, const void *x, int ldx, int b, void *y, int ldy,
                             void *ws, hipStream_t s);
-int mfma_slices(int M, int K);
 size_t mfma_workspace_bytes(int M, int K, int b);
 
 }  // namespace bcq

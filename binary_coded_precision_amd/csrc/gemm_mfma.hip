@@ -6,29 +6,46 @@
 // the decoded weights with the requests' activations, so it belongs on the
 // matrix cores; the BiLoCo summary's speed results make the same point for
 // its +-1 correction, whose add/subtract work grows with batch while the
-// weight read stays flat.  The decode (decode.h) is the same as the batched
-// vector kernel's: per plane and fp16 pair one shift, one bit-field insert and
-// one packed add, so a weight is decoded once per launch whatever the batch.
+// weight read stays flat.  A weight is decoded once per launch whatever the
+// batch (decode.h has the bit arithmetic).
 //
-// Operand layout.  A wavefront owns one 16-row tile.  For each group, lane
-// (r, h) decodes row r's h-th 32-column word into 16 fp16 pairs; pairs
-// 4n..4n+3 (columns 32h + 8n .. 8n+7) are that lane's A operand of MFMA n,
-// i.e. lane (r, h) supplies row r and k-block h of a 32-wide k slice made of
-// columns 8n..8n+7 of each of the group's four words.  The B operand of lane
-// (c, h) is then request c's activations at the same 8 columns: one 16-byte
-// LDS read of x in its natural order.  Four MFMAs cover a group for 16
-// requests; NT tiles of 16 requests reuse each decoded pair.
+// Operand layout.  A wavefront owns one 16-row tile and walks K in steps of
+// four groups.  Lane (r, h) takes row r of group h of the step: one 16-byte
+// load per plane brings its four sign words (128 columns), and the four lanes
+// of a row read four consecutive 256-byte blocks of the packed plane, so each
+// load instruction reads 1 KB contiguously.  MFMA n (n = 0..15) of a step
+// contracts 8-column block n of every group: lane (r, h) supplies row r's
+// weights at columns 8n..8n+7 of group h (fp16 pairs 4u..4u+3 of word n / 4,
+// u = n % 4) as its A operand, and request r's activations at the same
+// columns as its B operand.  The four k-blocks of one MFMA thus come from
+// four different groups, which is why the scale has to live in the A operand.
 //
-// Staging.  The four wavefronts (64 rows) share each window's activations,
-// staged in LDS as [group][word][8-column block][request] 16-byte blocks;
-// every word's region is padded by 128 bytes so the two words read by one
-// half-wavefront fall 32 banks apart.  The next window is loaded into
-// registers while the current one computes and written to the other LDS
-// buffer before the barrier, so one barrier per window suffices.
+// Two ways to apply the scales.
+//  * Per plane (up to 32 requests): A = the plane's +-alpha pair per column,
+//    one shift and one bit-field insert per pair, and one MFMA per plane plus
+//    one with A = (z, z) for the offset; the matrix cores do the sum over
+//    planes.  Two VALU operations per pair and plane.
+//  * Summed (48 and 64 requests): the weight z + sum +-alpha is formed on the
+//    vector ALUs (a third operation, a packed add, per pair and plane) and
+//    one MFMA per request tile contracts it, since with four request tiles
+//    the per-plane MFMAs would outnumber the VALU work they save.
 //
-// Split K.  blockIdx.y takes a contiguous run of windows; with more than one
-// run the partial products go to an fp32 workspace and a finalize kernel sums
-// them in a fixed order, so results are deterministic.
+// Staging.  The four wavefronts (64 rows) share each step's activations in
+// LDS as [request][group][8-column block] 16-byte blocks, the block index
+// XOR-swizzled by the request's low four bits: the 64 lanes writing one
+// request's 1 KB of a step land in distinct banks, and the 16 requests read at
+// one block land in 16 distinct 16-byte bank groups.  Activations of step s+1
+// are loaded into registers while step s computes and written to the other LDS
+// buffer before the barrier; sign words and scales are loaded two steps ahead.
+//
+// Split K.  blockIdx.y takes a contiguous run of steps (a slice); with more
+// than one slice the partial products go to an fp32 workspace and a finalize
+// kernel sums them in slice order, so results are deterministic.  (Summing
+// them in the same launch -- the last workgroup of a row block to arrive adds
+// the slices -- measured slower on gfx950: the hand-off across the XCDs' L2
+// caches needs either an L2 write-back per workgroup or write-through stores
+// and coherent reads, while the second launch of a captured graph costs
+// little.)
 #include "decode.h"
 
 namespace bcq {
@@ -38,174 +55,226 @@ using half_t = _Float16;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 // 16-byte blocks as a native vector (HIP's uint4 struct is copied with memcpy,
-// which keeps the staging registers from being promoted out of memory)
+// which keeps staging arrays from being promoted to registers)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMfWaves = 4;  // 16-row tiles per workgroup, one per wavefront
-constexpr int kMfThreads = 64 * kMfWaves;
-constexpr int kMfGroups = 4;           // groups per window
-constexpr int kMfWords = kGroup / 32;  // 32-column words per group
-constexpr int kMfBlocks = 4;           // 8-column blocks per word
+constexpr int kMfGroups = 4;           // groups per step (lane (r, h) takes group h)
+constexpr int kMfBlocks = kGroup / 8;  // 8-column blocks per group (MFMAs per step)
 
-template <int NB>
+// Wavefronts (16-row tiles) per workgroup: 8 -- two per SIMD, so one's waits
+// and issue stalls are filled by the other -- while the registers of two
+// wavefronts fit a SIMD (up to 32 requests); 4 above that.
+constexpr int mf_waves(int nt) { return nt <= 2 ? 8 : 4; }
+
+template <int NB, int W>
 struct MfStage {
-  static constexpr int kWordStride = kMfBlocks * NB + 8;  // 16-byte blocks
-  static constexpr int kGroupStride = kMfWords * kWordStride;
-  static constexpr int kBufBlocks = kMfGroups * kGroupStride;
-  static constexpr int kTasks = kMfGroups * kMfWords * kMfBlocks * NB / kMfThreads;  // NB / 4
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kBlocks = NB * kMfGroups * kMfBlocks;  // 16-byte blocks per step
+  static constexpr int kTasks = kBlocks / kThreads;           // NB / W per thread
 };
 
-// This thread's share of one window's activations (16-byte blocks).
-template <int NB>
+// LDS block of request q, group h of the step, 8-column block n.
+__device__ __forceinline__ int mf_slot(int q, int h, int n) {
+  return ((q * kMfGroups + h) << 4) + (n ^ (q & 15));
+}
+
+// This thread's share of one step's activations, and a mask of the blocks
+// that lie in a group past G (stored as zeros).
+template <int NB, int W>
 struct MfX {
-  u32x4 v[MfStage<NB>::kTasks];
+  u32x4 v[MfStage<NB, W>::kTasks];
+  uint32_t past;
 };
 
-// Operands of one window for one lane: sign words, scales and offsets of its
-// row in each of the window's groups.
+// One lane's operands of one step: its four sign words per plane, the scales
+// and offset of its (row, group) as raw fp16 bits.
 template <int P>
 struct MfW {
-  uint32_t bits[kMfGroups][P];
-  uint32_t a[kMfGroups][P];
-  uint32_t z[kMfGroups];
+  u32x4 bits[P];
+  uint32_t a[P];
+  uint32_t z;
 };
 
-// NT tiles of 16 requests, P planes.  The load phase has no branches: rows past
-// M, tiles past MT, requests past b and groups past G read clamped in-range
-// addresses whose values are never stored.
-template <int NT, int P>
-__global__ __launch_bounds__(kMfThreads) void gemm_mfma_kernel(
-    const uint32_t *__restrict__ bits, const half_t *__restrict__ alpha,
+template <bool SUM, int P>
+constexpr int mf_accs() { return SUM ? 4 : P + 1; }
+
+// NT tiles of 16 requests, P planes.  Loads clamp rows past M, tiles past MT,
+// requests past b and groups past G to in-range addresses; the activations of
+// a group past G are staged as zeros, so it adds nothing (its clamped weights
+// are finite), and rows or requests past the end are never stored.  Masks are
+// applied to the staged activations, never to loaded values right after their
+// load, so that no wait for a load is placed ahead of its use.
+template <int NT, int P, bool SUM, int W>
+__global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
+    const u32x4 *__restrict__ bits, const half_t *__restrict__ alpha,
     const half_t *__restrict__ zero, const half_t *__restrict__ X, int ldx, int b,
-    half_t *__restrict__ Y, int ldy, float *__restrict__ ws, int M, int G, int MT, int wps) {
+    half_t *__restrict__ Y, int ldy, float *__restrict__ ws, int M, int G, int MT, int sps) {
   constexpr int NB = 16 * NT;
-  using St = MfStage<NB>;
+  constexpr int NA = mf_accs<SUM, P>();
+  using St = MfStage<NB, W>;
   using OpsW = MfW<P>;
-  using OpsX = MfX<NB>;
-  __shared__ u32x4 xs[2][St::kBufBlocks];
+  using OpsX = MfX<NB, W>;
+  __shared__ u32x4 xs[2][St::kBlocks];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r = lane & 15;
   const int h = lane >> 4;
-  const int t = blockIdx.x * kMfWaves + wave;
+  const int t = blockIdx.x * W + wave;
   const int t_safe = min(t, MT - 1);
   const int m_safe = min(t_safe * kTileRows + r, M - 1);
-  const int nwin = (G + kMfGroups - 1) / kMfGroups;
-  const int s = blockIdx.y;
-  const int w0 = s * wps;
-  const int w1 = min(nwin, w0 + wps);  // the host leaves no slice empty
-  const size_t plane_words = (size_t)MT * G * kTileRows * 4;
+  const int nsteps = (G + kMfGroups - 1) / kMfGroups;
+  const int sl = blockIdx.y;
+  const int s0 = sl * sps;
+  const int s1 = min(nsteps, s0 + sps);  // the host leaves no slice empty
+  const size_t plane_blocks = (size_t)MT * G * kTileRows;
   const size_t MG = (size_t)M * G;
-  const uint32_t *tb = bits + ((size_t)t_safe * G * kTileRows + r) * 4 + h;
+  const u32x4 *tb = bits + (size_t)t_safe * G * kTileRows + r;
 
-  // staging: block u*256 + tid is (group, word, 8-column block, request), request fastest
-  auto fetch_x = [&](int w, OpsX &o) __attribute__((always_inline)) {
+  // block u*256 + tid of a step: 8-column block n fastest, then group, then
+  // request, so a wavefront reads 1 KB of one request's row
+  auto fetch_x = [&](int s, OpsX &o) __attribute__((always_inline)) {
+    const int g = (tid >> 4) & 3;  // the same group for every task of this thread
+    o.past = s * kMfGroups + g >= G ? ~0u : 0u;
+    const int j = min(s * kMfGroups + g, G - 1);
 #pragma unroll
     for (int u = 0; u < St::kTasks; ++u) {
-      const int id = u * kMfThreads + tid;
-      const int q = min(id % NB, b - 1);
-      const int blk = (id / NB) % kMfBlocks;
-      const int wrd = (id / (NB * kMfBlocks)) % kMfWords;
-      const int grp = id / (NB * kMfBlocks * kMfWords);
-      const int j = min(w * kMfGroups + grp, G - 1);
+      const int id = u * St::kThreads + tid;
+      const int q = min(id >> 6, b - 1);
       o.v[u] = *reinterpret_cast<const u32x4 *>(X + (size_t)q * ldx + (size_t)j * kGroup +
-                                                 wrd * 32 + blk * 8);
+                                                 (id & 15) * 8);
     }
   };
   auto write_x = [&](const OpsX &o, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < St::kTasks; ++u) {
-      const int id = u * kMfThreads + tid;
-      const int q = id % NB;
-      const int blk = (id / NB) % kMfBlocks;
-      const int wrd = (id / (NB * kMfBlocks)) % kMfWords;
-      const int grp = id / (NB * kMfBlocks * kMfWords);
-      xs[buf][grp * St::kGroupStride + wrd * St::kWordStride + blk * NB + q] = o.v[u];
+      const int id = u * St::kThreads + tid;
+      xs[buf][mf_slot(id >> 6, (id >> 4) & 3, id & 15)] = o.v[u] & ~o.past;
     }
   };
-  auto fetch_w = [&](int w, OpsW &o) __attribute__((always_inline)) {
+  auto fetch_w = [&](int s, OpsW &o) __attribute__((always_inline)) {
+    const int j = min(s * kMfGroups + h, G - 1);
 #pragma unroll
-    for (int g = 0; g < kMfGroups; ++g) {
-      const int j = min(w * kMfGroups + g, G - 1);
-#pragma unroll
-      for (int i = 0; i < P; ++i) {
-        o.bits[g][i] = tb[i * plane_words + (size_t)j * kTileRows * 4];
-        o.a[g][i] = *reinterpret_cast<const unsigned short *>(alpha + i * MG +
-                                                              (size_t)m_safe * G + j);
-      }
-      o.z[g] = *reinterpret_cast<const unsigned short *>(zero + (size_t)m_safe * G + j);
+    for (int i = 0; i < P; ++i) {
+      o.bits[i] = tb[i * plane_blocks + (size_t)j * kTileRows];
+      o.a[i] = *reinterpret_cast<const unsigned short *>(alpha + i * MG + (size_t)m_safe * G + j);
     }
+    o.z = *reinterpret_cast<const unsigned short *>(zero + (size_t)m_safe * G + j);
   };
 
-  // one accumulator per (request tile, 8-column block): the four MFMAs of a
-  // group are independent, so they issue back to back instead of waiting for
-  // each other's result; the blocks are summed once at the end
-  floatx4 acc[NT][kMfBlocks];
+  floatx4 acc[NT][NA];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int n = 0; n < kMfBlocks; ++n) acc[nt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NA; ++k) acc[nt][k] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int w, const OpsW &o, int buf) __attribute__((always_inline)) {
+  auto compute = [&](const OpsW &o, int buf) __attribute__((always_inline)) {
+    // per plane: sign words inverted unless alpha < 0 (a clear bit then
+    // yields +|alpha|), and |alpha| in both halves
+    uint32_t wp[P][4], mag[P];
 #pragma unroll
-    for (int g = 0; g < kMfGroups; ++g) {
-      if (w * kMfGroups + g >= G) break;  // uniform
-      dq_half2 wv[kDqPairs];
-      dq_init(wv, o.z[g]);
+    for (int i = 0; i < P; ++i) {
+      const uint32_t a16 = o.a[i];
+      const uint32_t neg = (uint32_t)((int32_t)(a16 << 16) >> 31);
+      mag[i] = (a16 & 0x7FFFu) * 0x10001u;
 #pragma unroll
-      for (int i = 0; i < P; ++i) dq_plane(wv, o.bits[g][i], o.a[g][i]);
-      const u32x4 *xb = &xs[buf][g * St::kGroupStride + h * St::kWordStride + r];
+      for (int q = 0; q < 4; ++q) wp[i][q] = ~(o.bits[i][q] ^ neg);
+    }
+    const uint32_t z2 = o.z * 0x10001u;
+    const u32x4 *xb = xs[buf];
 #pragma unroll
-      for (int n = 0; n < kMfBlocks; ++n) {
+    for (int n = 0; n < kMfBlocks; ++n) {
+      const int q = n >> 2;
+      const int u = n & 3;
+      half8 bop[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        bop[nt] = __builtin_bit_cast(half8, xb[mf_slot(nt * 16 + r, h, n)]);
+      if constexpr (SUM) {
+        dq_half2 w[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) w[v] = dq_as_h2(z2);
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            w[v] += dq_as_h2(((wp[i][q] << (15 - (4 * u + v))) & 0x80008000u) | mag[i]);
         half8 a;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          a[2 * u] = wv[4 * n + u][0];
-          a[2 * u + 1] = wv[4 * n + u][1];
+        for (int v = 0; v < 4; ++v) {
+          a[2 * v] = w[v][0];
+          a[2 * v + 1] = w[v][1];
         }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const half8 bop = __builtin_bit_cast(half8, xb[n * NB + nt * 16]);
-          acc[nt][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop, acc[nt][n], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt)
+          acc[nt][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop[nt], acc[nt][u], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+          u32x4 av;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            av[v] = ((wp[i][q] << (15 - (4 * u + v))) & 0x80008000u) | mag[i];
+          const half8 a = __builtin_bit_cast(half8, av);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            acc[nt][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop[nt], acc[nt][i], 0, 0, 0);
         }
+        const half8 az = __builtin_bit_cast(half8, u32x4{z2, z2, z2, z2});
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[nt][P] = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bop[nt], acc[nt][P], 0, 0, 0);
       }
     }
   };
 
-  // pipeline over the slice's windows: window w computes from one LDS buffer
-  // and its sign words and scales (loaded two windows earlier); then window
-  // w+1's activations (loaded a window earlier) go to the other buffer, and
-  // the loads of window w+2 are issued last, so the loop header sees the same
-  // loads in flight on every path and its waits stay partial
+  // pipeline over the slice's steps, two per iteration: step s computes from
+  // one LDS buffer and its sign words and scales (loaded two steps earlier);
+  // then step s+1's activations (loaded a step earlier) go to the other
+  // buffer, and the loads of step s+2 are issued last.  Every path issues the
+  // same loads (a fetch past the slice's last step re-reads that step, lines
+  // already in flight) and the loop has no exit but its header, so the loads
+  // stay where they are and the waits at the header stay partial.  An odd
+  // last step runs after the loop, from buffer 0.
+  const int s_last = s1 - 1;
   OpsW wa, wb;
   OpsX xo;
-  fetch_x(w0, xo);
-  fetch_w(w0, wa);
+  fetch_x(s0, xo);
+  fetch_w(s0, wa);
   write_x(xo, 0);
-  fetch_x(w0 + 1, xo);
-  fetch_w(w0 + 1, wb);
+  fetch_x(min(s0 + 1, s_last), xo);
+  fetch_w(min(s0 + 1, s_last), wb);
   __syncthreads();
-  for (int w = w0; w < w1; w += 2) {
-    compute(w, wa, 0);
+  int s = s0;
+  for (; s + 1 < s1; s += 2) {
+    // no instruction crosses a sched_barrier: the scheduler would otherwise
+    // start a step's scale arithmetic, or the staging of the next step's
+    // activations, early and wait there for loads issued just before
+    compute(wa, 0);
+    __builtin_amdgcn_sched_barrier(0);
     write_x(xo, 1);
-    fetch_x(w + 2, xo);
-    fetch_w(w + 2, wa);
+    fetch_x(min(s + 2, s_last), xo);
+    fetch_w(min(s + 2, s_last), wa);
     __syncthreads();
-    if (w + 1 >= w1) break;  // uniform
-    compute(w + 1, wb, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wb, 1);
+    __builtin_amdgcn_sched_barrier(0);
     write_x(xo, 0);
-    fetch_x(w + 3, xo);
-    fetch_w(w + 3, wb);
+    fetch_x(min(s + 3, s_last), xo);
+    fetch_w(min(s + 3, s_last), wb);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (s < s1) compute(wa, 0);
 
   // D layout: lane (r, h) holds rows 4h .. 4h+3 of the tile for request r of each tile
   if (t < MT) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const floatx4 d = (acc[nt][0] + acc[nt][1]) + (acc[nt][2] + acc[nt][3]);
+      floatx4 d = acc[nt][0];
+#pragma unroll
+      for (int k = 1; k < NA; ++k) d += acc[nt][k];
       const int n = nt * 16 + r;
       if (n >= b) continue;
 #pragma unroll
@@ -215,13 +284,14 @@ __global__ __launch_bounds__(kMfThreads) void gemm_mfma_kernel(
         if (ws == nullptr)
           Y[(size_t)n * ldy + mm] = (half_t)d[v];
         else
-          ws[((size_t)s * b + n) * M + mm] = d[v];
+          ws[((size_t)sl * b + n) * M + mm] = d[v];
       }
     }
   }
 }
 
-// Y[n][m] = sum over slices of the partial products, in slice order.
+// Y[n][m] = sum over slices of the partial products, in slice order.  The
+// partials of one output are loaded eight at a time so their latencies overlap.
 __global__ __launch_bounds__(256) void splitk_finalize_kernel(const float *__restrict__ ws,
                                                               int slices, int b, int M,
                                                               half_t *__restrict__ Y, int ldy) {
@@ -229,37 +299,66 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(const float *__res
   if (idx >= (size_t)b * M) return;
   const int n = (int)(idx / M);
   const int mm = (int)(idx % M);
+  const size_t stride = (size_t)b * M;
+  const float *pp = ws + idx;
   float s = 0.f;
-  for (int q = 0; q < slices; ++q) s += ws[((size_t)q * b + n) * M + mm];
+  for (int q0 = 0; q0 < slices; q0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = q0 + k < slices ? pp[(size_t)(q0 + k) * stride] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += v[k];
+  }
   Y[(size_t)n * ldy + mm] = (half_t)s;
 }
 
-// Windows per slice and slice count for (M, K): about 256 workgroups, at least
-// two windows per slice (the pipeline's depth), and no empty slice.
-void mfma_split(int M, int K, int *wps, int *slices) {
+// Steps per slice and slice count for (M, K) and W wavefronts per workgroup.
+// One workgroup is resident per compute unit (the register or LDS budget of
+// either size allows no second), so a launch runs in rounds of kMfSlots
+// workgroups.  A round costs its steps per slice plus about one step of start-up
+// (the first loads' latency, measured near one step's compute); the split
+// minimises rounds x (steps per slice + 1), the fewest slices (least
+// partial-sum traffic) among equals.  The count is MI355X's, fixed rather than
+// queried, because the workspace size follows from it and must not depend on
+// which device is current.
+constexpr int kMfSlots = 256;
+
+void mfma_split(int M, int K, int W, int *sps, int *slices) {
   const int G = K / kGroup;
-  const int nwin = (G + kMfGroups - 1) / kMfGroups;
-  const int wgs = (row_tiles(M) + kMfWaves - 1) / kMfWaves;
-  int s = (256 + wgs - 1) / wgs;
-  const int smax = nwin / 2 > 0 ? nwin / 2 : 1;
-  s = s < 1 ? 1 : (s > smax ? smax : s);
-  *wps = (nwin + s - 1) / s;
-  *slices = (nwin + *wps - 1) / *wps;
+  const int nsteps = (G + kMfGroups - 1) / kMfGroups;
+  const long wgs = (row_tiles(M) + W - 1) / W;
+  long best = -1;
+  for (int s = 1; s <= nsteps; ++s) {
+    const int sp = (nsteps + s - 1) / s;  // steps per slice
+    const int sl = (nsteps + sp - 1) / sp;  // slices actually used
+    if (sl != s) continue;                  // same split as a smaller s
+    const long cost = (wgs * sl + kMfSlots - 1) / kMfSlots * (sp + 1);
+    if (best < 0 || cost < best) {
+      best = cost;
+      *sps = sp;
+      *slices = sl;
+    }
+  }
+}
+
+// Workspace of one launch of n requests: fp32 partials [slice][request][row].
+size_t launch_workspace_bytes(int M, int K, int n) {
+  int sps, s;
+  mfma_split(M, K, mf_waves((n + 15) / 16), &sps, &s);
+  return s > 1 ? (size_t)s * n * M * sizeof(float) : 0;
 }
 
 }  // namespace
 
-int mfma_slices(int M, int K) {
-  int wps, s;
-  mfma_split(M, K, &wps, &s);
-  return s;
-}
-
 size_t mfma_workspace_bytes(int M, int K, int b) {
-  const int s = mfma_slices(M, K);
-  if (s <= 1) return 0;
-  const int bb = b < 64 ? b : 64;
-  return (size_t)s * bb * M * sizeof(float);
+  // the launches of one call run in order and reuse the workspace
+  size_t need = launch_workspace_bytes(M, K, b < kMfMaxBatch ? b : kMfMaxBatch);
+  const int rest = b % kMfMaxBatch;
+  if (b > kMfMaxBatch && rest > 0) {
+    const size_t r = launch_workspace_bytes(M, K, rest);
+    need = r > need ? r : need;
+  }
+  return need;
 }
 
 hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const void *alpha,
@@ -267,18 +366,20 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
                             void *ws, hipStream_t s) {
   const int G = K / kGroup;
   const int MT = row_tiles(M);
-  int wps, S;
-  mfma_split(M, K, &wps, &S);
+  const int NT = (b + 15) / 16;
+  const int W = mf_waves(NT);
+  int sps, S;
+  mfma_split(M, K, W, &sps, &S);
+  const u32x4 *b4 = reinterpret_cast<const u32x4 *>(bits);
   const half_t *a = static_cast<const half_t *>(alpha);
   const half_t *z = static_cast<const half_t *>(zero);
   const half_t *X = static_cast<const half_t *>(x);
   half_t *Y = static_cast<half_t *>(y);
   float *w = S > 1 ? static_cast<float *>(ws) : nullptr;
-  dim3 grid((MT + kMfWaves - 1) / kMfWaves, S), block(kMfThreads);
-  const int NT = (b + 15) / 16;
-#define BCQ_MF(NTV, PV)                                                                     \
-  hipLaunchKernelGGL((gemm_mfma_kernel<NTV, PV>), grid, block, 0, s, bits, a, z, X, ldx, b, Y, \
-                     ldy, w, M, G, MT, wps)
+  dim3 grid((MT + W - 1) / W, S), block(64 * W);
+#define BCQ_MF(NTV, PV)                                                                  \
+  hipLaunchKernelGGL((gemm_mfma_kernel<NTV, PV, (NTV >= 3), mf_waves(NTV)>), grid, block, 0, \
+                     s, b4, a, z, X, ldx, b, Y, ldy, w, M, G, MT, sps)
 #define BCQ_MF_NT(NTV)              \
   switch (p) {                      \
     case 1: BCQ_MF(NTV, 1); break;  \

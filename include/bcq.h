@@ -133,9 +133,11 @@ bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype 
  * weight pair per request on the vector ALUs (the decoded weight is rounded to
  * fp16).  fp16 batches of 16 and more dequantise tiles of W to fp16 and
  * contract them on the matrix cores; that path splits K over workgroups and needs
- * bcq_workspace_bytes(store, b) bytes of device workspace (4-byte aligned,
- * contents need no initialisation, clobbered by the call).  workspace may be
- * NULL when that size is 0; a smaller workspace gives BCQ_ERR_INVALID_ARG.
+ * bcq_workspace_bytes(store, b) bytes of device workspace (4-byte aligned) for
+ * the K slices' partial sums: contents need no initialisation and are
+ * clobbered by the call, so calls that may run at the same time need separate
+ * workspaces.  workspace may be NULL when that size is 0; a smaller workspace
+ * gives BCQ_ERR_INVALID_ARG.
  */
 bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int32_t b,
                            int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,

@@ -329,15 +329,18 @@ def test_mixed_rejects_bad_entry_and_writes_nothing():
 
 # ---------------------------------------------------------------- matrix-core path
 
+# shapes: ragged last step (K = 640, 384: 5 and 3 groups), one and several
+# K-slices, odd step counts per slice (K = 1408, 2688), every request-tile
+# count (b = 16..64) and a batch split over two launches (b = 80)
 @pytest.mark.parametrize("M,K,b", [(64, 512, 16), (100, 640, 17), (48, 1024, 32), (80, 2048, 64),
-                                   (33, 384, 80), (4096, 4096, 16)])
+                                   (33, 384, 80), (200, 1408, 48), (96, 2688, 40),
+                                   (4096, 4096, 16)])
 def test_mfma_batches(M, K, b):
     w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=M + b, outlier_frac=0.01)
     st = store_of(w)
-    ws_bytes = bcq.bcq_workspace_bytes(st, b)
-    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda")
+    ws = bcq.new_workspace(st, b)  # zeroed once, reused by every call below
     rows = sample_rows(M, 256)
-    for p in (2, 4):
+    for p in (1, 2, 3, 4):
         say("mfma", M, K, b, p)
         Y = torch.empty((b, M), dtype=torch.float16, device="cuda")
         bcq.bcq_gemm_skinny(st, p, dev(w.x), Y, workspace=ws)
@@ -347,14 +350,35 @@ def test_mfma_batches(M, K, b):
             assert rel_l2(got[r], ref[r]) <= 2e-3, (p, r)
 
 
+def test_mfma_workspace_reused_across_batch_sizes():
+    # one workspace, sized for the largest batch and never cleared, reused in
+    # stream order by calls whose launches use different workgroup sizes and
+    # slice counts (b = 80 runs 64 + 16 requests)
+    M, K = 200, 2688
+    w = bcq_synth.make(M, K, 4, b=80, dtype=np.float16, seed=91)
+    st = store_of(w)
+    ws = bcq.new_workspace(st, 80)
+    assert ws is not None
+    ws.fill_(0x7FC00000)  # stale contents (NaN bits) must not leak into a result
+    rows = sample_rows(M, 64)
+    for b, p in [(80, 4), (16, 2), (48, 3), (80, 1), (16, 4)]:
+        say("mfma workspace reuse", b, p)
+        assert bcq.bcq_workspace_bytes(st, b) <= ws.numel() * 4
+        Y = torch.empty((b, M), dtype=torch.float16, device="cuda")
+        bcq.bcq_gemm_skinny(st, p, dev(w.x[:b]), Y, workspace=ws)
+        ref = oracle_y(w, w.x[:b], [p] * b, rows)
+        got = Y.cpu().numpy()[:, rows]
+        for r in range(b):
+            assert rel_l2(got[r], ref[r]) <= 2e-3, (b, p, r)
+
+
 @pytest.mark.parametrize("shape", ["q_o", "k_v", "gate_up", "down"])
 @pytest.mark.parametrize("b", [16, 64])
 def test_config5_layer_sweep_sampled(shape, b):
     M, K = bcq_synth.LAYER_SHAPES[shape]
     w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=5)
     st = store_of(w)
-    ws = torch.empty(max(bcq.bcq_workspace_bytes(st, b) // 4, 1), dtype=torch.float32,
-                     device="cuda")
+    ws = bcq.new_workspace(st, b)
     say("mfma cfg5", shape, b)
     Y = torch.empty((b, M), dtype=torch.float16, device="cuda")
     bcq.bcq_gemm_skinny(st, 4, dev(w.x), Y, workspace=ws)
