@@ -246,11 +246,14 @@ def secondary(args, bcq, torch, bcq_synth):
     rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=w.b)
     Y = [torch.empty((w.b, w.M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
     pr = [int(p) for p in w.p_req]
+    ws = bcq.new_workspace(rot.stores[0], w.b)
     d_mixed = time_calls(torch, lambda i: bcq.bcq_gemv_mixed_p(rot.stores[i % rot.n], pr,
-                                                              rot.x[i % rot.n], Y[i % rot.n]),
+                                                              rot.x[i % rot.n], Y[i % rot.n],
+                                                              workspace=ws),
                          n, 10)
     d_uni = time_calls(torch, lambda i: bcq.bcq_gemm_skinny(rot.stores[i % rot.n], max(pr),
-                                                           rot.x[i % rot.n], Y[i % rot.n]),
+                                                           rot.x[i % rot.n], Y[i % rot.n],
+                                                           workspace=ws),
                        n, 10)
     nb = mixed_bytes(w.M, w.K, pr)
     rows["mixed_p_4096x4096_b8"] = {
@@ -259,7 +262,7 @@ def secondary(args, bcq, torch, bcq_synth):
         "uniform_pmax_us": round(d_uni * 1e3, 3),
         "GBps": round(nb / (d_mixed * 1e-3) / 1e9, 1),
     }
-    del rot, Y
+    del rot, Y, ws
 
     # small batches (MLP shapes, p = 3) and matrix-core batches (p = 4)
     for (M, K), b, p in [((4096, 4096), 2, 4), ((4096, 4096), 4, 4), ((4096, 4096), 8, 4),

@@ -94,7 +94,7 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
                                            ctypes.c_int, vp, sz, vp]),
         "bcq_workspace_bytes": (sz, [st, i32]),
         "bcq_gemv_mixed_p": (ctypes.c_int, [st, vp, vp, i32, i32, ctypes.c_int, vp, i32,
-                                            ctypes.c_int, vp]),
+                                            ctypes.c_int, vp, sz, vp]),
         "bcq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -166,7 +166,8 @@ def bcq_workspace_bytes(store: "Store", b: int) -> int:
 
 def new_workspace(store: "Store", b: int):
     """A device workspace of ``bcq_workspace_bytes(store, b)`` bytes for
-    ``bcq_gemm_skinny`` at batch b, or None when the call needs none.  Its
+    ``bcq_gemm_skinny`` or ``bcq_gemv_mixed_p`` at batch b, or None when the
+    call needs none.  Its
     contents need no initialisation; calls that may overlap need separate ones."""
     import torch
 
@@ -177,8 +178,13 @@ def new_workspace(store: "Store", b: int):
 
 
 def bcq_gemm_skinny(store: "Store", p: int, X, Y, workspace=None, stream=None) -> None:
-    """``Y[r] = product at precision p`` of ``X[r]`` for each row r of the [b][K] tensor X."""
+    """``Y[r] = product at precision p`` of ``X[r]`` for each row r of the [b][K] tensor X.
+
+    ``workspace=None`` allocates the workspace the call needs (through torch);
+    pass one from :func:`new_workspace` to keep allocation out of a hot loop."""
     b = X.shape[0]
+    if workspace is None:
+        workspace = new_workspace(store, b)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("bcq_gemm_skinny",
            load().bcq_gemm_skinny(store.ref(), p, _ptr(X), b, X.stride(0), _dtype_code(X),
@@ -186,13 +192,18 @@ def bcq_gemm_skinny(store: "Store", p: int, X, Y, workspace=None, stream=None) -
                                   ws_bytes, _stream(stream)))
 
 
-def bcq_gemv_mixed_p(store: "Store", p_host: Sequence[int], X, Y, stream=None) -> None:
-    """Request r at its own precision ``p_host[r]``."""
+def bcq_gemv_mixed_p(store: "Store", p_host: Sequence[int], X, Y, workspace=None,
+                     stream=None) -> None:
+    """Request r at its own precision ``p_host[r]`` (workspace as in :func:`bcq_gemm_skinny`)."""
     b = X.shape[0]
     ps = (ctypes.c_int32 * b)(*[int(v) for v in p_host])
+    if workspace is None:
+        workspace = new_workspace(store, b)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("bcq_gemv_mixed_p",
            load().bcq_gemv_mixed_p(store.ref(), ps, _ptr(X), b, X.stride(0), _dtype_code(X),
-                                   _ptr(Y), Y.stride(0), _dtype_code(Y), _stream(stream)))
+                                   _ptr(Y), Y.stride(0), _dtype_code(Y), _ptr(workspace),
+                                   ws_bytes, _stream(stream)))
 
 
 # ----------------------------------------------------------------------------- store

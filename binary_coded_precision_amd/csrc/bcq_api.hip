@@ -11,7 +11,11 @@ using bcq::kGroup;
 
 constexpr int32_t kMaxM = 1 << 24;
 constexpr int32_t kMaxK = 1 << 20;
-constexpr int32_t kDqMinBatch = 5;  // smallest fp16 batch sent to the decode kernel
+// Smallest fp16 batch sent to the matrix cores.  From 3 requests the decoded
+// tiles on the matrix cores beat the per-request table lookups at every shape
+// measured on gfx950 (4096x4096, 14336x4096, 4096x14336, p = 3 and 4); at 2
+// the table kernel is as fast or faster.
+constexpr int32_t kMfMinBatch = 3;
 
 size_t dtype_size(bcq_dtype d) { return d == BCQ_F16 ? 2 : 4; }
 bool dtype_valid(bcq_dtype d) { return d == BCQ_F16 || d == BCQ_F32; }
@@ -110,53 +114,30 @@ bcq_status run_table_batches(const bcq_store *st, const int32_t *p_of, const cha
   return BCQ_OK;
 }
 
-// fp16 requests through the decode kernel, up to kDqMaxReq per launch.  When
-// every precision used reads the same scale chain (alpha[p] and zero[p] alias
-// those of the largest p -- the shared-store layout), one launch serves all its
-// requests and the planes are read once; each request takes the weight after
-// its own p planes.  Otherwise the requests are grouped by precision and each
-// group reads its own tables.  A group of one request goes to the batch-1
-// kernel.
-bcq_status run_dq_batches(const bcq_store *st, const int32_t *p_of, const char *X, int32_t b,
-                          int32_t ldx, char *Y, int32_t ldy, hipStream_t stream) {
+// fp16 requests through the matrix-core kernel in launches of up to `chunk`
+// requests.  The kernel decodes p planes with alpha[p] / zero[p]; p_of (host,
+// b values, or nullptr for all p) gives each request's own precision, every
+// one of which must read the same tables (checked by the caller).
+bcq_status run_mfma_batches(const bcq_store *st, int32_t p, const int32_t *p_of, const char *X,
+                            int32_t b, int32_t ldx, char *Y, int32_t ldy, void *ws, int chunk,
+                            hipStream_t stream) {
   const size_t es = 2;
-  int pmax = 0;
-  for (int32_t r = 0; r < b; ++r) pmax = p_of[r] > pmax ? p_of[r] : pmax;
-  bool shared = true, uniform = true;
-  for (int32_t r = 0; r < b; ++r) {
-    shared = shared && st->alpha[p_of[r]] == st->alpha[pmax] && st->zero[p_of[r]] == st->zero[pmax];
-    uniform = uniform && p_of[r] == pmax;
+  for (int32_t r0 = 0; r0 < b; r0 += chunk) {
+    const int n = (b - r0) < chunk ? (b - r0) : chunk;
+    hipError_t e = bcq::launch_gemm_mfma(st->bits, st->M, st->K, p, st->alpha[p], st->zero[p],
+                                         X + (size_t)r0 * ldx * es, ldx, n,
+                                         Y + (size_t)r0 * ldy * es, ldy, ws,
+                                         p_of != nullptr ? p_of + r0 : nullptr, stream);
+    if (e != hipSuccess) return BCQ_ERR_HIP;
   }
-  // a launch mixing precisions holds fewer requests (see kDqMaxMixedReq)
-  const int cap = (shared && !uniform) ? bcq::kDqMaxMixedReq : bcq::kDqMaxReq;
-  // groups: one (chain precision, request subset) per launch
-  for (int chain = shared ? pmax : 1; chain <= pmax; ++chain) {
-    bcq::DqRequests rq{};
-    int p0 = 0;  // precision of the first request of the pending launch
-    auto flush = [&]() -> bcq_status {
-      if (rq.n == 0) return BCQ_OK;
-      hipError_t e;
-      if (rq.n == 1)
-        e = bcq::launch_gemv_lut(st->bits, st->M, st->K, p0, st->alpha[p0], st->zero[p0],
-                                 X + (size_t)rq.row[0] * ldx * es,
-                                 Y + (size_t)rq.row[0] * ldy * es, st->scale_dtype, stream);
-      else
-        e = bcq::launch_skinny_dq(st->bits, st->M, st->K, st->alpha[chain], st->zero[chain], rq,
-                                  X, ldx, Y, ldy, stream);
-      rq = bcq::DqRequests{};
-      p0 = 0;
-      return e == hipSuccess ? BCQ_OK : BCQ_ERR_HIP;
-    };
-    for (int32_t r = 0; r < b; ++r) {
-      if (!shared && p_of[r] != chain) continue;
-      if (rq.n == 0) p0 = p_of[r];
-      rq.row[rq.n] = r;
-      rq.at[p_of[r] - 1] |= 1u << rq.n;
-      ++rq.n;
-      if (rq.n == cap) BCQ_TRY(flush());
-    }
-    BCQ_TRY(flush());
-  }
+  return BCQ_OK;
+}
+
+// Workspace checks shared by the batched products.
+bcq_status check_workspace(const bcq_store *st, int32_t b, const void *ws, size_t ws_bytes) {
+  const size_t need = bcq_workspace_bytes(st, b);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return BCQ_ERR_INVALID_ARG;
+  if (need > 0 && !aligned(ws, 4)) return BCQ_ERR_ALIGNMENT;
   return BCQ_OK;
 }
 
@@ -198,7 +179,7 @@ bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype 
 
 size_t bcq_workspace_bytes(const bcq_store *store, int32_t b) {
   if (check_store(store) != BCQ_OK || b < 1 || b > BCQ_MAX_BATCH) return 0;
-  if (b < 16 || store->scale_dtype != BCQ_F16) return 0;
+  if (b < kMfMinBatch || store->scale_dtype != BCQ_F16) return 0;
   return bcq::mfma_workspace_bytes(store->M, store->K, b);
 }
 
@@ -210,43 +191,43 @@ bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int
   BCQ_TRY(check_precision(store, p));
   BCQ_TRY(check_dtypes(store, x_dtype, y_dtype));
   BCQ_TRY(check_batch(store, X, b, ldx, Y, ldy));
-  const size_t need = bcq_workspace_bytes(store, b);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return BCQ_ERR_INVALID_ARG;
-  if (need > 0 && !aligned(workspace, 4)) return BCQ_ERR_ALIGNMENT;
-
-  const size_t es = dtype_size(store->scale_dtype);
+  BCQ_TRY(check_workspace(store, b, workspace, workspace_bytes));
   const char *Xc = static_cast<const char *>(X);
   char *Yc = static_cast<char *>(Y);
-  if (b >= 16 && store->scale_dtype == BCQ_F16) {
-    for (int32_t r0 = 0; r0 < b; r0 += bcq::kMfMaxBatch) {
-      const int n = (b - r0) < bcq::kMfMaxBatch ? (b - r0) : bcq::kMfMaxBatch;
-      hipError_t e = bcq::launch_gemm_mfma(store->bits, store->M, store->K, p, store->alpha[p],
-                                           store->zero[p], Xc + (size_t)r0 * ldx * es, ldx, n,
-                                           Yc + (size_t)r0 * ldy * es, ldy, workspace, stream);
-      if (e != hipSuccess) return BCQ_ERR_HIP;
-    }
-    return BCQ_OK;
-  }
+  if (store->scale_dtype == BCQ_F16 && b >= kMfMinBatch)
+    return run_mfma_batches(store, p, nullptr, Xc, b, ldx, Yc, ldy, workspace, bcq::kMfMaxBatch,
+                            stream);
   int32_t ps[BCQ_MAX_BATCH];
   for (int32_t r = 0; r < b; ++r) ps[r] = p;
-  // fp16 batches of 5..15 decode each weight once for all requests; below
-  // that the per-request table lookups cost less than the decode (measured on
-  // gfx950 at 4096 and 14336 rows)
-  if (store->scale_dtype == BCQ_F16 && b >= kDqMinBatch)
-    return run_dq_batches(store, ps, Xc, b, ldx, Yc, ldy, stream);
   return run_table_batches(store, ps, Xc, b, ldx, Yc, ldy, stream);
 }
 
 bcq_status bcq_gemv_mixed_p(const bcq_store *store, const int32_t *p_host, const void *X,
                             int32_t b, int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,
-                            bcq_dtype y_dtype, hipStream_t stream) {
+                            bcq_dtype y_dtype, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
   BCQ_TRY(check_store(store));
   BCQ_TRY(check_dtypes(store, x_dtype, y_dtype));
   BCQ_TRY(check_batch(store, X, b, ldx, Y, ldy));
   if (p_host == nullptr) return BCQ_ERR_INVALID_ARG;
   for (int32_t r = 0; r < b; ++r) BCQ_TRY(check_precision(store, p_host[r]));
-  return run_table_batches(store, p_host, static_cast<const char *>(X), b, ldx,
-                           static_cast<char *>(Y), ldy, stream);
+  BCQ_TRY(check_workspace(store, b, workspace, workspace_bytes));
+  const char *Xc = static_cast<const char *>(X);
+  char *Yc = static_cast<char *>(Y);
+  // one decode of the largest precision serves every request when all of
+  // them read the same tables (the shared-store layout: alpha[p] and zero[p]
+  // alias those of the largest p); otherwise each request's tables are staged
+  // separately by the table kernel
+  int32_t pmax = 0;
+  for (int32_t r = 0; r < b; ++r) pmax = p_host[r] > pmax ? p_host[r] : pmax;
+  bool shared = true;
+  for (int32_t r = 0; r < b; ++r)
+    shared = shared && store->alpha[p_host[r]] == store->alpha[pmax] &&
+             store->zero[p_host[r]] == store->zero[pmax];
+  if (store->scale_dtype == BCQ_F16 && b >= kMfMinBatch && shared)
+    return run_mfma_batches(store, pmax, p_host, Xc, b, ldx, Yc, ldy, workspace,
+                            bcq::kMfMaxMixed, stream);
+  return run_table_batches(store, p_host, Xc, b, ldx, Yc, ldy, stream);
 }
 
 const char *bcq_status_string(bcq_status status) {

@@ -34,18 +34,6 @@ struct ReqTables {
 // of plane slots; the offsets go in the slot after them.
 constexpr int sk_zero_slot(int pmax) { return 2 * ((pmax + 1) / 2); }
 
-// Requests of one launch of the fp16 decode kernel.  All requests read one
-// scale chain (alpha [P][M][G], zero [M][G]); request q takes the weight
-// decoded from the first p[q] planes of it.  A launch holds up to kDqMaxReq
-// requests of one precision, or up to kDqMaxMixedReq of several.
-constexpr int kDqMaxReq = 16;
-constexpr int kDqMaxMixedReq = 8;
-struct DqRequests {
-  int row[kDqMaxReq];           // row of X and of Y holding request q
-  uint32_t at[BCQ_MAX_PLANES];  // bit q of at[i] set: request q has precision i + 1
-  int n;                        // requests in use, 1..kDqMaxReq
-};
-
 // ---- launchers (return hipGetLastError() after the launch) ----
 hipError_t launch_pack(const uint32_t *signs, int P, int M, int K, uint32_t *packed,
                        hipStream_t s);
@@ -63,20 +51,18 @@ hipError_t launch_skinny_lut(const uint32_t *bits, int M, int K, int p_max, cons
                              int nreq, const void *x, int ldx, void *y, int ldy, bcq_dtype dt,
                              hipStream_t s);
 
-// Batched fp16 products with 2..16 requests per launch: weights decoded once
-// per launch on the vector ALUs and reused by every request.
-hipError_t launch_skinny_dq(const uint32_t *bits, int M, int K, const void *alpha,
-                            const void *zero, const DqRequests &rq, const void *x, int ldx,
-                            void *y, int ldy, hipStream_t s);
-
-// Batched products with >= 16 requests at one precision: fp16 dequantised
-// tiles on the matrix cores.  fp16 only, b <= kMfMaxBatch per launch (a call
-// with more runs several launches in order); ws holds at least
-// mfma_workspace_bytes(M, K, b) bytes for the call's whole batch b.
+// Batched fp16 products on the matrix cores (weights decoded to fp16 tiles).
+// p planes are decoded with the tables alpha ([p][M][G]) and zero; request q
+// uses the first p_req[q] of them (p_req: host array of b values in 1..p, or
+// nullptr for all p).  Per-request precisions need b <= kMfMaxMixed; otherwise
+// b <= kMfMaxBatch per launch (a call with more runs several launches in
+// order).  ws holds at least mfma_workspace_bytes(M, K, b) bytes for the call's
+// whole batch b.
 constexpr int kMfMaxBatch = 64;
+constexpr int kMfMaxMixed = 32;
 hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const void *alpha,
                             const void *zero, const void *x, int ldx, int b, void *y, int ldy,
-                            void *ws, hipStream_t s);
+                            void *ws, const int32_t *p_req, hipStream_t s);
 size_t mfma_workspace_bytes(int M, int K, int b);
 
 }  // namespace bcq

@@ -7,7 +7,18 @@
 // matrix cores; the BiLoCo summary's speed results make the same point for
 // its +-1 correction, whose add/subtract work grows with batch while the
 // weight read stays flat.  A weight is decoded once per launch whatever the
-// batch (decode.h has the bit arithmetic).
+// batch.
+//
+// Decode.  A BCQ weight is w = z + sum_{i<p} alpha_i s_i with s_i = +-1 the
+// plane's sign bit (AnyBCQ paper notes, "Method / key designs").  Weights are
+// formed as fp16 pairs (columns 2t, 2t+1) of one 32-column packed sign word,
+// which holds even columns in its low half and odd columns in its high half
+// (pack.hip), so the pair's sign bits are bits t and t+16 and one shift moves
+// both to the fp16 sign positions (bits 15 and 31):
+//   m     = word' << (15 - t)                      one shift
+//   +-a   = (m & 0x80008000) | |alpha| in both     one bit-field insert
+// where word' is the sign word inverted, or not when alpha < 0, so that a set
+// bit yields +alpha.
 //
 // Operand layout.  A wavefront owns one 16-row tile and walks K in steps of
 // four groups.  Lane (r, h) takes row r of group h of the step: one 16-byte
@@ -24,7 +35,10 @@
 //  * Per plane (up to 32 requests): A = the plane's +-alpha pair per column,
 //    one shift and one bit-field insert per pair, and one MFMA per plane plus
 //    one with A = (z, z) for the offset; the matrix cores do the sum over
-//    planes.  Two VALU operations per pair and plane.
+//    planes.  Two VALU operations per pair and plane.  Each plane has its own
+//    accumulator, so requests of one launch may use different precisions
+//    (AnyBCQ notes, per-request precision): request r adds the accumulators of
+//    its first p_r planes only, all planes having been read once.
 //  * Summed (48 and 64 requests): the weight z + sum +-alpha is formed on the
 //    vector ALUs (a third operation, a packed add, per pair and plane) and
 //    one MFMA per request tile contracts it, since with four request tiles
@@ -46,12 +60,14 @@
 // caches needs either an L2 write-back per workgroup or write-through stores
 // and coherent reads, while the second launch of a captured graph costs
 // little.)
-#include "decode.h"
+#include "bcq_internal.h"
 
 namespace bcq {
 namespace {
 
 using half_t = _Float16;
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 // 16-byte blocks as a native vector (HIP's uint4 struct is copied with memcpy,
@@ -98,6 +114,11 @@ struct MfW {
 template <bool SUM, int P>
 constexpr int mf_accs() { return SUM ? 4 : P + 1; }
 
+// Precision of each request of a launch (1..P planes), passed by value.
+struct MfPrec {
+  uint8_t p[kMfMaxBatch];
+};
+
 // NT tiles of 16 requests, P planes.  Loads clamp rows past M, tiles past MT,
 // requests past b and groups past G to in-range addresses; the activations of
 // a group past G are staged as zeros, so it adds nothing (its clamped weights
@@ -108,7 +129,8 @@ template <int NT, int P, bool SUM, int W>
 __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
     const u32x4 *__restrict__ bits, const half_t *__restrict__ alpha,
     const half_t *__restrict__ zero, const half_t *__restrict__ X, int ldx, int b,
-    half_t *__restrict__ Y, int ldy, float *__restrict__ ws, int M, int G, int MT, int sps) {
+    half_t *__restrict__ Y, int ldy, float *__restrict__ ws, int M, int G, int MT, int sps,
+    const MfPrec prec) {
   constexpr int NB = 16 * NT;
   constexpr int NA = mf_accs<SUM, P>();
   using St = MfStage<NB, W>;
@@ -192,14 +214,14 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
       for (int nt = 0; nt < NT; ++nt)
         bop[nt] = __builtin_bit_cast(half8, xb[mf_slot(nt * 16 + r, h, n)]);
       if constexpr (SUM) {
-        dq_half2 w[4];
+        half2v w[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) w[v] = dq_as_h2(z2);
+        for (int v = 0; v < 4; ++v) w[v] = as_h2(z2);
 #pragma unroll
         for (int i = 0; i < P; ++i)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            w[v] += dq_as_h2(((wp[i][q] << (15 - (4 * u + v))) & 0x80008000u) | mag[i]);
+            w[v] += as_h2(((wp[i][q] << (15 - (4 * u + v))) & 0x80008000u) | mag[i]);
         half8 a;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -272,11 +294,18 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
   if (t < MT) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      floatx4 d = acc[nt][0];
-#pragma unroll
-      for (int k = 1; k < NA; ++k) d += acc[nt][k];
       const int n = nt * 16 + r;
       if (n >= b) continue;
+      floatx4 d;
+      if constexpr (SUM) {  // one precision per launch
+        d = (acc[nt][0] + acc[nt][1]) + (acc[nt][2] + acc[nt][3]);
+      } else {  // the offset, then the planes this request uses
+        const int pn = prec.p[n];
+        d = acc[nt][P];
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+          if (i < pn) d += acc[nt][i];
+      }
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int mm = t * kTileRows + 4 * h + v;
@@ -351,19 +380,24 @@ size_t launch_workspace_bytes(int M, int K, int n) {
 }  // namespace
 
 size_t mfma_workspace_bytes(int M, int K, int b) {
-  // the launches of one call run in order and reuse the workspace
-  size_t need = launch_workspace_bytes(M, K, b < kMfMaxBatch ? b : kMfMaxBatch);
-  const int rest = b % kMfMaxBatch;
-  if (b > kMfMaxBatch && rest > 0) {
-    const size_t r = launch_workspace_bytes(M, K, rest);
-    need = r > need ? r : need;
+  // the launches of one call run in order and reuse the workspace; a call
+  // splits b into launches of kMfMaxBatch requests (one precision) or of
+  // kMfMaxMixed (per-request precisions), the last launch taking the rest
+  size_t need = 0;
+  for (int chunk : {kMfMaxBatch, kMfMaxMixed}) {
+    const int sizes[2] = {b < chunk ? b : chunk, b > chunk ? b % chunk : 0};
+    for (int n : sizes) {
+      if (n == 0) continue;
+      const size_t r = launch_workspace_bytes(M, K, n);
+      need = r > need ? r : need;
+    }
   }
   return need;
 }
 
 hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const void *alpha,
                             const void *zero, const void *x, int ldx, int b, void *y, int ldy,
-                            void *ws, hipStream_t s) {
+                            void *ws, const int32_t *p_req, hipStream_t s) {
   const int G = K / kGroup;
   const int MT = row_tiles(M);
   const int NT = (b + 15) / 16;
@@ -377,9 +411,12 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
   half_t *Y = static_cast<half_t *>(y);
   float *w = S > 1 ? static_cast<float *>(ws) : nullptr;
   dim3 grid((MT + W - 1) / W, S), block(64 * W);
+  MfPrec prec;
+  for (int q = 0; q < kMfMaxBatch; ++q)
+    prec.p[q] = (uint8_t)(p_req != nullptr && q < b ? p_req[q] : p);
 #define BCQ_MF(NTV, PV)                                                                  \
   hipLaunchKernelGGL((gemm_mfma_kernel<NTV, PV, (NTV >= 3), mf_waves(NTV)>), grid, block, 0, \
-                     s, b4, a, z, X, ldx, b, Y, ldy, w, M, G, MT, sps)
+                     s, b4, a, z, X, ldx, b, Y, ldy, w, M, G, MT, sps, prec)
 #define BCQ_MF_NT(NTV)              \
   switch (p) {                      \
     case 1: BCQ_MF(NTV, 1); break;  \

@@ -11,7 +11,7 @@
 // bit b holds column 2b for b < 16 and column 2(b - 16) + 1 for b >= 16.  So
 // bits b and b + 16 are the adjacent columns (2b, 2b + 1): one shift moves
 // both to the two fp16 sign positions of a register, next to the natural fp16
-// pair of activations they multiply (see gemv_dq.hip).
+// pair of activations they multiply (gemm_mfma.hip decodes weights this way).
 #include "bcq_internal.h"
 
 namespace bcq {

@@ -126,18 +126,18 @@ bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype 
  * X: [b][ldx] (row r starts at X + r*ldx elements), 16-byte aligned, so ldx*size
  * must be a multiple of 16 bytes; ldx >= K.  Y: [b][ldy], ldy >= M, element
  * aligned.  1 <= b <= BCQ_MAX_BATCH.
- * Batch 1 runs the batch-1 kernel.  fp32 batches, and fp16 batches of 2..4,
- * run on the vector ALUs with sign-combination tables shared by up to 8
- * requests per launch.  fp16 batches of 5..15 decode each weight once per
- * launch of up to 16 requests into fp16 and take one fp16 dot product per
- * weight pair per request on the vector ALUs (the decoded weight is rounded to
- * fp16).  fp16 batches of 16 and more dequantise tiles of W to fp16 and
- * contract them on the matrix cores; that path splits K over workgroups and needs
- * bcq_workspace_bytes(store, b) bytes of device workspace (4-byte aligned) for
- * the K slices' partial sums: contents need no initialisation and are
- * clobbered by the call, so calls that may run at the same time need separate
- * workspaces.  workspace may be NULL when that size is 0; a smaller workspace
- * gives BCQ_ERR_INVALID_ARG.
+ * Batch 1 runs the batch-1 kernel.  fp32 batches, and fp16 batches of 2, run on
+ * the vector ALUs with sign-combination tables shared by up to 8 requests per
+ * launch (exact fp32 sums of the stored values).  fp16 batches of 3 and more
+ * decode tiles of W to fp16 once per launch of up to 64 requests and contract
+ * them with X on the matrix cores (fp32 accumulation; up to 32 requests each
+ * plane's +-alpha is an exact fp16 operand, from 48 the decoded weight
+ * z + sum +-alpha is rounded to fp16).  That path splits K over workgroups and
+ * needs bcq_workspace_bytes(store, b) bytes of device workspace (4-byte
+ * aligned) for the K slices' partial sums: contents need no initialisation
+ * and are clobbered by the call, so calls that may run at the same time need
+ * separate workspaces.  workspace may be NULL when that size is 0; a smaller
+ * workspace gives BCQ_ERR_INVALID_ARG.
  */
 bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int32_t b,
                            int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,
@@ -145,24 +145,31 @@ bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int
                            hipStream_t stream);
 
 /*
- * Device workspace bcq_gemm_skinny needs for a batch of b (0 when none), or 0
- * for an invalid store.
+ * Device workspace bcq_gemm_skinny and bcq_gemv_mixed_p need for a batch of b
+ * (0 when none), or 0 for an invalid store.
  */
 size_t bcq_workspace_bytes(const bcq_store *store, int32_t b);
 
 /*
  * Per-request precision: Y[r] = BCQ product of X[r] at precision p_host[r],
- * using alpha[p_host[r]] and zero[p_host[r]].  Requests run in launches of up
- * to 8; each launch reads every plane up to its largest requested precision
- * once for all its requests (planes past a request's own precision get a zero
- * scale for it), so mixing precisions costs no extra plane traffic.
+ * using alpha[p_host[r]] and zero[p_host[r]].  Every plane up to the largest
+ * requested precision is read once per launch for all its requests, so mixing
+ * precisions costs no extra plane traffic.  When every requested precision's
+ * tables alias those of the largest one (one shared [P][M][G] scale array and
+ * one offset array, as a shared store lays them out), fp16 batches of 3 and
+ * more run on the matrix cores in launches of up to 32: each plane has its own
+ * accumulator and request r sums its first p_host[r] planes.  Otherwise the
+ * table kernel runs launches of up to 8, giving each request zero scales for
+ * planes past its precision.
  * p_host: [b] in HOST memory; every entry must lie in [1, planes], otherwise
  * BCQ_ERR_INVALID_ARG and nothing is enqueued.  1 <= b <= BCQ_MAX_BATCH.
- * X, Y, ldx, ldy as in bcq_gemm_skinny.
+ * X, Y, ldx, ldy, workspace and workspace_bytes as in bcq_gemm_skinny (the
+ * workspace size is bcq_workspace_bytes(store, b) here too).
  */
 bcq_status bcq_gemv_mixed_p(const bcq_store *store, const int32_t *p_host, const void *X,
                             int32_t b, int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,
-                            bcq_dtype y_dtype, hipStream_t stream);
+                            bcq_dtype y_dtype, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /* Static text for a status code (never null). */
 const char *bcq_status_string(bcq_status status);

@@ -75,12 +75,12 @@ def skinny(st, p=2, X=FAKE, b=4, ldx=None, Y=FAKE, ldy=None, dt=bcq.BCQ_F16, ws=
                                       None)
 
 
-def mixed(st, ps, X=FAKE, ldx=None, Y=FAKE, ldy=None, dt=bcq.BCQ_F16):
+def mixed(st, ps, X=FAKE, ldx=None, Y=FAKE, ldy=None, dt=bcq.BCQ_F16, ws=None, wsb=0):
     ldx = st.K if ldx is None else ldx
     ldy = st.M if ldy is None else ldy
     arr = (ctypes.c_int32 * len(ps))(*ps)
     return bcq.load().bcq_gemv_mixed_p(ctypes.byref(st), arr, X, len(ps), ldx, dt, Y, ldy, dt,
-                                       None)
+                                       ws, wsb, None)
 
 
 E_ARG, E_UNS, E_ALN = bcq.BCQ_ERR_INVALID_ARG, bcq.BCQ_ERR_UNSUPPORTED, bcq.BCQ_ERR_ALIGNMENT
@@ -116,6 +116,8 @@ E_ARG, E_UNS, E_ALN = bcq.BCQ_ERR_INVALID_ARG, bcq.BCQ_ERR_UNSUPPORTED, bcq.BCQ_
     (lambda: skinny(make_store(), p=5), E_ARG),
     (lambda: skinny(make_store(M=4096, K=4096), b=16), E_ARG),  # needs a workspace
     (lambda: skinny(make_store(M=4096, K=4096), b=16, ws=FAKE, wsb=16), E_ARG),
+    (lambda: skinny(make_store(M=4096, K=4096), b=3), E_ARG),  # fp16 b >= 3: matrix cores
+    (lambda: mixed(make_store(M=4096, K=4096), [2, 3, 4]), E_ARG),  # needs a workspace too
     (lambda: mixed(make_store(), [2, 3, 0, 4]), E_ARG),
     (lambda: mixed(make_store(), [2, 3, 5, 4]), E_ARG),
     (lambda: mixed(make_store(planes=3), [2, 3, 4]), E_ARG),
@@ -129,7 +131,7 @@ def test_validation_rejects_before_launch(case, expect):
 def test_null_precision_array_rejected():
     st = make_store()
     r = bcq.load().bcq_gemv_mixed_p(ctypes.byref(st), None, FAKE, 2, st.K, bcq.BCQ_F16, FAKE,
-                                    st.M, bcq.BCQ_F16, None)
+                                    st.M, bcq.BCQ_F16, None, 0, None)
     assert r == E_ARG
 
 
@@ -145,8 +147,10 @@ def test_pack_validation():
 def test_workspace_sizes():
     lib = bcq.load()
     st = make_store(M=4096, K=4096)
+    # batch 1 and fp16 batch 2 use the table kernels; from 3 the matrix cores
     assert lib.bcq_workspace_bytes(ctypes.byref(st), 1) == 0
-    assert lib.bcq_workspace_bytes(ctypes.byref(st), 8) == 0
+    assert lib.bcq_workspace_bytes(ctypes.byref(st), 2) == 0
+    assert lib.bcq_workspace_bytes(ctypes.byref(st), 3) > 0
     # split-K partials: one fp32 value per (K slice, request, row), at most
     # one slice per 4-group step (K = 4096: 8 steps)
     need16 = lib.bcq_workspace_bytes(ctypes.byref(st), 16)

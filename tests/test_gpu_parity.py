@@ -317,6 +317,23 @@ def test_mixed_precision_independent_tables(b):
         assert rel_l2(Y[r].cpu().numpy(), ref[r]) <= 1e-5, r
 
 
+@pytest.mark.parametrize("M,K,b", [(96, 640, 3), (200, 1408, 17), (64, 2688, 40), (4096, 4096, 70)])
+def test_mixed_precision_on_matrix_cores(M, K, b):
+    """fp16, shared tables, b >= 3: one decode of the largest precision, each
+    request summing its own planes (launches of up to 32, so b = 40 and 70 run
+    several), every precision 1..4 present."""
+    w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=7 * b + M, p_choices=(1, 2, 3, 4))
+    st = store_of(w)
+    say("mixed mfma", M, K, b, list(w.p_req))
+    Y = torch.empty((b, M), dtype=torch.float16, device="cuda")
+    bcq.bcq_gemv_mixed_p(st, w.p_req, dev(w.x), Y, workspace=bcq.new_workspace(st, b))
+    rows = sample_rows(M, 128)
+    ref = oracle_y(w, w.x, w.p_req, rows)
+    got = Y.cpu().numpy()[:, rows]
+    for r in range(b):
+        assert rel_l2(got[r], ref[r]) <= 2e-3, (r, int(w.p_req[r]))
+
+
 def test_mixed_rejects_bad_entry_and_writes_nothing():
     w = bcq_synth.make(32, 256, 4, b=3, seed=5)
     st = store_of(w)
