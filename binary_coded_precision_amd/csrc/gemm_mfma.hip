@@ -233,15 +233,35 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
           acc[nt][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop[nt], acc[nt][u], 0, 0, 0);
       } else {
 #pragma unroll
-        for (int i = 0; i < P; ++i) {
-          u32x4 av;
+        for (int i = 0; i < P; i += 2) {
+          // planes i and i+1 share one 64-bit shift: the high word's bits
+          // shifted in from the low word land below bit 15, where the mask
+          // drops them
+          u32x4 av, bv;
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            av[v] = ((wp[i][q] << (15 - (4 * u + v))) & 0x80008000u) | mag[i];
-          const half8 a = __builtin_bit_cast(half8, av);
+          for (int v = 0; v < 4; ++v) {
+            int sh = 15 - (4 * u + v);
+            if (i + 1 < P) {
+              // opaque shift count: with it known, the compiler proves the
+              // spilled bits masked and splits the shift back into two
+              asm("" : "+s"(sh));
+              const uint64_t w2 = ((uint64_t)wp[i + 1][q] << 32 | wp[i][q]) << sh;
+              av[v] = ((uint32_t)w2 & 0x80008000u) | mag[i];
+              bv[v] = ((uint32_t)(w2 >> 32) & 0x80008000u) | mag[i + 1];
+            } else {
+              av[v] = ((wp[i][q] << sh) & 0x80008000u) | mag[i];
+            }
+          }
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
-            acc[nt][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop[nt], acc[nt][i], 0, 0, 0);
+            acc[nt][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av),
+                                                                bop[nt], acc[nt][i], 0, 0, 0);
+          if (i + 1 < P) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              acc[nt][i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  __builtin_bit_cast(half8, bv), bop[nt], acc[nt][i + 1], 0, 0, 0);
+          }
         }
         const half8 az = __builtin_bit_cast(half8, u32x4{z2, z2, z2, z2});
 #pragma unroll
@@ -252,41 +272,67 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
   };
 
   // pipeline over the slice's steps, two per iteration: step s computes from
-  // one LDS buffer and its sign words and scales (loaded two steps earlier);
-  // then step s+1's activations (loaded a step earlier) go to the other
-  // buffer, and the loads of step s+2 are issued last.  Every path issues the
-  // same loads (a fetch past the slice's last step re-reads that step, lines
-  // already in flight) and the loop has no exit but its header, so the loads
-  // stay where they are and the waits at the header stay partial.  An odd
-  // last step runs after the loop, from buffer 0.
+  // one LDS buffer and its sign words and scales (loaded two steps earlier).
+  // Every path issues the same loads (a fetch past the slice's last step
+  // re-reads that step, lines already in flight) and the loop has no exit but
+  // its header, so the waits stay partial; no instruction crosses a
+  // sched_barrier, since the scheduler would otherwise start a step's scale
+  // arithmetic, or the staging of the next step's activations, early and wait
+  // there for loads issued just before.  An odd last step runs after the loop,
+  // from buffer 0.
+  //  * Small staging share (up to 32 requests): the activations of step s+2
+  //    are requested as step s starts and staged to LDS after step s+1
+  //    computes, two compute phases later (register sets xa, xb alternate).
+  //  * Large share (48, 64 requests): one register set, requested after step
+  //    s computes and staged after step s+1 -- a second set would not fit the
+  //    registers.
+  constexpr bool kDeepX = St::kTasks <= 4;
   const int s_last = s1 - 1;
   OpsW wa, wb;
-  OpsX xo;
-  fetch_x(s0, xo);
+  OpsX xa, xb;
+  fetch_x(s0, xb);
   fetch_w(s0, wa);
-  write_x(xo, 0);
-  fetch_x(min(s0 + 1, s_last), xo);
+  write_x(xb, 0);
+  fetch_x(min(s0 + 1, s_last), xa);
   fetch_w(min(s0 + 1, s_last), wb);
   __syncthreads();
   int s = s0;
-  for (; s + 1 < s1; s += 2) {
-    // no instruction crosses a sched_barrier: the scheduler would otherwise
-    // start a step's scale arithmetic, or the staging of the next step's
-    // activations, early and wait there for loads issued just before
-    compute(wa, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    write_x(xo, 1);
-    fetch_x(min(s + 2, s_last), xo);
-    fetch_w(min(s + 2, s_last), wa);
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    compute(wb, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    write_x(xo, 0);
-    fetch_x(min(s + 3, s_last), xo);
-    fetch_w(min(s + 3, s_last), wb);
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kDeepX) {
+    for (; s + 1 < s1; s += 2) {
+      fetch_x(min(s + 2, s_last), xb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wa, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      write_x(xa, 1);
+      fetch_w(min(s + 2, s_last), wa);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_x(min(s + 3, s_last), xa);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wb, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      write_x(xb, 0);
+      fetch_w(min(s + 3, s_last), wb);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    for (; s + 1 < s1; s += 2) {
+      compute(wa, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      write_x(xa, 1);
+      fetch_x(min(s + 2, s_last), xa);
+      fetch_w(min(s + 2, s_last), wa);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wb, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      write_x(xa, 0);
+      fetch_x(min(s + 3, s_last), xa);
+      fetch_w(min(s + 3, s_last), wb);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   if (s < s1) compute(wa, 0);
 
