@@ -321,6 +321,8 @@ def main():
     ap.add_argument("--counter-run", type=int, default=0, metavar="N",
                     help="only run N cold eager calls of the batch-1 kernel at each of p=2,3,4 "
                          "on the 4096x4096 store (for per-dispatch HBM counters)")
+    ap.add_argument("--counter-batch", type=int, default=1, metavar="B",
+                    help="with --counter-run: run bcq_gemm_skinny at batch B (p = 4) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build's path runs on a single MI355X "
@@ -347,15 +349,21 @@ def main():
         return
 
     if args.counter_run:
-        w = bcq_synth.config(2)
-        rot = Rotation(w, ROTATE_BYTES, bcq, torch)
-        ys = [torch.empty(w.M, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
-        for p in (2, 3, 4):
+        b = args.counter_batch
+        w = bcq_synth.make(4096, 4096, 4, b=b, seed=2) if b > 1 else bcq_synth.config(2)
+        rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
+        ys = [torch.empty((b, w.M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+        ws = bcq.new_workspace(rot.stores[0], b) if b > 1 else None
+        for p in ((2, 3, 4) if b == 1 else (4,)):
             for i in range(args.counter_run):
                 c = i % rot.n
-                bcq.bcq_gemv(rot.stores[c], p, rot.x[c][0], ys[c])
+                if b == 1:
+                    bcq.bcq_gemv(rot.stores[c], p, rot.x[c][0], ys[c][0])
+                else:
+                    bcq.bcq_gemm_skinny(rot.stores[c], p, rot.x[c], ys[c], workspace=ws)
         torch.cuda.synchronize()
-        print(json.dumps({"counter_run_calls_per_p": args.counter_run, "copies": rot.n}))
+        print(json.dumps({"counter_run_calls_per_p": args.counter_run, "batch": b,
+                          "copies": rot.n}))
         return
 
     print("[bench] headline", file=sys.stderr, flush=True)
