@@ -18,18 +18,18 @@
 //  * Scales fuse at the group boundary: acc += alpha_i * P_i after the 32
 //    lookups of a group, and acc += z * S_j with S_j the group's activation sum
 //    (asymmetric BCQ offset, AnyBCQ paper notes, "Training strategy").
-//  * Lane mapping.  A workgroup owns a tile of 16 rows and all of K.  Lane
-//    (r, ks) of the 256 handles row r and one group per window of 16 groups, so
-//    a wavefront (16 rows x 4 groups) loads 1 KiB of contiguous packed bits per
-//    plane and per window (see pack.hip).  Every load of the workgroup is
-//    issued before the first table is built, so a workgroup keeps up to
-//    p * 16 B * windows per lane in flight.
+//  * Batch 1 (gemv_res_kernel, gemv_stream_kernel): a 512-lane workgroup owns
+//    16-row tiles; lane (r, hs) takes row r and half-group slot hs of a
+//    16-group window of tables (64 columns, two packed words per plane).
+//    K <= 4096 keeps the tables of all of K resident while the workgroup walks
+//    several tiles; larger K streams windows of tables through two buffers.
 //  * LDS banks.  Table c sits at 80-byte stride (16 entries + 16 B pad) so that
-//    the 16-byte writes of 16 consecutive chunks cover distinct banks, and
-//    groups sit at a stride that rotates the bank set by 16 so the four groups
-//    read by one wavefront use disjoint banks.
-//  * The reduction over the 16 K-sub lanes of a row is a fixed-order shuffle
-//    + LDS sum, so results are deterministic.
+//    the 16-byte writes of 16 consecutive chunks cover distinct banks, and the
+//    four slots of a wavefront read disjoint quarters of the 64 banks.
+//  * Batches of 2..8 (skinny_lut_kernel): tables hold several requests'
+//    sums per entry, see the section below.
+//  * Every reduction over lanes and wavefronts runs in a fixed order, so
+//    results are deterministic.
 #include "bcq_internal.h"
 
 namespace bcq {
@@ -175,162 +175,13 @@ __device__ __forceinline__ float sum8_lanes(float v) {
 
 // ---------------------------------------------------------------- batch 1
 
-constexpr int kG1Threads = 256;
-constexpr int kG1Ksub = 16;                                   // groups per window
-constexpr int kG1ChunkStride = 80;                            // bytes
-constexpr int kG1GroupStride = kChunksPerGroup * kG1ChunkStride + 64;  // 2624
-constexpr int kG1WindowBytes = kG1Ksub * kG1GroupStride;      // 41984
-
-// Sum over the 32 chunks of one group of T_c[nibble c of the row's 128 bits].
-// base is the LDS byte offset of the group's first table.
-__device__ __forceinline__ float g1_plane_sum(const uint4 bw, uint32_t base) {
-  constexpr int S = kG1ChunkStride / 4;  // chunk stride in floats
-  const uint32_t wd[4] = {bw.x, bw.y, bw.z, bw.w};
-  float s[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    // nibble n times 4 (the entry's byte offset), one per byte: even n, then odd n
-    const uint32_t ev = (wd[q] << 2) & 0x3C3C3C3Cu;
-    const uint32_t od = (wd[q] >> 2) & 0x3C3C3C3Cu;
-    const int c = q * 8;
-    const float t0 = lds_at<0>(base, ev)[(c + 0) * S] + lds_at<0>(base, od)[(c + 1) * S];
-    const float t1 = lds_at<1>(base, ev)[(c + 2) * S] + lds_at<1>(base, od)[(c + 3) * S];
-    const float t2 = lds_at<2>(base, ev)[(c + 4) * S] + lds_at<2>(base, od)[(c + 5) * S];
-    const float t3 = lds_at<3>(base, ev)[(c + 6) * S] + lds_at<3>(base, od)[(c + 7) * S];
-    if (q == 0) {
-      s[0] = t0;
-      s[1] = t1;
-      s[2] = t2;
-      s[3] = t3;
-    } else {
-      s[0] += t0;
-      s[1] += t1;
-      s[2] += t2;
-      s[3] += t3;
-    }
-  }
-  return (s[0] + s[1]) + (s[2] + s[3]);
-}
-
-// The load phase has no branches at all: the precision P is a template
-// argument, and lanes or windows past the end read clamped in-range addresses
-// whose values are never used.  LOOP = false: the whole of K fits one batch of
-// WMAX windows and the body runs once, so no register is loop-carried.  With
-// both, the compiler keeps every load of a batch in flight and waits only at
-// first use.
-template <typename T, int WMAX, bool LOOP, int P>
-__global__ __launch_bounds__(kG1Threads) void gemv_lut_kernel(
-    const uint4 *__restrict__ bits, const T *__restrict__ alpha, const T *__restrict__ zero,
-    const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT) {
-  __shared__ __attribute__((aligned(16))) char lut[kG1WindowBytes];
-  __shared__ float gsum[kG1Ksub];
-  __shared__ float part[kG1Threads / 64][kTileRows];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int r = lane & 15;
-  const int ks = wave * 4 + (lane >> 4);
-  const int tile = blockIdx.x;
-  const int m = tile * kTileRows + r;
-  const int m_safe = min(m, M - 1);  // padding rows read row M-1's scales, never stored
-  const int nwin = (G + kG1Ksub - 1) / kG1Ksub;
-  const size_t plane_stride = (size_t)MT * G * kTileRows;  // in uint4
-  const uint4 *tbits = bits + (size_t)tile * G * kTileRows + r;
-  const size_t MG = (size_t)M * G;
-
-  float acc = 0.f;
-
-  for (int w0 = 0; w0 < (LOOP ? nwin : 1); w0 += WMAX) {
-    // ---- issue every load of this batch of windows: x for the tables first,
-    // then per window the sign words, scales and offsets.
-    typename Act<T>::raw xr[WMAX][2];
-    uint4 bw[WMAX][P];
-    uint32_t al[WMAX][P];
-    uint32_t zz[WMAX];
-#pragma unroll
-    for (int u = 0; u < WMAX; ++u) {
-      const int w = min(w0 + u, nwin - 1);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = tid + h * kG1Threads;
-        const int j = min(w * kG1Ksub + c / kChunksPerGroup, G - 1);
-        xr[u][h] = Act<T>::load(x + (size_t)j * kGroup + chunk_base(c % kChunksPerGroup),
-                                chunk_parity(c % kChunksPerGroup));
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < WMAX; ++u) {
-      const int w = min(w0 + u, nwin - 1);
-      const int js = min(w * kG1Ksub + ks, G - 1);
-#pragma unroll
-      for (int i = 0; i < P; ++i) {
-        bw[u][i] = tbits[i * plane_stride + (size_t)js * kTileRows];
-        al[u][i] = load_raw(alpha + i * MG + (size_t)m_safe * G + js);
-      }
-      zz[u] = load_raw(zero + (size_t)m_safe * G + js);
-    }
-
-#pragma unroll
-    for (int u = 0; u < WMAX; ++u) {
-      const int w = w0 + u;
-      if (w >= nwin) break;  // uniform over the workgroup
-      __syncthreads();       // the previous window's lookups are done with lut[]
-      // ---- build the window's tables (chunk c = tid and tid + 256)
-      float cs[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = tid + h * kG1Threads;
-        float f[4];
-        Act<T>::cvt(xr[u][h], chunk_parity(c % kChunksPerGroup), f);
-        float4 v[4];
-        chunk_entries(f, v);
-        float4 *dst = reinterpret_cast<float4 *>(lut + (c / kChunksPerGroup) * kG1GroupStride +
-                                                 (c % kChunksPerGroup) * kG1ChunkStride);
-        dst[0] = v[0];
-        dst[1] = v[1];
-        dst[2] = v[2];
-        dst[3] = v[3];
-        cs[h] = (f[0] + f[1]) + (f[2] + f[3]);
-      }
-      // group sums: the 32 chunks of a group are 32 consecutive lanes
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) {
-        cs[0] += __shfl_xor(cs[0], off);
-        cs[1] += __shfl_xor(cs[1], off);
-      }
-      if ((tid & 31) == 0) {
-        gsum[tid / 32] = cs[0];
-        gsum[tid / 32 + 8] = cs[1];
-      }
-      __syncthreads();
-      // ---- lookups for this lane's group
-      const int j = w * kG1Ksub + ks;
-      if (j < G) {
-        const uint32_t base = lds_addr(lut + ks * kG1GroupStride);
-#pragma unroll
-        for (int i = 0; i < P; ++i)
-          acc = fmaf(raw_to_float<T>(al[u][i]), g1_plane_sum(bw[u][i], base), acc);
-        acc = fmaf(raw_to_float<T>(zz[u]), gsum[ks], acc);
-      }
-    }
-  }
-
-  // ---- reduce the 16 K-sub partials of each row in a fixed order
-  acc += __shfl_xor(acc, 16);
-  acc += __shfl_xor(acc, 32);
-  if (lane < 16) part[wave][lane] = acc;
-  __syncthreads();
-  if (tid < kTileRows) {
-    const float s = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
-    const int mm = tile * kTileRows + tid;
-    if (mm < M) y[mm] = (T)s;
-  }
-}
+constexpr int kG1Ksub = 16;         // groups per window of tables
+constexpr int kG1ChunkStride = 80;  // bytes per chunk table: 16 entries + 16 B pad
 
 // ------------------------------------------------ batch 1, whole-K tables
 //
-// For K <= 6144 the tables of all of K fit in LDS (NW windows of 16 groups).
+// For K <= 4096 the tables of all of K stay resident in LDS (NW <= 2 windows of
+// 16 groups).
 // A workgroup of 512 lanes (two wavefronts per SIMD, so one hides the other's
 // LDS latency) builds them once, then walks its row tiles (tile blockIdx.x +
 // k * gridDim.x), loading the next tile's sign words, scales and offsets while
@@ -545,6 +396,154 @@ __global__ __launch_bounds__(kRThreads) void gemv_res_kernel(
   }
 }
 
+// ------------------------------------------------ batch 1, K past the resident tables
+//
+// For K > 4096 the tables of all of K do not fit in LDS, so a workgroup (one
+// 16-row tile, 512 lanes, the lane mapping of gemv_res_kernel) streams K in
+// windows of 16 groups with two table buffers and one barrier per window:
+// after the barrier it builds window w+1's tables (one chunk per lane) and
+// stages its scales into the other buffer, then looks up window w.  Sign
+// words, activations and scales of window w+kStreamRing are requested when
+// window w is done with its ring slot, so kStreamRing windows of loads are in
+// flight; every path issues the same loads (a window past the end re-reads the
+// last one) and the loop's only exit is its header, so the waits stay
+// partial.  Before the first build only the activations and scales of the
+// first two windows and the first window's sign words are requested; queued
+// behind all four windows' sign words of every workgroup, the loads the first
+// build waits for arrived late (measured: the first window took 7 us).
+// Scales are staged through LDS with row-contiguous loads, as in
+// gemv_res_kernel.  A group's activation sum is kept as four 8-chunk partials
+// (DPP within 8 lanes, no LDS round trips) that the lookup adds in order.
+constexpr int kStreamRing = 4;  // windows of loads in flight
+
+template <typename T, int P>
+struct StreamSlot {
+  uint2 bits[P];                   // this lane's half-group, one uint2 per plane
+  typename Act<T>::raw x;          // the activations of the chunk this lane builds
+  uint32_t sc[4];                  // four scales or offsets this lane stages
+};
+
+template <typename T, int P>
+__global__ __launch_bounds__(kRThreads) void gemv_stream_kernel(
+    const uint4 *__restrict__ bits, const T *__restrict__ alpha, const T *__restrict__ zero,
+    const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT) {
+  __shared__ __attribute__((aligned(16))) char lut[2][kRWindowBytes];
+  __shared__ float gsum[2][kG1Ksub][4];
+  // staged scales: [buffer][plane, then offsets][row][group of the window],
+  // rows padded to 17 words so 16 rows x 2 groups hit distinct banks
+  __shared__ uint32_t scl[2][P + 1][kTileRows][kG1Ksub + 1];
+  __shared__ float part[kRWaves][kTileRows];
+  using Slot = StreamSlot<T, P>;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int hs = wave * 4 + (lane >> 4);  // half-group slot 0..31 of the window
+  const int gw = hs >> 1;                 // group within the window
+  const int half = hs & 1;
+  const int tile = blockIdx.x;
+  const int nwin = (G + kG1Ksub - 1) / kG1Ksub;
+  const size_t plane_stride = (size_t)MT * G * kTileRows;  // in uint4
+  const size_t MG = (size_t)M * G;
+  const uint2 *bits2 = reinterpret_cast<const uint2 *>(bits);
+  // staging task of this lane: array sa (planes, then offsets), row srow, groups 4*sq..+3
+  const bool stager = tid < (P + 1) * kTileRows * 4;
+  const int sa = min(tid / (kTileRows * 4), P);
+  const int srow = (tid / 4) % kTileRows;
+  const int sq = tid % 4;
+  const int s_m = min(tile * kTileRows + srow, M - 1);
+  const T *sbase = sa < P ? alpha + sa * MG + (size_t)s_m * G : zero + (size_t)s_m * G;
+
+  auto fetch_bits = [&](int v, Slot &o) __attribute__((always_inline)) {
+    const int w = min(v, nwin - 1);
+    const int js = min(w * kG1Ksub + gw, G - 1);
+    const size_t q = (((size_t)tile * G + js) * kTileRows + r) * 2 + half;  // uint2 index
+#pragma unroll
+    for (int i = 0; i < P; ++i) o.bits[i] = bits2[i * plane_stride * 2 + q];
+  };
+  auto fetch_small = [&](int v, Slot &o) __attribute__((always_inline)) {
+    const int w = min(v, nwin - 1);
+    const int c = tid % kChunksPerGroup;
+    const int jx = min(w * kG1Ksub + tid / kChunksPerGroup, G - 1);
+    o.x = Act<T>::load(x + (size_t)jx * kGroup + chunk_base(c), chunk_parity(c));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o.sc[e] = load_raw(sbase + min(w * kG1Ksub + 4 * sq + e, G - 1));
+  };
+  auto fetch = [&](int v, Slot &o) __attribute__((always_inline)) {
+    fetch_bits(v, o);
+    fetch_small(v, o);
+  };
+  // tables, group sums and scales of the window held in slot o -> buffer buf
+  auto build = [&](const Slot &o, int buf) __attribute__((always_inline)) {
+    const int c = tid % kChunksPerGroup;
+    float f[4];
+    Act<T>::cvt(o.x, chunk_parity(c), f);
+    float4 v[4];
+    chunk_entries(f, v);
+    float4 *dst = reinterpret_cast<float4 *>(lut[buf] + (tid / kChunksPerGroup) * kRGroupStride +
+                                             r_chunk_offset(c));
+    dst[0] = v[0];
+    dst[1] = v[1];
+    dst[2] = v[2];
+    dst[3] = v[3];
+    const float cs = sum8_lanes((f[0] + f[1]) + (f[2] + f[3]));
+    if ((tid & 7) == 0) gsum[buf][tid / kChunksPerGroup][(tid / 8) % 4] = cs;
+    if (stager) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) scl[buf][sa][srow][4 * sq + e] = o.sc[e];
+    }
+  };
+  float acc = 0.f;
+  auto consume = [&](int w, const Slot &o, int buf) __attribute__((always_inline)) {
+    const int j = w * kG1Ksub + gw;
+    if (j < G) {
+      const uint32_t base = lds_addr(lut[buf] + gw * kRGroupStride + r_chunk_offset(16 * half));
+#pragma unroll
+      for (int i = 0; i < P; ++i)
+        acc = fmaf(raw_to_float<T>(scl[buf][i][r][gw]), r_half_sum(o.bits[i], base), acc);
+      if (half == 0) {
+        const float *gs = gsum[buf][gw];
+        acc = fmaf(raw_to_float<T>(scl[buf][P][r][gw]), (gs[0] + gs[1]) + (gs[2] + gs[3]), acc);
+      }
+    }
+  };
+
+  Slot ring[kStreamRing];
+  fetch_small(0, ring[0]);
+  fetch_small(1, ring[1]);
+  fetch_bits(0, ring[0]);
+  build(ring[0], 0);
+  fetch_bits(1, ring[1]);
+#pragma unroll
+  for (int k = 2; k < kStreamRing; ++k) fetch(k, ring[k]);
+  // window w: barrier (window w's tables are built; window w-1's lookups are
+  // done with the other buffer), build w+1 there, look up w, refill w's slot
+  for (int w0 = 0; w0 < nwin; w0 += kStreamRing) {
+#pragma unroll
+    for (int k = 0; k < kStreamRing; ++k) {
+      const int w = w0 + k;
+      __syncthreads();
+      if (w + 1 < nwin) build(ring[(k + 1) % kStreamRing], (w + 1) & 1);  // uniform
+      if (w < nwin) consume(w, ring[k], w & 1);                            // uniform
+      fetch(w + kStreamRing, ring[k]);
+    }
+  }
+
+  // ---- reduce the 32 slot partials of each row in a fixed order
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  if (lane < 16) part[wave][lane] = acc;
+  __syncthreads();
+  if (tid < kTileRows) {
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kRWaves; ++v) sum += part[v][tid];
+    const int mm = tile * kTileRows + tid;
+    if (mm < M) y[mm] = (T)sum;
+  }
+}
+
 int compute_units() {
   static int n = 0;
   if (n == 0) {
@@ -614,25 +613,22 @@ hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *
     gemv_res_tiles<T, 2>(s, b4, a, z, xx, yy, M, G, MT, p);
     return hipGetLastError();
   }
-  // larger K: one tile per workgroup, tables built window by window
-  dim3 grid(MT), block(kG1Threads);
-#define BCQ_G1P(W, L, PP)                                                                 \
-  hipLaunchKernelGGL((gemv_lut_kernel<T, W, L, PP>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT)
-#define BCQ_G1(W, L)            \
-  switch (p) {                  \
-    case 1: BCQ_G1P(W, L, 1); break; \
-    case 2: BCQ_G1P(W, L, 2); break; \
-    case 3: BCQ_G1P(W, L, 3); break; \
-    default: BCQ_G1P(W, L, 4); break; \
+  // larger K: one tile per workgroup, tables streamed window by window
+  dim3 grid(MT), block(kRThreads);
+  switch (p) {
+    case 1:
+      hipLaunchKernelGGL((gemv_stream_kernel<T, 1>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT);
+      break;
+    case 2:
+      hipLaunchKernelGGL((gemv_stream_kernel<T, 2>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT);
+      break;
+    case 3:
+      hipLaunchKernelGGL((gemv_stream_kernel<T, 3>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT);
+      break;
+    default:
+      hipLaunchKernelGGL((gemv_stream_kernel<T, 4>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT);
+      break;
   }
-  if (nwin <= 4)
-    BCQ_G1(4, false)
-  else if (nwin <= 8)
-    BCQ_G1(8, false)
-  else
-    BCQ_G1(8, true)
-#undef BCQ_G1P
-#undef BCQ_G1
   return hipGetLastError();
 }
 
