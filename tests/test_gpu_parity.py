@@ -367,6 +367,32 @@ def test_mfma_batches(M, K, b):
             assert rel_l2(got[r], ref[r]) <= 2e-3, (p, r)
 
 
+@pytest.mark.parametrize("b", [3, 16, 29])
+def test_mfma_ragged_rows_and_groups(b):
+    """A ragged last row tile (M = 3100) and an odd group count (33), so the last
+    K slice holds fewer 4-group steps and the last chunk of row tiles is
+    partial; every precision, then per-request precisions."""
+    M, K = 3100, 4224
+    w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=300 + b, p_choices=(1, 2, 3, 4))
+    st = store_of(w)
+    rows = np.unique(np.concatenate([sample_rows(M, 96), np.arange(M - 20, M)]))
+    for p in (1, 2, 3, 4):
+        say("mfma ragged", M, K, b, p)
+        Y = torch.empty((b, M), dtype=torch.float16, device="cuda")
+        bcq.bcq_gemm_skinny(st, p, dev(w.x), Y)
+        ref = oracle_y(w, w.x, [p] * b, rows)
+        got = Y.cpu().numpy()[:, rows]
+        for r in range(b):
+            assert rel_l2(got[r], ref[r]) <= 2e-3, (p, r)
+    say("mfma ragged mixed", M, K, b, list(w.p_req))
+    Y = torch.empty((b, M), dtype=torch.float16, device="cuda")
+    bcq.bcq_gemv_mixed_p(st, w.p_req, dev(w.x), Y)
+    ref = oracle_y(w, w.x, w.p_req, rows)
+    got = Y.cpu().numpy()[:, rows]
+    for r in range(b):
+        assert rel_l2(got[r], ref[r]) <= 2e-3, (r, int(w.p_req[r]))
+
+
 def test_mfma_workspace_reused_across_batch_sizes():
     # one workspace, sized for the largest batch and never cleared, reused in
     # stream order by calls whose launches use different workgroup sizes and
