@@ -10,7 +10,7 @@ every call reads its planes from HBM.
 Printed: one JSON line with the headline value (GB/s of algorithmic bytes over
 the timed region), a roofline object for the batch-1 kernel (per-launch HIP
 event durations on the launch stream), the float64 CPU oracle timed on a
-bounded sample, and secondary rows (14336x4096 at batch 1, per-request
+bounded sample, and secondary rows (MLP shapes at batch 1, per-request
 precision, small batches, matrix-core batches) for context.
 
 Algorithmic bytes of one call:
@@ -214,21 +214,25 @@ def secondary(args, bcq, torch, bcq_synth):
     rows = {}
     n = max(20, args.steps // 4)
 
-    # 14336x4096 at batch 1, p = 2/3/4 (the large-shape target row)
-    w = bcq_synth.make(14336, 4096, 4, seed=3, name="gateup_14336x4096_b1")
-    rot = Rotation(w, ROTATE_BYTES, bcq, torch)
-    ys = [torch.empty(w.M, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
-    r = {}
-    for p in (2, 3, 4):
-        d = time_calls(torch, lambda i, p=p: bcq.bcq_gemv(rot.stores[i % rot.n], p,
-                                                          rot.x[i % rot.n][0], ys[i % rot.n]),
-                       n, 10)
-        nb = algorithmic_bytes(w.M, w.K, p)
-        r[str(p)] = {"us": round(d * 1e3, 3),
-                     "GBps": round(nb / (d * 1e-3) / 1e9, 1),
-                     "frac_of_peak": round(nb / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    rows["gemv_14336x4096_b1"] = r
-    del rot, ys
+    # MLP shapes at batch 1, p = 2/3/4: 14336x4096 (gate/up projection, the
+    # large-shape target row) and 4096x14336 (down projection, whose K exceeds
+    # what one workgroup keeps resident, so its tables stream through LDS)
+    for M, K, seed in ((14336, 4096, 3), (4096, 14336, 6)):
+        print("[bench] secondary %dx%d b=1" % (M, K), file=sys.stderr, flush=True)
+        w = bcq_synth.make(M, K, 4, seed=seed, name="mlp_%dx%d_b1" % (M, K))
+        rot = Rotation(w, ROTATE_BYTES, bcq, torch)
+        ys = [torch.empty(w.M, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+        r = {}
+        for p in (2, 3, 4):
+            d = time_calls(torch, lambda i, p=p: bcq.bcq_gemv(rot.stores[i % rot.n], p,
+                                                              rot.x[i % rot.n][0], ys[i % rot.n]),
+                           n, 10)
+            nb = algorithmic_bytes(w.M, w.K, p)
+            r[str(p)] = {"us": round(d * 1e3, 3),
+                         "GBps": round(nb / (d * 1e-3) / 1e9, 1),
+                         "frac_of_peak": round(nb / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        rows["gemv_%dx%d_b1" % (M, K)] = r
+        del rot, ys
 
     # 4096x4096 at batch 1 with one store repeated (planes served from the
     # Infinity Cache after the first call): context for the cold numbers
@@ -274,7 +278,7 @@ def secondary(args, bcq, torch, bcq_synth):
         w = bcq_synth.make(M, K, 4, b=b, seed=5)
         rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
         Y = [torch.empty((b, M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
-        ws = bcq.new_workspace(rot.stores[0], b)  # zeroed once; calls leave it zeroed
+        ws = bcq.new_workspace(rot.stores[0], b)  # None where the call needs none
         d = time_calls(torch, lambda i: bcq.bcq_gemm_skinny(rot.stores[i % rot.n], p,
                                                            rot.x[i % rot.n], Y[i % rot.n],
                                                            workspace=ws), n, 10)

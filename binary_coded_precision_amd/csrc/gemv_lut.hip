@@ -182,15 +182,15 @@ constexpr int kG1ChunkStride = 80;  // bytes per chunk table: 16 entries + 16 B 
 //
 // For K <= 4096 the tables of all of K stay resident in LDS (NW <= 2 windows of
 // 16 groups).
-// A workgroup of 512 lanes (two wavefronts per SIMD, so one hides the other's
-// LDS latency) builds them once, then walks its row tiles (tile blockIdx.x +
-// k * gridDim.x), loading the next tile's sign words, scales and offsets while
-// it looks up the current one, and reduces all its tiles at the end.  With
+// A workgroup of 512 lanes per window (at K = 4096 four wavefronts per SIMD,
+// so the others hide one's LDS latency) builds them once, then walks its row
+// tiles (tile blockIdx.x + k * gridDim.x), loading the next tile's sign words
+// while it looks up the current one, and reduces all its tiles at the end.  With
 // grid = min(row tiles, CUs) every CU holds one workgroup that streams several
 // tiles, so table builds are amortised and loads overlap lookups.
 //
-// Lane (r, hs): row r of the tile, half-group slot hs = 0..31 of the window
-// (group hs/2, columns 64*(hs%2) .. +63).  A wavefront's four slots are two
+// Lane (r, hs) of wavefronts 8w..8w+7: row r of the tile, half-group slot
+// hs = 0..31 of window w (group hs/2, columns 64*(hs%2) .. +63).  A wavefront's four slots are two
 // groups x two halves; in LDS the second half of a group sits 16 banks after
 // the first and consecutive groups 32 banks apart, so the four slots read
 // disjoint quarters of the 64 banks.
@@ -236,103 +236,108 @@ __device__ __forceinline__ float r_half_sum(const uint2 bw, uint32_t base) {
   return (s[0] + s[1]) + (s[2] + s[3]);
 }
 
-template <int NW, int P>
-struct G1Tile {
-  uint2 bits[NW][P];
-};
-
 // Scales and offsets of a tile are staged through LDS: in the caller's
 // [p][M][G] layout the 16 rows of a tile are one contiguous run of 16*G
 // values per plane, so consecutive threads load consecutive elements
 // (coalesced), and each lane then reads its own (row, group) values from
 // LDS.  Loading them per lane straight from memory instead touches one
 // cache line per row for every 2-byte value and more than doubles the
-// kernel's time.
-template <typename T, int NW, int P, int TMAX, int AHEAD = 1>
-__global__ __launch_bounds__(kRThreads) void gemv_res_kernel(
+// kernel's time.  Every tile's are staged before the table-build barrier,
+// the (tile, array) loads spread evenly over all lanes; the lookups then run
+// through all tiles with no further barrier.  (Staging later tiles behind a
+// barrier of their own was measured slower at 2 and 4 tiles per workgroup:
+// each barrier idles the SIMDs while the last wavefronts finish.)
+//
+// The workgroup has 512 lanes per window (NW * 8 wavefronts): wavefronts
+// 8w..8w+7 look up window w.  At K = 4096 that is four wavefronts per SIMD,
+// enough to hide the LDS latency of the lookups, and every lane builds one
+// chunk's table.
+template <typename T, int NW, int P, int TMAX>
+__global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
     const uint4 *__restrict__ bits, const T *__restrict__ alpha, const T *__restrict__ zero,
     const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT) {
   constexpr int kMaxG = NW * kG1Ksub;
+  constexpr int kWaves = kRWaves * NW;
+  constexpr int kPos = kTileRows * kMaxG;        // staging positions of one tile
+  constexpr int kParts = kRThreads * NW / kPos;  // thread sets sharing a tile's arrays
+  constexpr int kPairs = TMAX * (P + 1);                 // (tile, array) pairs to stage
+  constexpr int kPerThread = (kPairs + kParts - 1) / kParts;
+  static_assert(kRThreads * NW == kParts * kPos, "staging positions tile the workgroup");
   __shared__ __attribute__((aligned(16))) char lut[NW * kRWindowBytes];
   __shared__ float gsum[NW * kG1Ksub];
-  __shared__ float part[kRWaves][TMAX][kTileRows];
-  // staged scales: [tile][plane P = offsets][row][group]; rows padded to an
+  __shared__ float part[kWaves][TMAX][kTileRows];
+  // staged scales: [buffer][plane P = offsets][row][group]; rows padded to an
   // odd number of words so the 16 rows x 2 groups one wavefront reads hit
   // distinct banks
   __shared__ uint32_t scl[TMAX][P + 1][kTileRows][kMaxG + 1];
-  using Tile = G1Tile<NW, P>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int win = wave / kRWaves;                      // the window this wavefront looks up
   const int r = lane & 15;
-  const int hs = wave * 4 + (lane >> 4);  // half-group slot 0..31
-  const int gw = hs >> 1;                 // group within a window
+  const int hs = (wave % kRWaves) * 4 + (lane >> 4);  // half-group slot 0..31
+  const int gw = hs >> 1;                              // group within the window
   const int half = hs & 1;
   const int nt = (MT - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // my tiles
   const size_t plane_stride = (size_t)MT * G * kTileRows;  // in uint4
   const size_t MG = (size_t)M * G;
   const uint2 *bits2 = reinterpret_cast<const uint2 *>(bits);
 
-  // ---- activations for every window's tables: thread tid builds chunk tid
-  typename Act<T>::raw xr[NW];
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int j = min(w * kG1Ksub + tid / kChunksPerGroup, G - 1);
-    xr[w] = Act<T>::load(x + (size_t)j * kGroup + chunk_base(tid % kChunksPerGroup),
-                         chunk_parity(tid % kChunksPerGroup));
-  }
+  // ---- activations for the tables: thread tid builds chunk tid % 512 of
+  // window tid / 512
+  const int bc = tid % kChunksPerGroup;
+  const int bj = tid / kChunksPerGroup;  // group of K whose chunk this thread builds
+  const typename Act<T>::raw xr = Act<T>::load(
+      x + (size_t)min(bj, G - 1) * kGroup + chunk_base(bc), chunk_parity(bc));
 
-  // ---- scales and offsets first (they are small and the staging below waits
-  // for them).  Thread (row tid / 32, group tid % 32) owns one position of
-  // each tile's 16 x G run per plane: consecutive threads read consecutive
-  // groups of a row, so the loads are coalesced, and no index needs a division.
-  static_assert(kRThreads >= kTileRows * kMaxG, "one staging position per thread");
-  const bool sok = tid < kTileRows * kMaxG;  // threads past the 16 x kMaxG positions idle
-  const int srow = min(tid / kMaxG, kTileRows - 1);
+  // ---- scales and offsets of every tile.  Thread (row, group) =
+  // ((tid % kPos) / kMaxG, tid % kMaxG) owns one position of a tile's 16 x G
+  // run per array, for the pairs n = spart, spart + kParts, ... of
+  // (tile n / (P+1), array n % (P+1)) (planes, then offsets at array P):
+  // consecutive threads read consecutive groups of a row, so the loads are
+  // coalesced.  A thread whose last pair index passes the end re-reads the
+  // last pair and stages nothing from it.
+  const int spart = tid / kPos;
+  const int srow = (tid % kPos) / kMaxG;
   const int sg = tid % kMaxG;
   const int sgc = min(sg, G - 1);
-  uint32_t sv[TMAX][P + 1];
+  uint32_t sv[kPerThread];
 #pragma unroll
-  for (int k = 0; k < TMAX; ++k) {
-    const int row = min(((int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x) * kTileRows + srow,
-                        M - 1);
-#pragma unroll
-    for (int i = 0; i < P; ++i) sv[k][i] = load_raw(alpha + i * MG + (size_t)row * G + sgc);
-    sv[k][P] = load_raw(zero + (size_t)row * G + sgc);
+  for (int u = 0; u < kPerThread; ++u) {
+    const int n = min(u * kParts + spart, kPairs - 1);
+    const int k = n / (P + 1), a = n % (P + 1);
+    const int row =
+        min(((int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x) * kTileRows + srow, M - 1);
+    const T *src = a < P ? alpha + a * MG : zero;
+    sv[u] = load_raw(src + (size_t)row * G + sgc);
   }
 
-  // ---- then tile 0's sign words.  Later tiles are requested only after the
-  // barrier below, AHEAD tiles in front of the one being looked up: the small
-  // loads the barrier waits for (x, scales) are otherwise queued behind every
-  // tile's sign words and the whole workgroup idles for most of the stream.
-  // (Past my last tile a fetch re-reads my own last tile: lines already in
-  // flight, so the load phase stays branch-free.)
-  constexpr int kAhead = AHEAD < TMAX - 1 ? AHEAD : TMAX - 1;
-  constexpr int kRing = kAhead + 1;
-  Tile tiles[kRing];
-  auto fetch = [&](int k, Tile &o) {
+  // ---- sign words of this lane's half group, one uint2 per plane.  Past my
+  // last tile a fetch re-reads my own last tile (lines already in flight), so
+  // the load phase stays branch-free.
+  uint2 tiles[2][P];
+  const int js = min(win * kG1Ksub + gw, G - 1);
+  auto fetch = [&](int k, uint2 (&o)[P]) {
     const int t = (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x;
+    const size_t q = (((size_t)t * G + js) * kTileRows + r) * 2 + half;  // uint2 index
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int js = min(w * kG1Ksub + gw, G - 1);
-      const size_t q = (((size_t)t * G + js) * kTileRows + r) * 2 + half;  // uint2 index
-#pragma unroll
-      for (int i = 0; i < P; ++i) o.bits[w][i] = bits2[i * plane_stride * 2 + q];
-    }
+    for (int i = 0; i < P; ++i) o[i] = bits2[i * plane_stride * 2 + q];
   };
+  // tile 0's sign words after the scales (the barrier below waits for those);
+  // later tiles' are requested after the barrier, one ahead of the tile being
+  // looked up, so the small loads the barrier waits for are not queued behind
+  // every tile's sign words
   fetch(0, tiles[0]);
 
-  // ---- build every window's tables and group sums
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
+  // ---- build the tables and group sums
+  {
     float f[4];
-    Act<T>::cvt(xr[w], chunk_parity(tid % kChunksPerGroup), f);
+    Act<T>::cvt(xr, chunk_parity(bc), f);
     float4 v[4];
     chunk_entries(f, v);
-    float4 *dst = reinterpret_cast<float4 *>(lut + w * kRWindowBytes +
-                                             (tid / kChunksPerGroup) * kRGroupStride +
-                                             r_chunk_offset(tid % kChunksPerGroup));
+    float4 *dst = reinterpret_cast<float4 *>(lut + (tid / kRThreads) * kRWindowBytes +
+                                             (bj % kG1Ksub) * kRGroupStride + r_chunk_offset(bc));
     dst[0] = v[0];
     dst[1] = v[1];
     dst[2] = v[2];
@@ -340,31 +345,26 @@ __global__ __launch_bounds__(kRThreads) void gemv_res_kernel(
     float cs = (f[0] + f[1]) + (f[2] + f[3]);
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) cs += __shfl_xor(cs, off);
-    if ((tid & 31) == 0) gsum[w * kG1Ksub + tid / 32] = cs;
+    if ((tid & 31) == 0) gsum[bj] = cs;
   }
-  if (sok) {
 #pragma unroll
-    for (int k = 0; k < TMAX; ++k)
-#pragma unroll
-      for (int i = 0; i <= P; ++i) scl[k][i][srow][sg] = sv[k][i];
+  for (int u = 0; u < kPerThread; ++u) {
+    const int n = u * kParts + spart;
+    if (n < kPairs) scl[n / (P + 1)][n % (P + 1)][srow][sg] = sv[u];
   }
   __syncthreads();
-#pragma unroll
-  for (int k = 1; k <= kAhead; ++k) fetch(k, tiles[k]);
+  if (TMAX > 1) fetch(1, tiles[1]);
 
-  auto consume = [&](int k, const Tile &o) -> float {
+  const int j = win * kG1Ksub + gw;
+  const uint32_t base =
+      lds_addr(lut + win * kRWindowBytes + gw * kRGroupStride + r_chunk_offset(16 * half));
+  auto consume = [&](int k, const uint2 (&o)[P]) -> float {
     float a = 0.f;
+    if (j < G) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int j = w * kG1Ksub + gw;
-      if (j < G) {
-        const uint32_t base = lds_addr(lut + w * kRWindowBytes + gw * kRGroupStride +
-                                       r_chunk_offset(16 * half));
-#pragma unroll
-        for (int i = 0; i < P; ++i)
-          a = fmaf(raw_to_float<T>(scl[k][i][r][j]), r_half_sum(o.bits[w][i], base), a);
-        if (half == 0) a = fmaf(raw_to_float<T>(scl[k][P][r][j]), gsum[j], a);
-      }
+      for (int i = 0; i < P; ++i)
+        a = fmaf(raw_to_float<T>(scl[k][i][r][j]), r_half_sum(o[i], base), a);
+      if (half == 0) a = fmaf(raw_to_float<T>(scl[k][P][r][j]), gsum[j], a);
     }
     return a;
   };
@@ -373,11 +373,11 @@ __global__ __launch_bounds__(kRThreads) void gemv_res_kernel(
 #pragma unroll
   for (int k = 0; k < TMAX; ++k) {
     acc[k] = 0.f;
-    if (k < nt) acc[k] = consume(k, tiles[k % kRing]);
-    if (k + kRing < TMAX) fetch(k + kRing, tiles[k % kRing]);  // refill the slot just read
+    if (k < nt) acc[k] = consume(k, tiles[k % 2]);
+    if (k + 2 < TMAX) fetch(k + 2, tiles[k % 2]);  // refill the slot just read
   }
 
-  // ---- reduce the 32 slot partials of each row of each tile, fixed order
+  // ---- reduce the slot partials of each row of each tile, fixed order
 #pragma unroll
   for (int k = 0; k < TMAX; ++k) {
     acc[k] += __shfl_xor(acc[k], 16);
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(kRThreads) void gemv_res_kernel(
     const int mm = ((int)blockIdx.x + k * (int)gridDim.x) * kTileRows + rr;
     float sum = 0.f;
 #pragma unroll
-    for (int v = 0; v < kRWaves; ++v) sum += part[v][k][rr];
+    for (int v = 0; v < kWaves; ++v) sum += part[v][k][rr];
     if (k < nt && mm < M) y[mm] = (T)sum;
   }
 }
@@ -562,19 +562,19 @@ void gemv_res_launch(dim3 grid, hipStream_t s, const uint4 *b4, const T *a, cons
                      const T *xx, T *yy, int M, int G, int MT, int p) {
   switch (p) {
     case 1:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 1, TMAX>), grid, dim3(kRThreads), 0, s, b4, a,
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 1, TMAX>), grid, dim3(kRThreads * NW), 0, s, b4, a,
                          z, xx, yy, M, G, MT);
       break;
     case 2:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 2, TMAX>), grid, dim3(kRThreads), 0, s, b4, a,
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 2, TMAX>), grid, dim3(kRThreads * NW), 0, s, b4, a,
                          z, xx, yy, M, G, MT);
       break;
     case 3:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 3, TMAX>), grid, dim3(kRThreads), 0, s, b4, a,
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 3, TMAX>), grid, dim3(kRThreads * NW), 0, s, b4, a,
                          z, xx, yy, M, G, MT);
       break;
     default:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 4, TMAX>), grid, dim3(kRThreads), 0, s, b4, a,
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 4, TMAX>), grid, dim3(kRThreads * NW), 0, s, b4, a,
                          z, xx, yy, M, G, MT);
       break;
   }

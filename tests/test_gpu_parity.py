@@ -153,6 +153,9 @@ def test_config1_tiny_fp32():
     (1, 128, 1, np.float32), (15, 128, 2, np.float16), (17, 256, 4, np.float32),
     (100, 384, 3, np.float16), (48, 2048, 4, np.float32), (33, 2176, 2, np.float16),
     (64, 4224, 4, np.float16), (20, 16384 + 2048, 2, np.float32), (8, 40960, 1, np.float16),
+    # two windows, several row tiles per workgroup, and a last round of tiles
+    # that only some workgroups take
+    (4100, 3968, 4, np.float16), (9000, 2560, 3, np.float32),
 ])
 def test_gemv_ragged_and_windowed_shapes(M, K, P, dt):
     """Ragged row tiles, partial K windows, more windows than one prefetch batch."""
