@@ -33,14 +33,14 @@
 //
 // Two ways to apply the scales.
 //  * Per plane (up to 32 requests): A = the plane's +-alpha pair per column,
-//    one shift and one bit-field insert per pair, and one MFMA per plane plus
-//    one with A = (z, z) for the offset; the matrix cores do the sum over
-//    planes.  Two VALU operations per pair and plane.  Each plane has its own
+//    one bit-field insert per pair and plane (the shift is shared by two
+//    planes, see below), and one MFMA per plane plus one with A = (z, z) for
+//    the offset; the matrix cores do the sum over planes.  Each plane has its own
 //    accumulator, so requests of one launch may use different precisions
 //    (AnyBCQ notes, per-request precision): request r adds the accumulators of
 //    its first p_r planes only, all planes having been read once.
 //  * Summed (48 and 64 requests): the weight z + sum +-alpha is formed on the
-//    vector ALUs (a third operation, a packed add, per pair and plane) and
+//    vector ALUs (a packed add per pair and plane on top of the decode) and
 //    one MFMA per request tile contracts it, since with four request tiles
 //    the per-plane MFMAs would outnumber the VALU work they save.
 //
@@ -77,10 +77,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMfGroups = 4;           // groups per step (lane (r, h) takes group h)
 constexpr int kMfBlocks = kGroup / 8;  // 8-column blocks per group (MFMAs per step)
 
-// Wavefronts (16-row tiles) per workgroup: 8 -- two per SIMD, so one's waits
-// and issue stalls are filled by the other -- while the registers of two
-// wavefronts fit a SIMD (up to 32 requests); 4 above that.
-constexpr int mf_waves(int nt) { return nt <= 2 ? 8 : 4; }
+// Wavefronts (16-row tiles) per workgroup: 8, two per SIMD, so one's waits
+// and issue stalls are filled by the other.  At 64 requests two wavefronts
+// just fit a SIMD's registers (256 each, no spills); measured 5% faster than
+// four wavefronts with one per SIMD.
+constexpr int mf_waves(int) { return 8; }
 
 template <int NB, int W>
 struct MfStage {
@@ -217,11 +218,22 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
         half2v w[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) w[v] = as_h2(z2);
+        // planes added in order; planes i and i+1 share one 64-bit shift, as
+        // in the per-plane branch below
 #pragma unroll
-        for (int i = 0; i < P; ++i)
+        for (int i = 0; i < P; i += 2)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            w[v] += as_h2(((wp[i][q] << (15 - (4 * u + v))) & 0x80008000u) | mag[i]);
+          for (int v = 0; v < 4; ++v) {
+            int sh = 15 - (4 * u + v);
+            if (i + 1 < P) {
+              asm("" : "+s"(sh));
+              const uint64_t w2 = ((uint64_t)wp[i + 1][q] << 32 | wp[i][q]) << sh;
+              w[v] += as_h2(((uint32_t)w2 & 0x80008000u) | mag[i]);
+              w[v] += as_h2(((uint32_t)(w2 >> 32) & 0x80008000u) | mag[i + 1]);
+            } else {
+              w[v] += as_h2(((wp[i][q] << sh) & 0x80008000u) | mag[i]);
+            }
+          }
         half8 a;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
