@@ -399,6 +399,170 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(const float *__res
   Y[(size_t)n * ldy + mm] = (half_t)s;
 }
 
+// ---------------------------------------------------------------- whole K
+//
+// Up to 16 requests and K <= 4096 (at most 32 groups): a workgroup owns whole
+// 16-row tiles and needs no second pass.  Its eight wavefronts split K, four
+// groups each, so wavefront w and lane (r, h) take group 4w + h: one step of
+// the split kernel above, with the same decode and per-plane MFMAs.  Every
+// request's activations for all of K (at most 16 x 4096 fp16, 128 KB) are
+// staged once per workgroup in LDS with coalesced loads, laid out and
+// swizzled like the split kernel's stage, and serve every tile the workgroup
+// walks (tiles blockIdx.x + k * gridDim.x, grid = min(tiles, CUs)).  Per tile
+// the eight wavefronts' partial products meet in LDS and are summed in
+// wavefront order (deterministic).  The next tile's sign words and scales are
+// requested while the current one computes.
+constexpr int kWkWaves = 8;
+constexpr int kWkMaxGroups = kWkWaves * kMfGroups;  // 32 groups: K <= 4096
+
+__device__ __forceinline__ int wk_slot(int q, int g, int n) {
+  return ((q * kWkMaxGroups + g) << 4) + (n ^ (q & 15));
+}
+
+template <int P>
+__global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
+    const u32x4 *__restrict__ bits, const half_t *__restrict__ alpha,
+    const half_t *__restrict__ zero, const half_t *__restrict__ X, int ldx, int b,
+    half_t *__restrict__ Y, int ldy, int M, int G, int MT, const MfPrec prec) {
+  constexpr int kReq = 16;
+  __shared__ u32x4 xs[kReq * kWkMaxGroups * kMfBlocks];  // 128 KB
+  __shared__ floatx4 red[kWkWaves][64];
+  using OpsW = MfW<P>;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int h = lane >> 4;
+  const int g = wave * kMfGroups + h;  // this lane's group of K
+  const int gc = min(g, G - 1);
+  const int nt = (MT - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // my tiles
+  const size_t plane_blocks = (size_t)MT * G * kTileRows;
+  const size_t MG = (size_t)M * G;
+
+  // ---- stage the activations: thread tid holds block (group tid / 16,
+  // 8-column block tid % 16) of every request; requests past b and groups
+  // past G are stored as zeros
+  {
+    const int sg = tid >> 4;
+    const int sn = tid & 15;
+    const bool gin = sg < G;
+    const half_t *src = X + (size_t)min(sg, G - 1) * kGroup + sn * 8;
+    u32x4 v[kReq];
+#pragma unroll
+    for (int q = 0; q < kReq; ++q)
+      v[q] = q < b ? *reinterpret_cast<const u32x4 *>(src + (size_t)q * ldx) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int q = 0; q < kReq; ++q) xs[wk_slot(q, sg, sn)] = gin ? v[q] : u32x4{0, 0, 0, 0};
+  }
+
+  auto fetch_w = [&](int k, OpsW &o) __attribute__((always_inline)) {
+    const int t = (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x;
+    const int m = min(t * kTileRows + r, M - 1);
+    const u32x4 *tb = bits + ((size_t)t * G + gc) * kTileRows + r;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      o.bits[i] = tb[i * plane_blocks];
+      o.a[i] = *reinterpret_cast<const unsigned short *>(alpha + i * MG + (size_t)m * G + gc);
+    }
+    o.z = *reinterpret_cast<const unsigned short *>(zero + (size_t)m * G + gc);
+  };
+
+  OpsW wa, wb;
+  fetch_w(0, wa);
+  __syncthreads();
+
+  auto tile = [&](int k, const OpsW &o) __attribute__((always_inline)) {
+    floatx4 acc[P + 1];
+#pragma unroll
+    for (int i = 0; i <= P; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    uint32_t wp[P][4], mag[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const uint32_t a16 = o.a[i];
+      const uint32_t neg = (uint32_t)((int32_t)(a16 << 16) >> 31);
+      mag[i] = (a16 & 0x7FFFu) * 0x10001u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wp[i][q] = ~(o.bits[i][q] ^ neg);
+    }
+    const uint32_t z2 = o.z * 0x10001u;
+    const half8 az = __builtin_bit_cast(half8, u32x4{z2, z2, z2, z2});
+#pragma unroll
+    for (int n = 0; n < kMfBlocks; ++n) {
+      const int q = n >> 2;
+      const int u = n & 3;
+      const half8 bop = __builtin_bit_cast(half8, xs[wk_slot(r, g, n)]);
+#pragma unroll
+      for (int i = 0; i < P; i += 2) {
+        u32x4 av, bv;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          int sh = 15 - (4 * u + v);
+          if (i + 1 < P) {
+            asm("" : "+s"(sh));
+            const uint64_t w2 = ((uint64_t)wp[i + 1][q] << 32 | wp[i][q]) << sh;
+            av[v] = ((uint32_t)w2 & 0x80008000u) | mag[i];
+            bv[v] = ((uint32_t)(w2 >> 32) & 0x80008000u) | mag[i + 1];
+          } else {
+            av[v] = ((wp[i][q] << sh) & 0x80008000u) | mag[i];
+          }
+        }
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), bop,
+                                                        acc[i], 0, 0, 0);
+        if (i + 1 < P)
+          acc[i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, bv), bop,
+                                                              acc[i + 1], 0, 0, 0);
+      }
+      acc[P] = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bop, acc[P], 0, 0, 0);
+    }
+    // D layout: lane (c, h) holds rows 4h .. 4h+3 for request c; the offset,
+    // then the planes request c uses
+    const int pn = prec.p[r];
+    floatx4 d = acc[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      if (i < pn) d += acc[i];
+    red[wave][lane] = d;
+    __syncthreads();
+    if (tid < 64 * 4) {
+      const int l = tid >> 2, v = tid & 3;
+      const int c = l & 15;
+      const int t = (int)blockIdx.x + k * (int)gridDim.x;
+      const int mm = t * kTileRows + 4 * (l >> 4) + v;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWkWaves; ++w) sum += red[w][l][v];
+      if (c < b && mm < M) Y[(size_t)c * ldy + mm] = (half_t)sum;
+    }
+    __syncthreads();
+  };
+
+  // two tiles per iteration, alternating register sets; a fetch past my last
+  // tile re-reads it (lines already in flight), and the loop exits only at its
+  // header, so the waits stay partial
+  int k = 0;
+  for (; k + 1 < nt; k += 2) {
+    fetch_w(k + 1, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(k, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_w(k + 2, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    tile(k + 1, wb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (k < nt) tile(k, wa);
+}
+
+// The whole-K kernel serves a launch when it has one request tile, K fits
+// its 32 groups with more than half of them used (below that the split
+// kernel's slices keep more of the chip busy), and there are enough row tiles
+// to give most compute units one.
+bool use_wk(int M, int K, int n) {
+  const int G = K / kGroup;
+  return n <= 16 && G > kWkMaxGroups / 2 && G <= kWkMaxGroups && row_tiles(M) >= 192;
+}
+
 // Steps per slice and slice count for (M, K) and W wavefronts per workgroup.
 // One workgroup is resident per compute unit (the register or LDS budget of
 // either size allows no second), so a launch runs in rounds of kMfSlots
@@ -430,6 +594,7 @@ void mfma_split(int M, int K, int W, int *sps, int *slices) {
 
 // Workspace of one launch of n requests: fp32 partials [slice][request][row].
 size_t launch_workspace_bytes(int M, int K, int n) {
+  if (use_wk(M, K, n)) return 0;
   int sps, s;
   mfma_split(M, K, mf_waves((n + 15) / 16), &sps, &s);
   return s > 1 ? (size_t)s * n * M * sizeof(float) : 0;
@@ -459,19 +624,33 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
   const int G = K / kGroup;
   const int MT = row_tiles(M);
   const int NT = (b + 15) / 16;
-  const int W = mf_waves(NT);
-  int sps, S;
-  mfma_split(M, K, W, &sps, &S);
   const u32x4 *b4 = reinterpret_cast<const u32x4 *>(bits);
   const half_t *a = static_cast<const half_t *>(alpha);
   const half_t *z = static_cast<const half_t *>(zero);
   const half_t *X = static_cast<const half_t *>(x);
   half_t *Y = static_cast<half_t *>(y);
-  float *w = S > 1 ? static_cast<float *>(ws) : nullptr;
-  dim3 grid((MT + W - 1) / W, S), block(64 * W);
   MfPrec prec;
   for (int q = 0; q < kMfMaxBatch; ++q)
     prec.p[q] = (uint8_t)(p_req != nullptr && q < b ? p_req[q] : p);
+  if (use_wk(M, K, b)) {
+    dim3 grid(MT < kMfSlots ? MT : kMfSlots), block(64 * kWkWaves);
+#define BCQ_WK(PV)                                                                        \
+  hipLaunchKernelGGL((gemm_wk_kernel<PV>), grid, block, 0, s, b4, a, z, X, ldx, b, Y, ldy, M, \
+                     G, MT, prec)
+    switch (p) {
+      case 1: BCQ_WK(1); break;
+      case 2: BCQ_WK(2); break;
+      case 3: BCQ_WK(3); break;
+      default: BCQ_WK(4); break;
+    }
+#undef BCQ_WK
+    return hipGetLastError();
+  }
+  const int W = mf_waves(NT);
+  int sps, S;
+  mfma_split(M, K, W, &sps, &S);
+  float *w = S > 1 ? static_cast<float *>(ws) : nullptr;
+  dim3 grid((MT + W - 1) / W, S), block(64 * W);
 #define BCQ_MF(NTV, PV)                                                                  \
   hipLaunchKernelGGL((gemm_mfma_kernel<NTV, PV, (NTV >= 3), mf_waves(NTV)>), grid, block, 0, \
                      s, b4, a, z, X, ldx, b, Y, ldy, w, M, G, MT, sps, prec)

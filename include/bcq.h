@@ -132,12 +132,15 @@ bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype 
  * decode tiles of W to fp16 once per launch of up to 64 requests and contract
  * them with X on the matrix cores (fp32 accumulation; up to 32 requests each
  * plane's +-alpha is an exact fp16 operand, from 48 the decoded weight
- * z + sum +-alpha is rounded to fp16).  That path splits K over workgroups and
- * needs bcq_workspace_bytes(store, b) bytes of device workspace (4-byte
- * aligned) for the K slices' partial sums: contents need no initialisation
- * and are clobbered by the call, so calls that may run at the same time need
- * separate workspaces.  workspace may be NULL when that size is 0; a smaller
- * workspace gives BCQ_ERR_INVALID_ARG.
+ * z + sum +-alpha is rounded to fp16).  Launches of up to 16 requests with
+ * 17..32 groups of K (K in 2176..4096) and at least 192 tiles of 16 rows
+ * (M >= 3057) keep K within one workgroup; other launches split K over
+ * workgroups and need
+ * bcq_workspace_bytes(store, b) bytes of device workspace (4-byte aligned) for
+ * the K slices' partial sums: contents need no initialisation and are
+ * clobbered by the call, so calls that may run at the same time need separate
+ * workspaces.  workspace may be NULL when that size is 0; a smaller workspace
+ * gives BCQ_ERR_INVALID_ARG.
  */
 bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int32_t b,
                            int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,

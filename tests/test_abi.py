@@ -114,10 +114,14 @@ E_ARG, E_UNS, E_ALN = bcq.BCQ_ERR_INVALID_ARG, bcq.BCQ_ERR_UNSUPPORTED, bcq.BCQ_
     (lambda: skinny(make_store(), ldx=260), E_ALN),  # 260 halves = 520 B, not a multiple of 16
     (lambda: skinny(make_store(), X=FAKE + 2), E_ALN),
     (lambda: skinny(make_store(), p=5), E_ARG),
-    (lambda: skinny(make_store(M=4096, K=4096), b=16), E_ARG),  # needs a workspace
-    (lambda: skinny(make_store(M=4096, K=4096), b=16, ws=FAKE, wsb=16), E_ARG),
-    (lambda: skinny(make_store(M=4096, K=4096), b=3), E_ARG),  # fp16 b >= 3: matrix cores
-    (lambda: mixed(make_store(M=4096, K=4096), [2, 3, 4]), E_ARG),  # needs a workspace too
+    # K split over workgroups needs a workspace: fewer than 192 row tiles, or
+    # more than 16 requests in a launch
+    (lambda: skinny(make_store(M=1024, K=4096), b=16), E_ARG),
+    (lambda: skinny(make_store(M=1024, K=4096), b=16, ws=FAKE, wsb=16), E_ARG),
+    (lambda: skinny(make_store(M=1024, K=4096), b=3), E_ARG),  # fp16 b >= 3: matrix cores
+    (lambda: skinny(make_store(M=4096, K=4096), b=32), E_ARG),
+    (lambda: mixed(make_store(M=1024, K=4096), [2, 3, 4]), E_ARG),  # needs a workspace too
+    (lambda: mixed(make_store(M=4096, K=4096), [2, 3, 4] * 6), E_ARG),
     (lambda: mixed(make_store(), [2, 3, 0, 4]), E_ARG),
     (lambda: mixed(make_store(), [2, 3, 5, 4]), E_ARG),
     (lambda: mixed(make_store(planes=3), [2, 3, 4]), E_ARG),
@@ -146,22 +150,26 @@ def test_pack_validation():
 
 def test_workspace_sizes():
     lib = bcq.load()
+    ws = lambda st, b: lib.bcq_workspace_bytes(ctypes.byref(st), b)
     st = make_store(M=4096, K=4096)
-    # batch 1 and fp16 batch 2 use the table kernels; from 3 the matrix cores
-    assert lib.bcq_workspace_bytes(ctypes.byref(st), 1) == 0
-    assert lib.bcq_workspace_bytes(ctypes.byref(st), 2) == 0
-    assert lib.bcq_workspace_bytes(ctypes.byref(st), 3) > 0
-    # split-K partials: one fp32 value per (K slice, request, row), at most
-    # one slice per 4-group step (K = 4096: 8 steps)
-    need16 = lib.bcq_workspace_bytes(ctypes.byref(st), 16)
-    need64 = lib.bcq_workspace_bytes(ctypes.byref(st), 64)
-    assert need16 > 0 and need64 > 0
-    assert need16 % (16 * 4096 * 4) == 0 and need16 <= 8 * 16 * 4096 * 4
-    assert need64 % (64 * 4096 * 4) == 0 and need64 <= 8 * 64 * 4096 * 4
-    # launched 64 at a time, the launches reuse the workspace in order
-    assert lib.bcq_workspace_bytes(ctypes.byref(st), 256) == need64
-    assert lib.bcq_workspace_bytes(ctypes.byref(st), 80) == max(
-        need64, lib.bcq_workspace_bytes(ctypes.byref(st), 16))
+    # batch 1 and fp16 batch 2 use the table kernels, 3..16 requests on 256
+    # row tiles the whole-K matrix-core kernel: none of them needs a workspace
+    for b in (1, 2, 3, 16):
+        assert ws(st, b) == 0, b
+    # from 17 requests K is split over workgroups: one fp32 partial per (K
+    # slice, request, row), at most one slice per 4-group step (8 steps here)
+    need32, need64 = ws(st, 32), ws(st, 64)
+    assert need32 > 0 and need32 % (32 * 4096 * 4) == 0 and need32 <= 8 * 32 * 4096 * 4
+    assert need64 > 0 and need64 % (64 * 4096 * 4) == 0 and need64 <= 8 * 64 * 4096 * 4
+    # a call runs launches of 64 (one precision) or 32 (per-request
+    # precisions) in order, reusing the workspace: the size covers the largest
+    assert ws(st, 256) == max(need64, need32)
+    assert ws(st, 80) == max(need64, need32)
+    # fewer row tiles than the chip has compute units: split K from 3 requests
+    small = make_store(M=1024, K=4096)
+    need3, need16 = ws(small, 3), ws(small, 16)
+    assert need3 > 0 and need3 % (3 * 1024 * 4) == 0
+    assert need16 > 0 and need16 % (16 * 1024 * 4) == 0 and need16 <= 8 * 16 * 1024 * 4
     f32 = make_store(M=4096, K=4096, dtype=bcq.BCQ_F32)
     assert lib.bcq_workspace_bytes(ctypes.byref(f32), 64) == 0  # fp32 uses the table path
     assert lib.bcq_workspace_bytes(None, 16) == 0

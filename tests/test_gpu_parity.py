@@ -358,7 +358,7 @@ def test_mixed_rejects_bad_entry_and_writes_nothing():
 def test_mfma_batches(M, K, b):
     w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=M + b, outlier_frac=0.01)
     st = store_of(w)
-    ws = bcq.new_workspace(st, b)  # zeroed once, reused by every call below
+    ws = bcq.new_workspace(st, b)  # one workspace, never cleared, reused by every call below
     rows = sample_rows(M, 256)
     for p in (1, 2, 3, 4):
         say("mfma", M, K, b, p)
@@ -388,6 +388,37 @@ def test_mfma_ragged_rows_and_groups(b):
         for r in range(b):
             assert rel_l2(got[r], ref[r]) <= 2e-3, (p, r)
     say("mfma ragged mixed", M, K, b, list(w.p_req))
+    Y = torch.empty((b, M), dtype=torch.float16, device="cuda")
+    bcq.bcq_gemv_mixed_p(st, w.p_req, dev(w.x), Y)
+    ref = oracle_y(w, w.x, w.p_req, rows)
+    got = Y.cpu().numpy()[:, rows]
+    for r in range(b):
+        assert rel_l2(got[r], ref[r]) <= 2e-3, (r, int(w.p_req[r]))
+
+
+@pytest.mark.parametrize("M,K", [(3100, 3712), (12375, 2304)])
+@pytest.mark.parametrize("b", [3, 16])
+def test_mfma_whole_k_workgroups(M, K, b):
+    """Up to 16 requests with 17..32 groups and at least 192 row tiles: one
+    workgroup per row tile (or several, walked in turn), K split over its
+    wavefronts.  M = 3100 leaves a partial last tile; K = 3712 (29 groups)
+    leaves the last wavefront one group and three lanes' groups past K;
+    M = 12375 (774 tiles) gives workgroups 3 or 4 tiles, an odd count
+    included.  Every precision, then per-request precisions; no workspace."""
+    w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=M + K + b, outlier_frac=0.01,
+                       p_choices=(1, 2, 3, 4))
+    st = store_of(w)
+    assert bcq.bcq_workspace_bytes(st, b) == 0
+    rows = np.unique(np.concatenate([sample_rows(M, 160), np.arange(M - 40, M)]))
+    for p in (1, 2, 3, 4):
+        say("mfma whole-K", M, K, b, p)
+        Y = torch.empty((b, M), dtype=torch.float16, device="cuda")
+        bcq.bcq_gemm_skinny(st, p, dev(w.x), Y)
+        ref = oracle_y(w, w.x, [p] * b, rows)
+        got = Y.cpu().numpy()[:, rows]
+        for r in range(b):
+            assert rel_l2(got[r], ref[r]) <= 2e-3, (p, r)
+    say("mfma whole-K mixed", M, K, b, list(w.p_req))
     Y = torch.empty((b, M), dtype=torch.float16, device="cuda")
     bcq.bcq_gemv_mixed_p(st, w.p_req, dev(w.x), Y)
     ref = oracle_y(w, w.x, w.p_req, rows)
@@ -433,6 +464,34 @@ def test_config5_layer_sweep_sampled(shape, b):
     got = Y.cpu().numpy()[:, rows]
     for r in range(b):
         assert rel_l2(got[r], ref[r]) <= 2e-3
+
+
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+def test_maximum_batch(dt):
+    """b = BCQ_MAX_BATCH: fp16 runs four matrix-core launches of 64 requests
+    (mixed precision eight of 32), fp32 thirty-two table launches of 8; one
+    workspace serves every launch of a call.  Every row and request checked."""
+    M, K, b = 200, 640, bcq.BCQ_MAX_BATCH
+    w = bcq_synth.make(M, K, 4, b=b, dtype=dt, seed=256, p_choices=(1, 2, 3, 4))
+    st = store_of(w)
+    tdt = torch.float16 if dt == np.float16 else torch.float32
+    ws = bcq.new_workspace(st, b)
+    tol = 2e-3 if dt == np.float16 else 1e-5
+    for p in (3, 4):
+        say("max batch", np.dtype(dt).name, b, p)
+        Y = torch.empty((b, M), dtype=tdt, device="cuda")
+        bcq.bcq_gemm_skinny(st, p, dev(w.x), Y, workspace=ws)
+        ref = oracle_y(w, w.x, [p] * b)
+        got = Y.cpu().numpy()
+        for r in range(b):
+            assert rel_l2(got[r], ref[r]) <= tol, (p, r)
+    say("max batch mixed", np.dtype(dt).name, b)
+    Y = torch.empty((b, M), dtype=tdt, device="cuda")
+    bcq.bcq_gemv_mixed_p(st, w.p_req, dev(w.x), Y, workspace=ws)
+    ref = oracle_y(w, w.x, w.p_req)
+    got = Y.cpu().numpy()
+    for r in range(b):
+        assert rel_l2(got[r], ref[r]) <= tol, (r, int(w.p_req[r]))
 
 
 def test_fp32_large_batch_uses_exact_tables():
