@@ -419,7 +419,7 @@ __device__ __forceinline__ int wk_slot(int q, int g, int n) {
   return ((q * kWkMaxGroups + g) << 4) + (n ^ (q & 15));
 }
 
-template <int P>
+template <int P, bool MIXED>
 __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
     const u32x4 *__restrict__ bits, const half_t *__restrict__ alpha,
     const half_t *__restrict__ zero, const half_t *__restrict__ X, int ldx, int b,
@@ -441,19 +441,26 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
   const size_t MG = (size_t)M * G;
 
   // ---- stage the activations: thread tid holds block (group tid / 16,
-  // 8-column block tid % 16) of every request; requests past b and groups
-  // past G are stored as zeros
+  // 8-column block tid % 16) of every request.  Groups past G are stored as
+  // zeros (their lanes' clamped weights then add nothing).  Requests past b
+  // are left unwritten: B-operand column c only reaches output column c, and
+  // columns past b are never stored.
   {
     const int sg = tid >> 4;
     const int sn = tid & 15;
-    const bool gin = sg < G;
-    const half_t *src = X + (size_t)min(sg, G - 1) * kGroup + sn * 8;
-    u32x4 v[kReq];
+    if (sg < G) {
+      const half_t *src = X + (size_t)sg * kGroup + sn * 8;
+      u32x4 v[kReq];
 #pragma unroll
-    for (int q = 0; q < kReq; ++q)
-      v[q] = q < b ? *reinterpret_cast<const u32x4 *>(src + (size_t)q * ldx) : u32x4{0, 0, 0, 0};
+      for (int q = 0; q < kReq; ++q)
+        if (q < b) v[q] = *reinterpret_cast<const u32x4 *>(src + (size_t)q * ldx);
 #pragma unroll
-    for (int q = 0; q < kReq; ++q) xs[wk_slot(q, sg, sn)] = gin ? v[q] : u32x4{0, 0, 0, 0};
+      for (int q = 0; q < kReq; ++q)
+        if (q < b) xs[wk_slot(q, sg, sn)] = v[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < kReq; ++q) xs[wk_slot(q, sg, sn)] = u32x4{0, 0, 0, 0};
+    }
   }
 
   auto fetch_w = [&](int k, OpsW &o) __attribute__((always_inline)) {
@@ -516,12 +523,17 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
       acc[P] = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bop, acc[P], 0, 0, 0);
     }
     // D layout: lane (c, h) holds rows 4h .. 4h+3 for request c; the offset,
-    // then the planes request c uses
-    const int pn = prec.p[r];
+    // then the planes request c uses (all P unless precisions differ)
     floatx4 d = acc[P];
+    if constexpr (MIXED) {
+      const int pn = prec.p[r];
 #pragma unroll
-    for (int i = 0; i < P; ++i)
-      if (i < pn) d += acc[i];
+      for (int i = 0; i < P; ++i)
+        if (i < pn) d += acc[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < P; ++i) d += acc[i];
+    }
     red[wave][lane] = d;
     __syncthreads();
     if (tid < 64 * 4) {
@@ -634,9 +646,15 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
     prec.p[q] = (uint8_t)(p_req != nullptr && q < b ? p_req[q] : p);
   if (use_wk(M, K, b)) {
     dim3 grid(MT < kMfSlots ? MT : kMfSlots), block(64 * kWkWaves);
-#define BCQ_WK(PV)                                                                        \
-  hipLaunchKernelGGL((gemm_wk_kernel<PV>), grid, block, 0, s, b4, a, z, X, ldx, b, Y, ldy, M, \
-                     G, MT, prec)
+    bool mixed = false;
+    for (int q = 0; q < b; ++q) mixed = mixed || prec.p[q] != p;
+#define BCQ_WK(PV)                                                                           \
+  if (mixed)                                                                                 \
+    hipLaunchKernelGGL((gemm_wk_kernel<PV, true>), grid, block, 0, s, b4, a, z, X, ldx, b, Y, \
+                       ldy, M, G, MT, prec);                                                 \
+  else                                                                                       \
+    hipLaunchKernelGGL((gemm_wk_kernel<PV, false>), grid, block, 0, s, b4, a, z, X, ldx, b, Y, \
+                       ldy, M, G, MT, prec)
     switch (p) {
       case 1: BCQ_WK(1); break;
       case 2: BCQ_WK(2); break;
