@@ -11,11 +11,18 @@ using bcq::kGroup;
 
 constexpr int32_t kMaxM = 1 << 24;
 constexpr int32_t kMaxK = 1 << 20;
-// Smallest fp16 batch sent to the matrix cores.  From 3 requests the decoded
-// tiles on the matrix cores beat the per-request table lookups at every shape
-// measured on gfx950 (4096x4096, 14336x4096, 4096x14336, p = 3 and 4); at 2
-// the table kernel is as fast or faster.
+// Smallest fp16 batch always sent to the matrix cores.  From 3 requests the
+// decoded tiles on the matrix cores beat the per-request table lookups at
+// every shape measured on gfx950 (4096x4096, 14336x4096, 4096x14336, p = 3
+// and 4).  At 2 they win only where K stays within one workgroup (4096x4096:
+// 7.5 vs 8.3 us); where K is split the table kernel is faster (4096x14336:
+// 20.0 vs 22.6 us).
 constexpr int32_t kMfMinBatch = 3;
+
+bool on_matrix_cores(const bcq_store *st, int32_t b) {
+  return st->scale_dtype == BCQ_F16 &&
+         (b >= kMfMinBatch || (b == 2 && bcq::mfma_whole_k(st->M, st->K, b)));
+}
 
 size_t dtype_size(bcq_dtype d) { return d == BCQ_F16 ? 2 : 4; }
 bool dtype_valid(bcq_dtype d) { return d == BCQ_F16 || d == BCQ_F32; }
@@ -179,7 +186,7 @@ bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype 
 
 size_t bcq_workspace_bytes(const bcq_store *store, int32_t b) {
   if (check_store(store) != BCQ_OK || b < 1 || b > BCQ_MAX_BATCH) return 0;
-  if (b < kMfMinBatch || store->scale_dtype != BCQ_F16) return 0;
+  if (!on_matrix_cores(store, b)) return 0;
   return bcq::mfma_workspace_bytes(store->M, store->K, b);
 }
 
@@ -194,7 +201,7 @@ bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int
   BCQ_TRY(check_workspace(store, b, workspace, workspace_bytes));
   const char *Xc = static_cast<const char *>(X);
   char *Yc = static_cast<char *>(Y);
-  if (store->scale_dtype == BCQ_F16 && b >= kMfMinBatch)
+  if (on_matrix_cores(store, b))
     return run_mfma_batches(store, p, nullptr, Xc, b, ldx, Yc, ldy, workspace, bcq::kMfMaxBatch,
                             stream);
   int32_t ps[BCQ_MAX_BATCH];
@@ -224,7 +231,7 @@ bcq_status bcq_gemv_mixed_p(const bcq_store *store, const int32_t *p_host, const
   for (int32_t r = 0; r < b; ++r)
     shared = shared && store->alpha[p_host[r]] == store->alpha[pmax] &&
              store->zero[p_host[r]] == store->zero[pmax];
-  if (store->scale_dtype == BCQ_F16 && b >= kMfMinBatch && shared)
+  if (on_matrix_cores(store, b) && shared)
     return run_mfma_batches(store, pmax, p_host, Xc, b, ldx, Yc, ldy, workspace,
                             bcq::kMfMaxMixed, stream);
   return run_table_batches(store, p_host, Xc, b, ldx, Yc, ldy, stream);

@@ -65,4 +65,8 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
                             void *ws, const int32_t *p_req, hipStream_t s);
 size_t mfma_workspace_bytes(int M, int K, int b);
 
+// True when a launch of n fp16 requests on (M, K) keeps K within one
+// workgroup (no workspace, no second kernel).
+bool mfma_whole_k(int M, int K, int n);
+
 }  // namespace bcq

@@ -614,6 +614,8 @@ size_t launch_workspace_bytes(int M, int K, int n) {
 
 }  // namespace
 
+bool mfma_whole_k(int M, int K, int n) { return use_wk(M, K, n); }
+
 size_t mfma_workspace_bytes(int M, int K, int b) {
   // the launches of one call run in order and reuse the workspace; a call
   // splits b into launches of kMfMaxBatch requests (one precision) or of

@@ -126,9 +126,10 @@ bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype 
  * X: [b][ldx] (row r starts at X + r*ldx elements), 16-byte aligned, so ldx*size
  * must be a multiple of 16 bytes; ldx >= K.  Y: [b][ldy], ldy >= M, element
  * aligned.  1 <= b <= BCQ_MAX_BATCH.
- * Batch 1 runs the batch-1 kernel.  fp32 batches, and fp16 batches of 2, run on
- * the vector ALUs with sign-combination tables shared by up to 8 requests per
- * launch (exact fp32 sums of the stored values).  fp16 batches of 3 and more
+ * Batch 1 runs the batch-1 kernel.  fp32 batches, and fp16 batches of 2 unless
+ * K stays within one workgroup (below), run on the vector ALUs with
+ * sign-combination tables shared by up to 8 requests per launch (exact fp32
+ * sums of the stored values).  Other fp16 batches of 2, and those of 3 and more,
  * decode tiles of W to fp16 once per launch of up to 64 requests and contract
  * them with X on the matrix cores (fp32 accumulation; up to 32 requests each
  * plane's +-alpha is an exact fp16 operand, from 48 the decoded weight
@@ -159,9 +160,10 @@ size_t bcq_workspace_bytes(const bcq_store *store, int32_t b);
  * requested precision is read once per launch for all its requests, so mixing
  * precisions costs no extra plane traffic.  When every requested precision's
  * tables alias those of the largest one (one shared [P][M][G] scale array and
- * one offset array, as a shared store lays them out), fp16 batches of 3 and
- * more run on the matrix cores in launches of up to 32: each plane has its own
- * accumulator and request r sums its first p_host[r] planes.  Otherwise the
+ * one offset array, as a shared store lays them out), fp16 batches that
+ * bcq_gemm_skinny would send to the matrix cores (3 and more, or 2 where K
+ * stays within one workgroup) run there in launches of up to 32: each plane
+ * has its own accumulator and request r sums its first p_host[r] planes.  Otherwise the
  * table kernel runs launches of up to 8, giving each request zero scales for
  * planes past its precision.
  * p_host: [b] in HOST memory; every entry must lie in [1, planes], otherwise

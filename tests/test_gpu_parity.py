@@ -397,7 +397,7 @@ def test_mfma_ragged_rows_and_groups(b):
 
 
 @pytest.mark.parametrize("M,K", [(3100, 3712), (12375, 2304)])
-@pytest.mark.parametrize("b", [3, 16])
+@pytest.mark.parametrize("b", [2, 3, 16])
 def test_mfma_whole_k_workgroups(M, K, b):
     """Up to 16 requests with 17..32 groups and at least 192 row tiles: one
     workgroup per row tile (or several, walked in turn), K split over its
