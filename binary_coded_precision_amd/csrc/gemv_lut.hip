@@ -22,7 +22,8 @@
 //    16-row tiles; lane (r, hs) takes row r and half-group slot hs of a
 //    16-group window of tables (64 columns, two packed words per plane).
 //    K <= 4096 keeps the tables of all of K resident while the workgroup walks
-//    several tiles; larger K streams windows of tables through two buffers.
+//    several tiles; larger K streams windows of tables through two buffers
+//    (with two or more planes, 1024 lanes split the planes of each window).
 //  * LDS banks.  Table c sits at 80-byte stride (16 entries + 16 B pad) so that
 //    the 16-byte writes of 16 consecutive chunks cover distinct banks, and the
 //    four slots of a wavefront read disjoint quarters of the 64 banks.
@@ -544,6 +545,153 @@ __global__ __launch_bounds__(kRThreads) void gemv_stream_kernel(
   }
 }
 
+// 1024-lane variant for two or more planes.  Wavefronts 8..15 look up planes
+// PA..P-1 (PA = ceil(P/2)) of the same half-group slots in the same tables,
+// so a SIMD holds four wavefronts instead of two; wavefronts 0..7 build the
+// tables, stage the scales and look up planes 0..PA-1 and the offset term.
+// The halves run separate straight-line code, each issuing its own loads in a
+// fixed order so that its waits stay partial, and meet at the same barriers.
+template <typename T, int P>
+struct StreamShared {
+  __attribute__((aligned(16))) char lut[2][kRWindowBytes];
+  float gsum[2][kG1Ksub][4];
+  uint32_t scl[2][P + 1][kTileRows][kG1Ksub + 1];
+  float part[2 * kRWaves][kTileRows];
+};
+
+template <typename T, int P, bool UPPER>
+__device__ __forceinline__ void stream_half(StreamShared<T, P> &sm, const uint4 *__restrict__ bits,
+                                            const T *__restrict__ alpha,
+                                            const T *__restrict__ zero, const T *__restrict__ x,
+                                            int M, int G, int MT, int tid) {
+  constexpr int PA = (P + 1) / 2;
+  constexpr int I0 = UPPER ? PA : 0;       // first plane of this half
+  constexpr int NP = UPPER ? P - PA : PA;  // planes of this half
+  const int lane = tid & 63;
+  const int wave = tid >> 6;  // 0..7 within the half
+  const int r = lane & 15;
+  const int hs = wave * 4 + (lane >> 4);  // half-group slot 0..31 of the window
+  const int gw = hs >> 1;
+  const int half = hs & 1;
+  const int tile = blockIdx.x;
+  const int nwin = (G + kG1Ksub - 1) / kG1Ksub;
+  const size_t plane_stride = (size_t)MT * G * kTileRows;  // in uint4
+  const size_t MG = (size_t)M * G;
+  const uint2 *bits2 = reinterpret_cast<const uint2 *>(bits);
+  const bool stager = tid < (P + 1) * kTileRows * 4;
+  const int sa = min(tid / (kTileRows * 4), P);
+  const int srow = (tid / 4) % kTileRows;
+  const int sq = tid % 4;
+  const int s_m = min(tile * kTileRows + srow, M - 1);
+  const T *sbase = sa < P ? alpha + sa * MG + (size_t)s_m * G : zero + (size_t)s_m * G;
+
+  struct Slot {
+    uint2 bits[NP];
+    typename Act<T>::raw x;
+    uint32_t sc[4];
+  };
+  auto fetch_bits = [&](int v, Slot &o) __attribute__((always_inline)) {
+    const int w = min(v, nwin - 1);
+    const int js = min(w * kG1Ksub + gw, G - 1);
+    const size_t q = (((size_t)tile * G + js) * kTileRows + r) * 2 + half;  // uint2 index
+#pragma unroll
+    for (int u = 0; u < NP; ++u) o.bits[u] = bits2[(I0 + u) * plane_stride * 2 + q];
+  };
+  auto fetch_small = [&](int v, Slot &o) __attribute__((always_inline)) {
+    if constexpr (!UPPER) {
+      const int w = min(v, nwin - 1);
+      const int c = tid % kChunksPerGroup;
+      const int jx = min(w * kG1Ksub + tid / kChunksPerGroup, G - 1);
+      o.x = Act<T>::load(x + (size_t)jx * kGroup + chunk_base(c), chunk_parity(c));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o.sc[e] = load_raw(sbase + min(w * kG1Ksub + 4 * sq + e, G - 1));
+    }
+  };
+  auto fetch = [&](int v, Slot &o) __attribute__((always_inline)) {
+    fetch_bits(v, o);
+    fetch_small(v, o);
+  };
+  auto build = [&](const Slot &o, int buf) __attribute__((always_inline)) {
+    if constexpr (!UPPER) {
+      const int c = tid % kChunksPerGroup;
+      float f[4];
+      Act<T>::cvt(o.x, chunk_parity(c), f);
+      float4 v[4];
+      chunk_entries(f, v);
+      float4 *dst = reinterpret_cast<float4 *>(sm.lut[buf] + (tid / kChunksPerGroup) * kRGroupStride +
+                                               r_chunk_offset(c));
+      dst[0] = v[0];
+      dst[1] = v[1];
+      dst[2] = v[2];
+      dst[3] = v[3];
+      const float cs = sum8_lanes((f[0] + f[1]) + (f[2] + f[3]));
+      if ((tid & 7) == 0) sm.gsum[buf][tid / kChunksPerGroup][(tid / 8) % 4] = cs;
+      if (stager) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.scl[buf][sa][srow][4 * sq + e] = o.sc[e];
+      }
+    }
+  };
+  float acc = 0.f;
+  auto consume = [&](int w, const Slot &o, int buf) __attribute__((always_inline)) {
+    const int j = w * kG1Ksub + gw;
+    if (j < G) {
+      const uint32_t base = lds_addr(sm.lut[buf] + gw * kRGroupStride + r_chunk_offset(16 * half));
+#pragma unroll
+      for (int u = 0; u < NP; ++u)
+        acc = fmaf(raw_to_float<T>(sm.scl[buf][I0 + u][r][gw]), r_half_sum(o.bits[u], base), acc);
+      if (!UPPER && half == 0) {
+        const float *gs = sm.gsum[buf][gw];
+        acc = fmaf(raw_to_float<T>(sm.scl[buf][P][r][gw]), (gs[0] + gs[1]) + (gs[2] + gs[3]), acc);
+      }
+    }
+  };
+
+  Slot ring[kStreamRing];
+  fetch_small(0, ring[0]);
+  fetch_small(1, ring[1]);
+  fetch_bits(0, ring[0]);
+  build(ring[0], 0);
+  fetch_bits(1, ring[1]);
+#pragma unroll
+  for (int k = 2; k < kStreamRing; ++k) fetch(k, ring[k]);
+  for (int w0 = 0; w0 < nwin; w0 += kStreamRing) {
+#pragma unroll
+    for (int k = 0; k < kStreamRing; ++k) {
+      const int w = w0 + k;
+      __syncthreads();
+      if (w + 1 < nwin) build(ring[(k + 1) % kStreamRing], (w + 1) & 1);  // uniform
+      if (w < nwin) consume(w, ring[k], w & 1);                            // uniform
+      fetch(w + kStreamRing, ring[k]);
+    }
+  }
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  if (lane < 16) sm.part[(UPPER ? kRWaves : 0) + wave][lane] = acc;
+}
+
+template <typename T, int P>
+__global__ __launch_bounds__(2 * kRThreads) void gemv_stream2_kernel(
+    const uint4 *__restrict__ bits, const T *__restrict__ alpha, const T *__restrict__ zero,
+    const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT) {
+  __shared__ StreamShared<T, P> sm;
+  const int tid = threadIdx.x;
+  if (tid < kRThreads)
+    stream_half<T, P, false>(sm, bits, alpha, zero, x, M, G, MT, tid);
+  else
+    stream_half<T, P, true>(sm, bits, alpha, zero, x, M, G, MT, tid - kRThreads);
+  // ---- reduce the 64 slot partials of each row in a fixed order
+  __syncthreads();
+  if (tid < kTileRows) {
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 2 * kRWaves; ++v) sum += sm.part[v][tid];
+    const int mm = blockIdx.x * kTileRows + tid;
+    if (mm < M) y[mm] = (T)sum;
+  }
+}
+
 int compute_units() {
   static int n = 0;
   if (n == 0) {
@@ -614,19 +762,22 @@ hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *
     return hipGetLastError();
   }
   // larger K: one tile per workgroup, tables streamed window by window
-  dim3 grid(MT), block(kRThreads);
+  dim3 grid(MT), block(kRThreads), block2(2 * kRThreads);
   switch (p) {
     case 1:
       hipLaunchKernelGGL((gemv_stream_kernel<T, 1>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT);
       break;
     case 2:
-      hipLaunchKernelGGL((gemv_stream_kernel<T, 2>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT);
+      hipLaunchKernelGGL((gemv_stream2_kernel<T, 2>), grid, block2, 0, s, b4, a, z, xx, yy, M, G,
+                         MT);
       break;
     case 3:
-      hipLaunchKernelGGL((gemv_stream_kernel<T, 3>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT);
+      hipLaunchKernelGGL((gemv_stream2_kernel<T, 3>), grid, block2, 0, s, b4, a, z, xx, yy, M, G,
+                         MT);
       break;
     default:
-      hipLaunchKernelGGL((gemv_stream_kernel<T, 4>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT);
+      hipLaunchKernelGGL((gemv_stream2_kernel<T, 4>), grid, block2, 0, s, b4, a, z, xx, yy, M, G,
+                         MT);
       break;
   }
   return hipGetLastError();

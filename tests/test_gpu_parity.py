@@ -156,6 +156,9 @@ def test_config1_tiny_fp32():
     # two windows, several row tiles per workgroup, and a last round of tiles
     # that only some workgroups take
     (4100, 3968, 4, np.float16), (9000, 2560, 3, np.float32),
+    # streamed windows with three planes (split 2 + 1 between the halves of
+    # the workgroup) and a last window of one group
+    (40, 8320, 3, np.float16), (300, 6272, 3, np.float32),
 ])
 def test_gemv_ragged_and_windowed_shapes(M, K, P, dt):
     """Ragged row tiles, partial K windows, more windows than one prefetch batch."""
