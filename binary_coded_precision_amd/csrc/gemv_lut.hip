@@ -328,7 +328,14 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   // tile 0's sign words after the scales (the barrier below waits for those);
   // later tiles' are requested after the barrier, one ahead of the tile being
   // looked up, so the small loads the barrier waits for are not queued behind
-  // every tile's sign words
+  // every tile's sign words.  A short sleep first (about 0.4 us) lets the
+  // activation and scale requests of workgroups that start later reach
+  // memory before this one's sign words: workgroups start over about 0.6 us,
+  // and without it their small loads queue behind the early ones' bulk
+  // (measured 4096x4096: 5.60 -> 5.31 us at p = 4; 8192x4096: 7.72 -> 7.35;
+  // 14336x4096 within noise).  No sleep at all and requesting the sign words
+  // only after the table barrier were both slower.
+  __builtin_amdgcn_s_sleep(12);
   fetch(0, tiles[0]);
 
   // ---- build the tables and group sums
