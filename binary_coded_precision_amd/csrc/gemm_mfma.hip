@@ -413,10 +413,77 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(const float *__res
 // wavefront order (deterministic).  The next tile's sign words and scales are
 // requested while the current one computes.
 constexpr int kWkWaves = 8;
+// compute units of an MI355X (fixed, not queried: workspace sizes follow from it)
+constexpr int kMfSlots = 256;
 constexpr int kWkMaxGroups = kWkWaves * kMfGroups;  // 32 groups: K <= 4096
 
 __device__ __forceinline__ int wk_slot(int q, int g, int n) {
   return ((q * kWkMaxGroups + g) << 4) + (n ^ (q & 15));
+}
+
+// One step of lane (r, h): its group's four sign words per plane against the
+// staged activations of group slot gs (the four lanes h of a row take four
+// groups), per-plane MFMAs plus the offset MFMA into acc.  rq is the staged
+// request row this lane reads as its B operand.
+template <int P>
+__device__ __forceinline__ void wk_step(floatx4 (&acc)[P + 1], const MfW<P> &o, const u32x4 *xs,
+                                        int rq, int gs) {
+  uint32_t wp[P][4], mag[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const uint32_t a16 = o.a[i];
+    const uint32_t neg = (uint32_t)((int32_t)(a16 << 16) >> 31);
+    mag[i] = (a16 & 0x7FFFu) * 0x10001u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wp[i][q] = ~(o.bits[i][q] ^ neg);
+  }
+  const uint32_t z2 = o.z * 0x10001u;
+  const half8 az = __builtin_bit_cast(half8, u32x4{z2, z2, z2, z2});
+#pragma unroll
+  for (int n = 0; n < kMfBlocks; ++n) {
+    const int q = n >> 2;
+    const int u = n & 3;
+    const half8 bop = __builtin_bit_cast(half8, xs[wk_slot(rq, gs, n)]);
+#pragma unroll
+    for (int i = 0; i < P; i += 2) {
+      u32x4 av, bv;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        int sh = 15 - (4 * u + v);
+        if (i + 1 < P) {
+          asm("" : "+s"(sh));
+          const uint64_t w2 = ((uint64_t)wp[i + 1][q] << 32 | wp[i][q]) << sh;
+          av[v] = ((uint32_t)w2 & 0x80008000u) | mag[i];
+          bv[v] = ((uint32_t)(w2 >> 32) & 0x80008000u) | mag[i + 1];
+        } else {
+          av[v] = ((wp[i][q] << sh) & 0x80008000u) | mag[i];
+        }
+      }
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), bop, acc[i],
+                                                      0, 0, 0);
+      if (i + 1 < P)
+        acc[i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, bv), bop,
+                                                            acc[i + 1], 0, 0, 0);
+    }
+    acc[P] = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bop, acc[P], 0, 0, 0);
+  }
+}
+
+// The offset, then the planes request r uses (all P unless precisions differ).
+template <int P, bool MIXED>
+__device__ __forceinline__ floatx4 wk_sum(const floatx4 (&acc)[P + 1], const MfPrec &prec,
+                                          int r) {
+  floatx4 d = acc[P];
+  if constexpr (MIXED) {
+    const int pn = prec.p[r];
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      if (i < pn) d += acc[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < P; ++i) d += acc[i];
+  }
+  return d;
 }
 
 template <int P, bool MIXED>
@@ -483,57 +550,9 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
     floatx4 acc[P + 1];
 #pragma unroll
     for (int i = 0; i <= P; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-    uint32_t wp[P][4], mag[P];
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const uint32_t a16 = o.a[i];
-      const uint32_t neg = (uint32_t)((int32_t)(a16 << 16) >> 31);
-      mag[i] = (a16 & 0x7FFFu) * 0x10001u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) wp[i][q] = ~(o.bits[i][q] ^ neg);
-    }
-    const uint32_t z2 = o.z * 0x10001u;
-    const half8 az = __builtin_bit_cast(half8, u32x4{z2, z2, z2, z2});
-#pragma unroll
-    for (int n = 0; n < kMfBlocks; ++n) {
-      const int q = n >> 2;
-      const int u = n & 3;
-      const half8 bop = __builtin_bit_cast(half8, xs[wk_slot(r, g, n)]);
-#pragma unroll
-      for (int i = 0; i < P; i += 2) {
-        u32x4 av, bv;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          int sh = 15 - (4 * u + v);
-          if (i + 1 < P) {
-            asm("" : "+s"(sh));
-            const uint64_t w2 = ((uint64_t)wp[i + 1][q] << 32 | wp[i][q]) << sh;
-            av[v] = ((uint32_t)w2 & 0x80008000u) | mag[i];
-            bv[v] = ((uint32_t)(w2 >> 32) & 0x80008000u) | mag[i + 1];
-          } else {
-            av[v] = ((wp[i][q] << sh) & 0x80008000u) | mag[i];
-          }
-        }
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), bop,
-                                                        acc[i], 0, 0, 0);
-        if (i + 1 < P)
-          acc[i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, bv), bop,
-                                                              acc[i + 1], 0, 0, 0);
-      }
-      acc[P] = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bop, acc[P], 0, 0, 0);
-    }
-    // D layout: lane (c, h) holds rows 4h .. 4h+3 for request c; the offset,
-    // then the planes request c uses (all P unless precisions differ)
-    floatx4 d = acc[P];
-    if constexpr (MIXED) {
-      const int pn = prec.p[r];
-#pragma unroll
-      for (int i = 0; i < P; ++i)
-        if (i < pn) d += acc[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < P; ++i) d += acc[i];
-    }
+    wk_step<P>(acc, o, xs, r, g);
+    // D layout: lane (c, h) holds rows 4h .. 4h+3 for request c
+    const floatx4 d = wk_sum<P, MIXED>(acc, prec, r);
     red[wave][lane] = d;
     __syncthreads();
     if (tid < 64 * 4) {
@@ -584,7 +603,6 @@ bool use_wk(int M, int K, int n) {
 // partial-sum traffic) among equals.  The count is MI355X's, fixed rather than
 // queried, because the workspace size follows from it and must not depend on
 // which device is current.
-constexpr int kMfSlots = 256;
 
 void mfma_split(int M, int K, int W, int *sps, int *slices) {
   const int G = K / kGroup;
