@@ -507,3 +507,86 @@ def test_fp32_large_batch_uses_exact_tables():
     ref = oracle_y(w, w.x, [2] * b)
     for r in range(b):
         assert rel_l2(Y[r].cpu().numpy(), ref[r]) <= 1e-5
+
+
+# ---------------------------------------------------------------- graphs and streams
+
+def test_graph_replays_match_eager():
+    """Every product kernel captured in one HIP graph (batch 1 whole-K and
+    streamed, whole-K and split matrix cores with their finalize, tables for
+    fp16 batch 2, per-request precision), replayed three times with new
+    activations written eagerly between replays; each replay must equal the
+    eager calls on the same inputs bit for bit (the kernels are deterministic)."""
+    import bench
+
+    cases = []
+    for M, K, b in [(3200, 2304, 1), (64, 8320, 1), (3200, 2304, 8), (3200, 2304, 32),
+                    (256, 8320, 2)]:
+        w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=M + K + b,
+                           p_choices=(2, 3, 4))
+        st = store_of(w)
+        X = dev(w.x)
+        Yg = torch.empty((b, M), dtype=torch.float16, device="cuda")
+        Ym = torch.empty((b, M), dtype=torch.float16, device="cuda")
+        ws = bcq.new_workspace(st, b)
+        cases.append((w, st, X, Yg, Ym, ws))
+
+    def body():
+        for w, st, X, Yg, Ym, ws in cases:
+            if w.b == 1:
+                bcq.bcq_gemv(st, 3, X[0], Yg[0])
+            else:
+                bcq.bcq_gemm_skinny(st, 4, X, Yg, workspace=ws)
+            bcq.bcq_gemv_mixed_p(st, w.p_req, X, Ym, workspace=ws)
+
+    say("graph capture", [c[0].M for c in cases])
+    g = bench.capture(torch, body)
+    rng = np.random.default_rng(5)
+    for rep in range(3):
+        for w, st, X, Yg, Ym, ws in cases:  # eager work between replays
+            X.copy_(torch.from_numpy(rng.standard_normal(w.x.shape).astype(np.float16)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [(Yg.clone(), Ym.clone()) for _, _, _, Yg, Ym, _ in cases]
+        body()  # the same calls, eagerly, on the same inputs
+        torch.cuda.synchronize()
+        for (w, st, X, Yg, Ym, ws), (gg, gm) in zip(cases, got):
+            assert torch.equal(gg, Yg), (rep, w.M, w.K, w.b)
+            assert torch.equal(gm, Ym), (rep, w.M, w.K, w.b, "mixed")
+
+
+def test_calls_on_two_streams_are_independent():
+    """Two stores on two streams at once, each stream running several calls in
+    a row; results equal the same calls run one after the other."""
+    ws_ = []
+    for M, K, b, seed in [(3200, 2304, 8, 1), (4096, 4096, 1, 2)]:
+        w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=seed)
+        ws_.append((w, store_of(w), dev(w.x)))
+    def run(stream, item, Y):
+        w, st, X = item
+        with torch.cuda.stream(stream):
+            for p in (2, 3, 4):
+                if w.b == 1:
+                    bcq.bcq_gemv(st, p, X[0], Y[p - 2][0], stream=stream)
+                else:
+                    bcq.bcq_gemm_skinny(st, p, X, Y[p - 2], stream=stream)
+    outs = []
+    for concurrent in (False, True):
+        Ys = [[torch.empty((w.b, w.M), dtype=torch.float16, device="cuda") for _ in range(3)]
+              for w, _, _ in ws_]
+        torch.cuda.synchronize()
+        if concurrent:
+            s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+            run(s1, ws_[0], Ys[0])
+            run(s2, ws_[1], Ys[1])
+        else:
+            s = torch.cuda.current_stream()
+            run(s, ws_[0], Ys[0])
+            run(s, ws_[1], Ys[1])
+        torch.cuda.synchronize()
+        outs.append(Ys)
+    say("two streams")
+    for a, b_ in zip(outs[0], outs[1]):
+        for ya, yb in zip(a, b_):
+            assert torch.equal(ya, yb)
