@@ -57,7 +57,8 @@ hipError_t launch_skinny_lut(const uint32_t *bits, int M, int K, int p_max, cons
 // nullptr for all p).  Per-request precisions need b <= kMfMaxMixed; otherwise
 // b <= kMfMaxBatch per launch (a call with more runs several launches in
 // order).  ws holds at least mfma_workspace_bytes(M, K, b) bytes for the call's
-// whole batch b.
+// whole batch b (nullptr when that is 0: launches that keep K within one
+// workgroup need none).
 constexpr int kMfMaxBatch = 64;
 constexpr int kMfMaxMixed = 32;
 hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const void *alpha,

@@ -1,6 +1,9 @@
-// gemm_mfma.hip -- BCQ product for 16 or more fp16 requests at one precision:
-// weights decoded to fp16 on the vector ALUs and contracted on the matrix
-// cores (v_mfma_f32_16x16x32_f16, fp32 accumulation).
+// gemm_mfma.hip -- BCQ product for batches of fp16 requests (from 3, or 2
+// where K stays within one workgroup): weights decoded to fp16 on the vector
+// ALUs and contracted on the matrix cores (v_mfma_f32_16x16x32_f16, fp32
+// accumulation).  Two kernels: one that splits K over workgroups (any batch
+// up to 64 per launch, partials summed by a finalize kernel) and one that
+// keeps K within a workgroup (up to 16 requests, K <= 4096), below.
 //
 // Why this path: past a few requests the product is a dense contraction of
 // the decoded weights with the requests' activations, so it belongs on the
