@@ -31,6 +31,8 @@
 //    sums per entry, see the section below.
 //  * Every reduction over lanes and wavefronts runs in a fixed order, so
 //    results are deterministic.
+#include <atomic>
+
 #include "bcq_internal.h"
 
 namespace bcq {
@@ -699,15 +701,20 @@ __global__ __launch_bounds__(2 * kRThreads) void gemv_stream2_kernel(
   }
 }
 
+// Compute units of the current device, cached per device (atomics: calls may
+// come from several host threads).  Only the grid size depends on it.
 int compute_units() {
-  static int n = 0;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
   if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
+    int v = 0;
+    n = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0
+            ? v
+            : 256;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
   return n;
 }
