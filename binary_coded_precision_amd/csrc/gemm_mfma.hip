@@ -35,17 +35,19 @@
 // four different groups, which is why the scale has to live in the A operand.
 //
 // Two ways to apply the scales.
-//  * Per plane (up to 32 requests): A = the plane's +-alpha pair per column,
+//  * Per plane (one tile of up to 16 requests, or up to 32 with per-request
+//    precisions): A = the plane's +-alpha pair per column,
 //    one bit-field insert per pair and plane (the shift is shared by two
 //    planes, see below), and one MFMA per plane plus one with A = (z, z) for
 //    the offset; the matrix cores do the sum over planes.  Each plane has its own
 //    accumulator, so requests of one launch may use different precisions
 //    (AnyBCQ notes, per-request precision): request r adds the accumulators of
 //    its first p_r planes only, all planes having been read once.
-//  * Summed (48 and 64 requests): the weight z + sum +-alpha is formed on the
-//    vector ALUs (a packed add per pair and plane on top of the decode) and
-//    one MFMA per request tile contracts it, since with four request tiles
-//    the per-plane MFMAs would outnumber the VALU work they save.
+//  * Summed (two or more request tiles at one precision): the weight
+//    z + sum +-alpha is formed on the vector ALUs (a packed add per pair and
+//    plane on top of the decode) and one MFMA per request tile contracts it,
+//    since from two request tiles the per-plane MFMAs cost more than the VALU
+//    work they save.
 //
 // Staging.  The four wavefronts (64 rows) share each step's activations in
 // LDS as [request][group][8-column block] 16-byte blocks, the block index
@@ -692,9 +694,16 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
   mfma_split(M, K, W, &sps, &S);
   float *w = S > 1 ? static_cast<float *>(ws) : nullptr;
   dim3 grid((MT + W - 1) / W, S), block(64 * W);
-#define BCQ_MF(NTV, PV)                                                                  \
-  hipLaunchKernelGGL((gemm_mfma_kernel<NTV, PV, (NTV >= 3), mf_waves(NTV)>), grid, block, 0, \
-                     s, b4, a, z, X, ldx, b, Y, ldy, w, M, G, MT, sps, prec)
+  // summed decode from two request tiles at one precision (measured 6-11%
+  // faster at 32 requests: half the MFMAs for one packed add per pair and
+  // plane); per-plane accumulators for one tile or per-request precisions
+#define BCQ_MF(NTV, PV)                                                                      \
+  if (NTV >= 3 || (NTV == 2 && p_req == nullptr))                                            \
+    hipLaunchKernelGGL((gemm_mfma_kernel<NTV, PV, true, mf_waves(NTV)>), grid, block, 0, s, b4, \
+                       a, z, X, ldx, b, Y, ldy, w, M, G, MT, sps, prec);                     \
+  else                                                                                       \
+    hipLaunchKernelGGL((gemm_mfma_kernel<NTV, PV, false, mf_waves(NTV)>), grid, block, 0, s,   \
+                       b4, a, z, X, ldx, b, Y, ldy, w, M, G, MT, sps, prec)
 #define BCQ_MF_NT(NTV)              \
   switch (p) {                      \
     case 1: BCQ_MF(NTV, 1); break;  \

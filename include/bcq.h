@@ -131,9 +131,10 @@ bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype 
  * sign-combination tables shared by up to 8 requests per launch (exact fp32
  * sums of the stored values).  Other fp16 batches of 2, and those of 3 and more,
  * decode tiles of W to fp16 once per launch of up to 64 requests and contract
- * them with X on the matrix cores (fp32 accumulation; up to 32 requests each
- * plane's +-alpha is an exact fp16 operand, from 48 the decoded weight
- * z + sum +-alpha is rounded to fp16).  Launches of up to 16 requests with
+ * them with X on the matrix cores (fp32 accumulation; in launches of up to 16
+ * requests, and in per-request-precision launches of up to 32, each plane's
+ * +-alpha is an exact fp16 operand; in larger launches at one precision the
+ * decoded weight z + sum +-alpha is rounded to fp16).  Launches of up to 16 requests with
  * 17..32 groups of K (K in 2176..4096) and at least 192 tiles of 16 rows
  * (M >= 3057) keep K within one workgroup; other launches split K over
  * workgroups and need
