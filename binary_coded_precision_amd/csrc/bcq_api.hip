@@ -12,16 +12,18 @@ using bcq::kGroup;
 constexpr int32_t kMaxM = 1 << 24;
 constexpr int32_t kMaxK = 1 << 20;
 // Smallest fp16 batch always sent to the matrix cores.  From 3 requests the
-// decoded tiles on the matrix cores beat the per-request table lookups at
-// every shape measured on gfx950 (4096x4096, 14336x4096, 4096x14336, p = 3
-// and 4).  At 2 they win only where K stays within one workgroup (4096x4096:
-// 7.5 vs 8.3 us); where K is split the table kernel is faster (4096x14336:
-// 20.0 vs 22.6 us).
+// decoded tiles on the matrix cores beat the per-request table lookups at the
+// layer shapes measured on gfx950 (1024..14336 rows, K 1024..14336, p = 3 and
+// 4); only tiny products lose about 1 us to the tables (256x1024 at 4
+// requests: 5.0 vs 4.0 us).  At 2 the matrix cores win where K stays within
+// one workgroup and is past 2048 columns (4096x4096: 7.5 vs 8.3 us;
+// 1024x4096: 5.9 vs 7.1 us); with K split, or K <= 2048, the table kernel is
+// faster (4096x14336: 20.0 vs 22.6 us; 2048x2048: 5.2 vs 6.1 us).
 constexpr int32_t kMfMinBatch = 3;
 
 bool on_matrix_cores(const bcq_store *st, int32_t b) {
   return st->scale_dtype == BCQ_F16 &&
-         (b >= kMfMinBatch || (b == 2 && bcq::mfma_whole_k(st->M, st->K, b)));
+         (b >= kMfMinBatch || (b == 2 && st->K > 2048 && bcq::mfma_whole_k(st->M, st->K, b)));
 }
 
 size_t dtype_size(bcq_dtype d) { return d == BCQ_F16 ? 2 : 4; }

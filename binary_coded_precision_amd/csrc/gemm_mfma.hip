@@ -590,13 +590,15 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
   if (k < nt) tile(k, wa);
 }
 
-// The whole-K kernel serves a launch when it has one request tile, K fits
-// its 32 groups with more than half of them used (below that the split
-// kernel's slices keep more of the chip busy), and there are enough row tiles
-// to give most compute units one.
+// The whole-K kernel serves a launch when it has one request tile and K fits
+// its 32 groups, except at 16 groups or fewer on more tiles than compute units
+// (there half its wavefronts idle on every tile and the split kernel wins).
+// Measured against the split kernel: 4096x4096 b = 16 10.2 -> 8.7 us,
+// 1024x4096 b = 4 7.7 -> 6.2 us, 4096x1024 b = 8 7.4 -> 5.6 us; 14336x2048
+// b = 16 16.1 -> 18.4 us.
 bool use_wk(int M, int K, int n) {
   const int G = K / kGroup;
-  return n <= 16 && G > kWkMaxGroups / 2 && G <= kWkMaxGroups && row_tiles(M) >= 192;
+  return n <= 16 && G <= kWkMaxGroups && (G > kWkMaxGroups / 2 || row_tiles(M) <= kMfSlots);
 }
 
 // Steps per slice and slice count for (M, K) and W wavefronts per workgroup.

@@ -127,17 +127,17 @@ bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype 
  * must be a multiple of 16 bytes; ldx >= K.  Y: [b][ldy], ldy >= M, element
  * aligned.  1 <= b <= BCQ_MAX_BATCH.
  * Batch 1 runs the batch-1 kernel.  fp32 batches, and fp16 batches of 2 unless
- * K stays within one workgroup (below), run on the vector ALUs with
- * sign-combination tables shared by up to 8 requests per launch (exact fp32
- * sums of the stored values).  Other fp16 batches of 2, and those of 3 and more,
+ * K is past 2048 and stays within one workgroup (below), run on the vector
+ * ALUs with sign-combination tables shared by up to 8 requests per launch
+ * (exact fp32 sums of the stored values).  Other fp16 batches of 2, and those
+ * of 3 and more,
  * decode tiles of W to fp16 once per launch of up to 64 requests and contract
  * them with X on the matrix cores (fp32 accumulation; in launches of up to 16
  * requests, and in per-request-precision launches of up to 32, each plane's
  * +-alpha is an exact fp16 operand; in larger launches at one precision the
  * decoded weight z + sum +-alpha is rounded to fp16).  Launches of up to 16 requests with
- * 17..32 groups of K (K in 2176..4096) and at least 192 tiles of 16 rows
- * (M >= 3057) keep K within one workgroup; other launches split K over
- * workgroups and need
+ * K <= 4096 keep K within one workgroup, except K <= 2048 on more than 256
+ * tiles of 16 rows (M > 4096); other launches split K over workgroups and need
  * bcq_workspace_bytes(store, b) bytes of device workspace (4-byte aligned) for
  * the K slices' partial sums: contents need no initialisation and are
  * clobbered by the call, so calls that may run at the same time need separate
@@ -162,9 +162,10 @@ size_t bcq_workspace_bytes(const bcq_store *store, int32_t b);
  * precisions costs no extra plane traffic.  When every requested precision's
  * tables alias those of the largest one (one shared [P][M][G] scale array and
  * one offset array, as a shared store lays them out), fp16 batches that
- * bcq_gemm_skinny would send to the matrix cores (3 and more, or 2 where K
- * stays within one workgroup) run there in launches of up to 32: each plane
- * has its own accumulator and request r sums its first p_host[r] planes.  Otherwise the
+ * bcq_gemm_skinny would send to the matrix cores (3 and more, or 2 where K is
+ * past 2048 and stays within one workgroup) run there in launches of up to 32:
+ * each plane has its own accumulator and request r sums its first p_host[r]
+ * planes.  Otherwise the
  * table kernel runs launches of up to 8, giving each request zero scales for
  * planes past its precision.
  * p_host: [b] in HOST memory; every entry must lie in [1, planes], otherwise

@@ -114,13 +114,13 @@ E_ARG, E_UNS, E_ALN = bcq.BCQ_ERR_INVALID_ARG, bcq.BCQ_ERR_UNSUPPORTED, bcq.BCQ_
     (lambda: skinny(make_store(), ldx=260), E_ALN),  # 260 halves = 520 B, not a multiple of 16
     (lambda: skinny(make_store(), X=FAKE + 2), E_ALN),
     (lambda: skinny(make_store(), p=5), E_ARG),
-    # K split over workgroups needs a workspace: fewer than 192 row tiles, or
-    # more than 16 requests in a launch
-    (lambda: skinny(make_store(M=1024, K=4096), b=16), E_ARG),
-    (lambda: skinny(make_store(M=1024, K=4096), b=16, ws=FAKE, wsb=16), E_ARG),
-    (lambda: skinny(make_store(M=1024, K=4096), b=3), E_ARG),  # fp16 b >= 3: matrix cores
+    # K split over workgroups needs a workspace: K past 4096, or more than 16
+    # requests in a launch
+    (lambda: skinny(make_store(M=1024, K=8192), b=16), E_ARG),
+    (lambda: skinny(make_store(M=1024, K=8192), b=16, ws=FAKE, wsb=16), E_ARG),
+    (lambda: skinny(make_store(M=1024, K=8192), b=3), E_ARG),  # fp16 b >= 3: matrix cores
     (lambda: skinny(make_store(M=4096, K=4096), b=32), E_ARG),
-    (lambda: mixed(make_store(M=1024, K=4096), [2, 3, 4]), E_ARG),  # needs a workspace too
+    (lambda: mixed(make_store(M=1024, K=8192), [2, 3, 4]), E_ARG),  # needs a workspace too
     (lambda: mixed(make_store(M=4096, K=4096), [2, 3, 4] * 6), E_ARG),
     (lambda: mixed(make_store(), [2, 3, 0, 4]), E_ARG),
     (lambda: mixed(make_store(), [2, 3, 5, 4]), E_ARG),
@@ -152,8 +152,8 @@ def test_workspace_sizes():
     lib = bcq.load()
     ws = lambda st, b: lib.bcq_workspace_bytes(ctypes.byref(st), b)
     st = make_store(M=4096, K=4096)
-    # batch 1 and fp16 batch 2 use the table kernels, 3..16 requests on 256
-    # row tiles the whole-K matrix-core kernel: none of them needs a workspace
+    # batch 1 uses the table kernel, 2..16 requests the whole-K matrix-core
+    # kernel: none of them needs a workspace
     for b in (1, 2, 3, 16):
         assert ws(st, b) == 0, b
     # from 17 requests K is split over workgroups: one fp32 partial per (K
@@ -165,11 +165,16 @@ def test_workspace_sizes():
     # precisions) in order, reusing the workspace: the size covers the largest
     assert ws(st, 256) == max(need64, need32)
     assert ws(st, 80) == max(need64, need32)
-    # fewer row tiles than the chip has compute units: split K from 3 requests
-    small = make_store(M=1024, K=4096)
-    need3, need16 = ws(small, 3), ws(small, 16)
+    # up to 16 requests keep K <= 4096 within a workgroup at any row count
+    # (K <= 2048 only up to 256 row tiles); past that K is split from 3 requests
+    assert ws(make_store(M=1024, K=4096), 16) == 0
+    assert ws(make_store(M=4096, K=2048), 16) == 0
+    assert ws(make_store(M=14336, K=2048), 16) > 0
+    long_k = make_store(M=1024, K=8192)
+    need3, need16 = ws(long_k, 3), ws(long_k, 16)
     assert need3 > 0 and need3 % (3 * 1024 * 4) == 0
-    assert need16 > 0 and need16 % (16 * 1024 * 4) == 0 and need16 <= 8 * 16 * 1024 * 4
+    # at most one slice per 4-group step (16 steps here)
+    assert need16 > 0 and need16 % (16 * 1024 * 4) == 0 and need16 <= 16 * 16 * 1024 * 4
     f32 = make_store(M=4096, K=4096, dtype=bcq.BCQ_F32)
     assert lib.bcq_workspace_bytes(ctypes.byref(f32), 64) == 0  # fp32 uses the table path
     assert lib.bcq_workspace_bytes(None, 16) == 0

@@ -399,15 +399,18 @@ def test_mfma_ragged_rows_and_groups(b):
         assert rel_l2(got[r], ref[r]) <= 2e-3, (r, int(w.p_req[r]))
 
 
-@pytest.mark.parametrize("M,K", [(3100, 3712), (12375, 2304)])
+@pytest.mark.parametrize("M,K", [(3100, 3712), (12375, 2304), (40, 1280), (1000, 384),
+                                 (2000, 4096)])
 @pytest.mark.parametrize("b", [2, 3, 16])
 def test_mfma_whole_k_workgroups(M, K, b):
-    """Up to 16 requests with 17..32 groups and at least 192 row tiles: one
-    workgroup per row tile (or several, walked in turn), K split over its
-    wavefronts.  M = 3100 leaves a partial last tile; K = 3712 (29 groups)
-    leaves the last wavefront one group and three lanes' groups past K;
-    M = 12375 (774 tiles) gives workgroups 3 or 4 tiles, an odd count
-    included.  Every precision, then per-request precisions; no workspace."""
+    """Up to 16 requests with K <= 4096: one workgroup per row tile (or several,
+    walked in turn), K split over its wavefronts.  M = 3100 leaves a partial
+    last tile; K = 3712 (29 groups) leaves the last wavefront one group and
+    three lanes' groups past K; M = 12375 (774 tiles) gives workgroups 3 or 4
+    tiles, an odd count included; K = 1280 and 384 (10 and 3 groups) leave
+    most wavefronts without a group; M = 40 and 1000 give fewer workgroups
+    than compute units.  (At b = 2 the calls with K <= 2048 take the table
+    kernel.)  Every precision, then per-request precisions; no workspace."""
     w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=M + K + b, outlier_frac=0.01,
                        p_choices=(1, 2, 3, 4))
     st = store_of(w)
