@@ -593,3 +593,54 @@ def test_calls_on_two_streams_are_independent():
     for a, b_ in zip(outs[0], outs[1]):
         for ya, yb in zip(a, b_):
             assert torch.equal(ya, yb)
+
+
+def test_random_shapes_every_path():
+    """36 seeded random problems across the dispatch boundaries (batch 1
+    resident and streamed, tables, whole-K and split matrix cores, launches
+    chunked past 64 or 32 requests, fp16 and fp32): each product, and the
+    per-request-precision call for batches, against the oracle.
+
+    With fewer than 16 rows a request's output vector has so few elements
+    that one near-cancelling output (terms of 0.03 summing to 0.008) makes its
+    relative error meaningless: the summed decode's fp16 weights carry about
+    5e-4 of each weight's size, not of the output's.  Those calls are checked
+    over the whole output matrix (all requests' rows as one vector)."""
+
+    def check(got, ref, what):
+        if got.shape[1] < 16:
+            assert rel_l2(got.ravel(), ref.ravel()) <= tol, what
+        else:
+            for r in range(got.shape[0]):
+                assert rel_l2(got[r], ref[r]) <= tol, what + (r,)
+
+    rng = np.random.default_rng(20261203)
+    for case in range(36):
+        M = int(rng.choice([1, 15, 16, 17, 100, 300, 1000, 3100]))
+        G = int(rng.choice([1, 3, 16, 17, 32, 33, 40]))
+        K = 128 * G
+        P = int(rng.integers(1, 5))
+        b = int(rng.choice([1, 2, 3, 5, 16, 17, 33, 65]))
+        dt = np.float16 if rng.random() < 0.75 else np.float32
+        if M * K * b > 60_000_000:  # keep the oracle to a second or so
+            b = 3
+        p = int(rng.integers(1, P + 1))
+        w = bcq_synth.make(M, K, P, b=b, dtype=dt, seed=case + 1000, outlier_frac=0.01,
+                           p_choices=tuple(range(1, P + 1)))
+        st = store_of(w)
+        tdt = torch.float16 if dt == np.float16 else torch.float32
+        tol = TOL[np.dtype(dt)]
+        rows = sample_rows(M, 64) if M > 64 else np.arange(M)
+        say("random", case, M, K, P, b, np.dtype(dt).name, p)
+        Y = torch.empty((b, M), dtype=tdt, device="cuda")
+        if b == 1:
+            bcq.bcq_gemv(st, p, dev(w.x[0]), Y[0])
+        else:
+            bcq.bcq_gemm_skinny(st, p, dev(w.x), Y)
+        ref = oracle_y(w, w.x, [p] * b, rows)
+        check(Y.cpu().numpy()[:, rows], np.asarray(ref), (case, M, K, P, b, p))
+        if b > 1:
+            Y = torch.empty((b, M), dtype=tdt, device="cuda")
+            bcq.bcq_gemv_mixed_p(st, w.p_req, dev(w.x), Y)
+            ref = oracle_y(w, w.x, w.p_req, rows)
+            check(Y.cpu().numpy()[:, rows], np.asarray(ref), (case, "mixed"))
