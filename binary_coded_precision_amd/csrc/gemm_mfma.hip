@@ -74,6 +74,7 @@ using half_t = _Float16;
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 // 16-byte blocks as a native vector (HIP's uint4 struct is copied with memcpy,
 // which keeps staging arrays from being promoted to registers)
@@ -118,7 +119,7 @@ struct MfW {
 };
 
 template <bool SUM, int P>
-constexpr int mf_accs() { return SUM ? 4 : P + 1; }
+constexpr int mf_accs() { return SUM ? 1 : P + 1; }
 
 // Precision of each request of a launch (1..P planes), passed by value.
 struct MfPrec {
@@ -211,20 +212,20 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
     }
     const uint32_t z2 = o.z * 0x10001u;
     const u32x4 *xb = xs[buf];
-#pragma unroll
-    for (int n = 0; n < kMfBlocks; ++n) {
-      const int q = n >> 2;
-      const int u = n & 3;
-      half8 bop[NT];
+    auto read_b = [&](int n, half8 (&bo)[NT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        bop[nt] = __builtin_bit_cast(half8, xb[mf_slot(nt * 16 + r, h, n)]);
-      if constexpr (SUM) {
+        bo[nt] = __builtin_bit_cast(half8, xb[mf_slot(nt * 16 + r, h, n)]);
+    };
+    if constexpr (SUM) {
+      // weights of block n: z + sum +-alpha per column, planes added in order;
+      // planes i and i+1 share one 64-bit shift, as in the per-plane branch
+      auto decode = [&](int n) __attribute__((always_inline)) -> half8 {
+        const int q = n >> 2;
+        const int u = n & 3;
         half2v w[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) w[v] = as_h2(z2);
-        // planes added in order; planes i and i+1 share one 64-bit shift, as
-        // in the per-plane branch below
 #pragma unroll
         for (int i = 0; i < P; i += 2)
 #pragma unroll
@@ -245,10 +246,38 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
           a[2 * v] = w[v][0];
           a[2 * v + 1] = w[v][1];
         }
+        return a;
+      };
+      // software pipeline: block n+1's activations are read and its weights
+      // decoded before block n's products are issued, so the LDS latency and
+      // the matrix-core work overlap the decode (the compiler otherwise reads
+      // each operand just before its product and waits for it there)
+      half8 bc[NT], bn[NT];
+      read_b(0, bc);
+      half8 ac = decode(0);
+#pragma unroll
+      for (int n = 0; n < kMfBlocks; ++n) {
+        half8 an;
+        if (n + 1 < kMfBlocks) {
+          read_b(n + 1, bn);
+          an = decode(n + 1);
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          acc[nt][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop[nt], acc[nt][u], 0, 0, 0);
-      } else {
+          acc[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac, bc[nt], acc[nt][0], 0, 0, 0);
+        if (n + 1 < kMfBlocks) {
+          ac = an;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) bc[nt] = bn[nt];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < kMfBlocks; ++n) {
+        const int q = n >> 2;
+        const int u = n & 3;
+        half8 bop[NT];
+        read_b(n, bop);
 #pragma unroll
         for (int i = 0; i < P; i += 2) {
           // planes i and i+1 share one 64-bit shift: the high word's bits
@@ -354,6 +383,8 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
   if (s < s1) compute(wa, 0);
 
   // D layout: lane (r, h) holds rows 4h .. 4h+3 of the tile for request r of each tile
+  const bool vec_ws = (M & 3) == 0 && (reinterpret_cast<uintptr_t>(ws) & 15) == 0;
+  const bool vec_y = (M & 3) == 0 && (ldy & 3) == 0 && (reinterpret_cast<uintptr_t>(Y) & 7) == 0;
   if (t < MT) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -361,7 +392,7 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
       if (n >= b) continue;
       floatx4 d;
       if constexpr (SUM) {  // one precision per launch
-        d = (acc[nt][0] + acc[nt][1]) + (acc[nt][2] + acc[nt][3]);
+        d = acc[nt][0];
       } else {  // the offset, then the planes this request uses
         const int pn = prec.p[n];
         d = acc[nt][P];
@@ -369,14 +400,24 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
         for (int i = 0; i < P; ++i)
           if (i < pn) d += acc[nt][i];
       }
+      // the four rows are consecutive: one 16-byte (partials) or 8-byte
+      // (outputs) store where the row length and the buffer allow it
+      const int mm0 = t * kTileRows + 4 * h;
+      if (ws != nullptr && vec_ws && mm0 < M) {
+        *reinterpret_cast<floatx4 *>(ws + ((size_t)sl * b + n) * M + mm0) = d;
+      } else if (ws == nullptr && vec_y && mm0 < M) {
+        *reinterpret_cast<half4v *>(Y + (size_t)n * ldy + mm0) =
+            half4v{(half_t)d[0], (half_t)d[1], (half_t)d[2], (half_t)d[3]};
+      } else {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int mm = t * kTileRows + 4 * h + v;
-        if (mm >= M) continue;
-        if (ws == nullptr)
-          Y[(size_t)n * ldy + mm] = (half_t)d[v];
-        else
-          ws[((size_t)sl * b + n) * M + mm] = d[v];
+        for (int v = 0; v < 4; ++v) {
+          const int mm = mm0 + v;
+          if (mm >= M) continue;
+          if (ws == nullptr)
+            Y[(size_t)n * ldy + mm] = (half_t)d[v];
+          else
+            ws[((size_t)sl * b + n) * M + mm] = d[v];
+        }
       }
     }
   }
@@ -384,24 +425,52 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
 
 // Y[n][m] = sum over slices of the partial products, in slice order.  The
 // partials of one output are loaded eight at a time so their latencies overlap.
+// VEC (M a multiple of 4, workspace 16-byte aligned): each thread sums four
+// consecutive outputs of one request with 16-byte loads, and stores them as
+// one 8-byte store when Y's rows allow (vec_y).
+template <bool VEC>
 __global__ __launch_bounds__(256) void splitk_finalize_kernel(const float *__restrict__ ws,
                                                               int slices, int b, int M,
-                                                              half_t *__restrict__ Y, int ldy) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)b * M) return;
-  const int n = (int)(idx / M);
-  const int mm = (int)(idx % M);
+                                                              half_t *__restrict__ Y, int ldy,
+                                                              int vec_y) {
+  constexpr int E = VEC ? 4 : 1;  // outputs per thread
+  const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * E;
+  if (e0 >= (size_t)b * M) return;
+  const int n = (int)(e0 / M);
+  const int mm = (int)(e0 % M);
   const size_t stride = (size_t)b * M;
-  const float *pp = ws + idx;
-  float s = 0.f;
+  const float *pp = ws + e0;
+  float s[E];
+#pragma unroll
+  for (int c = 0; c < E; ++c) s[c] = 0.f;
   for (int q0 = 0; q0 < slices; q0 += 8) {
-    float v[8];
+    float v[8][E];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = q0 + k < slices ? pp[(size_t)(q0 + k) * stride] : 0.f;
+    for (int k = 0; k < 8; ++k) {
+      if constexpr (VEC) {
+        const floatx4 f = q0 + k < slices
+                              ? *reinterpret_cast<const floatx4 *>(pp + (size_t)(q0 + k) * stride)
+                              : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s += v[k];
+        for (int c = 0; c < E; ++c) v[k][c] = f[c];
+      } else {
+        v[k][0] = q0 + k < slices ? pp[(size_t)(q0 + k) * stride] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int c = 0; c < E; ++c) s[c] += v[k][c];
   }
-  Y[(size_t)n * ldy + mm] = (half_t)s;
+  half_t *dst = Y + (size_t)n * ldy + mm;
+  if constexpr (VEC) {
+    if (vec_y) {
+      *reinterpret_cast<half4v *>(dst) = half4v{(half_t)s[0], (half_t)s[1], (half_t)s[2], (half_t)s[3]};
+      return;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < E; ++c) dst[c] = (half_t)s[c];
 }
 
 // ---------------------------------------------------------------- whole K
@@ -726,8 +795,13 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || w == nullptr) return e;
   const size_t n = (size_t)b * M;
-  hipLaunchKernelGGL(splitk_finalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     w, S, b, M, Y, ldy);
+  const int vec_y = M % 4 == 0 && ldy % 4 == 0 && reinterpret_cast<uintptr_t>(Y) % 8 == 0;
+  if (M % 4 == 0 && reinterpret_cast<uintptr_t>(w) % 16 == 0)
+    hipLaunchKernelGGL(splitk_finalize_kernel<true>, dim3((unsigned)((n / 4 + 255) / 256)),
+                       dim3(256), 0, s, w, S, b, M, Y, ldy, vec_y);
+  else
+    hipLaunchKernelGGL(splitk_finalize_kernel<false>, dim3((unsigned)((n + 255) / 256)),
+                       dim3(256), 0, s, w, S, b, M, Y, ldy, 0);
   return hipGetLastError();
 }
 
