@@ -706,6 +706,49 @@ size_t launch_workspace_bytes(int M, int K, int n) {
   return s > 1 ? (size_t)s * n * M * sizeof(float) : 0;
 }
 
+// Arguments of one split-kernel launch.
+struct MfArgs {
+  const u32x4 *bits;
+  const half_t *alpha, *zero, *X;
+  int ldx, b;
+  half_t *Y;
+  int ldy;
+  float *ws;
+  int M, G, MT, sps;
+  MfPrec prec;
+};
+
+// Instantiates only the variants the dispatch can reach: the per-plane form
+// for one or two request tiles, the summed form from two.
+template <int NTV, int PV>
+void launch_mf(bool sum, dim3 grid, hipStream_t s, const MfArgs &g) {
+  constexpr int W = mf_waves(NTV);
+  if constexpr (NTV >= 2) {
+    if (sum) {
+      hipLaunchKernelGGL((gemm_mfma_kernel<NTV, PV, true, W>), grid, dim3(64 * W), 0, s, g.bits,
+                         g.alpha, g.zero, g.X, g.ldx, g.b, g.Y, g.ldy, g.ws, g.M, g.G, g.MT, g.sps,
+                         g.prec);
+      return;
+    }
+  }
+  if constexpr (NTV <= 2)
+    hipLaunchKernelGGL((gemm_mfma_kernel<NTV, PV, false, W>), grid, dim3(64 * W), 0, s, g.bits,
+                       g.alpha, g.zero, g.X, g.ldx, g.b, g.Y, g.ldy, g.ws, g.M, g.G, g.MT, g.sps,
+                       g.prec);
+}
+
+template <int PV>
+void launch_mf_nt(int NT, bool sum, dim3 grid, hipStream_t s, const MfArgs &g) {
+  if (NT <= 1)
+    launch_mf<1, PV>(sum, grid, s, g);
+  else if (NT == 2)
+    launch_mf<2, PV>(sum, grid, s, g);
+  else if (NT == 3)
+    launch_mf<3, PV>(sum, grid, s, g);
+  else
+    launch_mf<4, PV>(sum, grid, s, g);
+}
+
 }  // namespace
 
 bool mfma_whole_k(int M, int K, int n) { return use_wk(M, K, n); }
@@ -764,34 +807,18 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
   int sps, S;
   mfma_split(M, K, W, &sps, &S);
   float *w = S > 1 ? static_cast<float *>(ws) : nullptr;
-  dim3 grid((MT + W - 1) / W, S), block(64 * W);
   // summed decode from two request tiles at one precision (measured 6-11%
   // faster at 32 requests: half the MFMAs for one packed add per pair and
   // plane); per-plane accumulators for one tile or per-request precisions
-#define BCQ_MF(NTV, PV)                                                                      \
-  if (NTV >= 3 || (NTV == 2 && p_req == nullptr))                                            \
-    hipLaunchKernelGGL((gemm_mfma_kernel<NTV, PV, true, mf_waves(NTV)>), grid, block, 0, s, b4, \
-                       a, z, X, ldx, b, Y, ldy, w, M, G, MT, sps, prec);                     \
-  else                                                                                       \
-    hipLaunchKernelGGL((gemm_mfma_kernel<NTV, PV, false, mf_waves(NTV)>), grid, block, 0, s,   \
-                       b4, a, z, X, ldx, b, Y, ldy, w, M, G, MT, sps, prec)
-#define BCQ_MF_NT(NTV)              \
-  switch (p) {                      \
-    case 1: BCQ_MF(NTV, 1); break;  \
-    case 2: BCQ_MF(NTV, 2); break;  \
-    case 3: BCQ_MF(NTV, 3); break;  \
-    default: BCQ_MF(NTV, 4); break; \
+  const bool sum = NT >= 3 || (NT == 2 && p_req == nullptr);
+  const MfArgs args{b4, a, z, X, ldx, b, Y, ldy, w, M, G, MT, sps, prec};
+  dim3 grid((MT + W - 1) / W, S);
+  switch (p) {
+    case 1: launch_mf_nt<1>(NT, sum, grid, s, args); break;
+    case 2: launch_mf_nt<2>(NT, sum, grid, s, args); break;
+    case 3: launch_mf_nt<3>(NT, sum, grid, s, args); break;
+    default: launch_mf_nt<4>(NT, sum, grid, s, args); break;
   }
-  if (NT <= 1)
-    BCQ_MF_NT(1)
-  else if (NT == 2)
-    BCQ_MF_NT(2)
-  else if (NT == 3)
-    BCQ_MF_NT(3)
-  else
-    BCQ_MF_NT(4)
-#undef BCQ_MF_NT
-#undef BCQ_MF
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || w == nullptr) return e;
   const size_t n = (size_t)b * M;
