@@ -417,14 +417,15 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
 // window w is done with its ring slot, so kStreamRing windows of loads are in
 // flight; every path issues the same loads (a window past the end re-reads the
 // last one) and the loop's only exit is its header, so the waits stay
-// partial.  Before the first build only the activations and scales of the
-// first two windows and the first window's sign words are requested; queued
-// behind all four windows' sign words of every workgroup, the loads the first
-// build waits for arrived late (measured: the first window took 7 us).
-// Scales are staged through LDS with row-contiguous loads, as in
+// partial.  Two windows in flight measured faster than four at every
+// streaming shape tried (p = 4: 4096x14336 16.1 -> 14.1 us, 4096x8192 11.6 ->
+// 10.1, 14336x8192 39.4 -> 34.2, 12288x6144 23.4 -> 20.0); three, six and
+// eight were slower than four.  Before the first build only the activations
+// and scales of the first two windows and the first window's sign words are
+// requested.  Scales are staged through LDS with row-contiguous loads, as in
 // gemv_res_kernel.  A group's activation sum is kept as four 8-chunk partials
 // (DPP within 8 lanes, no LDS round trips) that the lookup adds in order.
-constexpr int kStreamRing = 4;  // windows of loads in flight
+constexpr int kStreamRing = 2;  // windows of loads in flight
 
 template <typename T, int P>
 struct StreamSlot {
