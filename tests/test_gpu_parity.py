@@ -433,6 +433,32 @@ def test_mfma_whole_k_workgroups(M, K, b):
         assert rel_l2(got[r], ref[r]) <= 2e-3, (r, int(w.p_req[r]))
 
 
+@pytest.mark.parametrize("M,K,b", [(264, 8192, 40), (4096, 512, 40), (258, 8192, 20)])
+def test_split_stores_any_alignment(M, K, b):
+    """The split kernel and its finalize store four consecutive rows at once
+    only where the row length, the leading dimension and the buffer allow it.
+    Here the workspace starts 4 bytes past a 16-byte boundary and Y's rows are
+    M + 1 long, so every store takes the element-wise path; then the aligned
+    case with padded rows.  4096x512 is a single K slice (outputs written
+    straight from the main kernel), 258 rows a row count that is not a
+    multiple of 4.  Nothing may land past a row's M outputs."""
+    w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=M + K + b, outlier_frac=0.01)
+    st = store_of(w)
+    need = bcq.bcq_workspace_bytes(st, b)
+    rows = np.unique(np.concatenate([sample_rows(M, 96), np.arange(M - 8, M)]))
+    for ld, off in ((M + 1, 1), (M + 4, 0)):
+        ws_full = torch.empty(need // 4 + 8, dtype=torch.int32, device="cuda")
+        ws = ws_full[off:] if need else None
+        Yb = torch.full((b, ld), 7.0, dtype=torch.float16, device="cuda")
+        say("split stores", M, K, b, ld, off)
+        bcq.bcq_gemm_skinny(st, 4, dev(w.x), Yb[:, :M], workspace=ws)
+        ref = oracle_y(w, w.x, [4] * b, rows)
+        got = Yb[:, :M].cpu().numpy()[:, rows]
+        for r in range(b):
+            assert rel_l2(got[r], ref[r]) <= 2e-3, (ld, off, r)
+        assert (Yb[:, M:].float() == 7.0).all(), (ld, off)
+
+
 def test_mfma_workspace_reused_across_batch_sizes():
     # one workspace, sized for the largest batch and never cleared, reused in
     # stream order by calls whose launches use different workgroup sizes and
