@@ -329,8 +329,8 @@ def main():
                     help="with --counter-run: run bcq_gemm_skinny at batch B (p = 4) instead")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build's path runs on a single MI355X "
-              "(multi-GPU sharding is a design note, not built); use --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the BCQ product runs on a single MI355X "
+              "(sharding across GPUs is not implemented); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
