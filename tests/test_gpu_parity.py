@@ -670,3 +670,59 @@ def test_random_shapes_every_path():
             bcq.bcq_gemv_mixed_p(st, w.p_req, dev(w.x), Y)
             ref = oracle_y(w, w.x, w.p_req, rows)
             check(Y.cpu().numpy()[:, rows], np.asarray(ref), (case, "mixed"))
+
+
+def test_wide_random_sweep_with_padding_and_offsets():
+    """300 seeded problems up to 9000 rows, 64 groups and 80 requests, both
+    dtypes: each product and, for batches, the per-request-precision call,
+    with output rows of M, M + 1 or M + 4 (nothing may land in the padding)
+    and the workspace at a 16-byte boundary or 4 bytes past one.  Rows are
+    sampled (48 per call); below 16 sampled rows the error is taken over the
+    whole output matrix, as in test_random_shapes_every_path."""
+    rng = np.random.default_rng(20261204)
+
+    def check(got, ref, tol, what):
+        if got.shape[1] < 16:
+            assert rel_l2(got.ravel(), ref.ravel()) <= tol, what
+        else:
+            for r in range(got.shape[0]):
+                assert rel_l2(got[r], ref[r]) <= tol, what + (r,)
+
+    for case in range(300):
+        M = int(rng.choice([1, 7, 16, 33, 258, 1000, 3100, 4100, 5000, 9000]))
+        G = int(rng.choice([1, 2, 5, 16, 31, 32, 33, 40, 56, 64]))
+        K = 128 * G
+        P = int(rng.integers(1, 5))
+        p = int(rng.integers(1, P + 1))
+        b = int(rng.choice([1, 1, 2, 3, 4, 8, 15, 16, 17, 32, 33, 48, 64, 65, 80]))
+        dt = np.float16 if rng.random() < 0.8 else np.float32
+        while M * K * b > 200_000_000 and b > 1:
+            b //= 2
+        w = bcq_synth.make(M, K, P, b=b, dtype=dt, seed=50000 + case, outlier_frac=0.01,
+                           p_choices=tuple(range(1, P + 1)))
+        st = store_of(w)
+        tdt = torch.float16 if dt == np.float16 else torch.float32
+        tol = TOL[np.dtype(dt)]
+        ld = M + int(rng.choice([0, 1, 4]))
+        off = int(rng.integers(0, 2))
+        rows = np.unique(np.concatenate([rng.choice(M, size=min(M, 48), replace=False),
+                                         [0, M - 1]]))
+        say("wide", case, M, K, P, p, b, np.dtype(dt).name, ld, off)
+        need = bcq.bcq_workspace_bytes(st, b) if b > 1 else 0
+        ws = None
+        if need:
+            ws = torch.empty(need // 4 + 8, dtype=torch.int32, device="cuda")[off:]
+        Yb = torch.full((b, ld), 3.0, dtype=tdt, device="cuda")
+        if b == 1:
+            bcq.bcq_gemv(st, p, dev(w.x[0]), Yb[0, :M])
+        else:
+            bcq.bcq_gemm_skinny(st, p, dev(w.x), Yb[:, :M], workspace=ws)
+        ref = np.asarray(oracle_y(w, w.x, [p] * b, rows))
+        check(Yb[:, :M].cpu().numpy()[:, rows], ref, tol, (case,))
+        assert (Yb[:, M:].float() == 3.0).all(), case
+        if b > 1:
+            Yb = torch.full((b, ld), 3.0, dtype=tdt, device="cuda")
+            bcq.bcq_gemv_mixed_p(st, w.p_req, dev(w.x), Yb[:, :M], workspace=ws)
+            ref = np.asarray(oracle_y(w, w.x, w.p_req, rows))
+            check(Yb[:, :M].cpu().numpy()[:, rows], ref, tol, (case, "mixed"))
+            assert (Yb[:, M:].float() == 3.0).all(), (case, "mixed")
