@@ -482,10 +482,12 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(const float *__res
 // request's activations for all of K (at most 16 x 4096 fp16, 128 KB) are
 // staged once per workgroup in LDS with coalesced loads, laid out and
 // swizzled like the split kernel's stage, and serve every tile the workgroup
-// walks (tiles blockIdx.x + k * gridDim.x, grid = min(tiles, CUs)).  Per tile
-// the eight wavefronts' partial products meet in LDS and are summed in
-// wavefront order (deterministic).  The next tile's sign words and scales are
-// requested while the current one computes.
+// walks (tiles blockIdx.x + k * gridDim.x, grid = min(tiles, CUs)).  The
+// eight wavefronts' partial products of each tile meet in LDS and are summed
+// in wavefront order (deterministic), two tiles per pair of barriers (one pair
+// per tile measured 2-5% slower at 3-4 tiles per workgroup: 14336x4096, b = 4,
+// 15.0 -> 14.6 us).  The next tile's sign words and scales are requested while
+// the current one computes.
 constexpr int kWkWaves = 8;
 // compute units of an MI355X (fixed, not queried: workspace sizes follow from it)
 constexpr int kMfSlots = 256;
@@ -567,7 +569,7 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
     half_t *__restrict__ Y, int ldy, int M, int G, int MT, const MfPrec prec) {
   constexpr int kReq = 16;
   __shared__ u32x4 xs[kReq * kWkMaxGroups * kMfBlocks];  // 128 KB
-  __shared__ floatx4 red[kWkWaves][64];
+  __shared__ floatx4 red[2][kWkWaves][64];  // partial products of two tiles
   using OpsW = MfW<P>;
 
   const int tid = threadIdx.x;
@@ -626,17 +628,21 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
     for (int i = 0; i <= P; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     wk_step<P>(acc, o, xs, r, g);
     // D layout: lane (c, h) holds rows 4h .. 4h+3 for request c
-    const floatx4 d = wk_sum<P, MIXED>(acc, prec, r);
-    red[wave][lane] = d;
+    red[k & 1][wave][lane] = wk_sum<P, MIXED>(acc, prec, r);
+  };
+  // sum the eight wavefronts' partials of tiles k0 .. k0+n-1 (n = 1 or 2, k0
+  // even) in wavefront order and store them: one pair of barriers per two tiles
+  auto flush = [&](int k0, int n) __attribute__((always_inline)) {
     __syncthreads();
-    if (tid < 64 * 4) {
-      const int l = tid >> 2, v = tid & 3;
+    if (tid < 64 * 4 * n) {
+      const int kk = tid >> 8;
+      const int l = (tid >> 2) & 63, v = tid & 3;
       const int c = l & 15;
-      const int t = (int)blockIdx.x + k * (int)gridDim.x;
+      const int t = (int)blockIdx.x + (k0 + kk) * (int)gridDim.x;
       const int mm = t * kTileRows + 4 * (l >> 4) + v;
       float sum = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWkWaves; ++w) sum += red[w][l][v];
+      for (int w = 0; w < kWkWaves; ++w) sum += red[kk][w][l][v];
       if (c < b && mm < M) Y[(size_t)c * ldy + mm] = (half_t)sum;
     }
     __syncthreads();
@@ -655,8 +661,12 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
     __builtin_amdgcn_sched_barrier(0);
     tile(k + 1, wb);
     __builtin_amdgcn_sched_barrier(0);
+    flush(k, 2);
   }
-  if (k < nt) tile(k, wa);
+  if (k < nt) {
+    tile(k, wa);
+    flush(k, 1);
+  }
 }
 
 // The whole-K kernel serves a launch when it has one request tile and K fits
