@@ -49,7 +49,7 @@
 //    since from two request tiles the per-plane MFMAs cost more than the VALU
 //    work they save.
 //
-// Staging.  The four wavefronts (64 rows) share each step's activations in
+// Staging.  The eight wavefronts (128 rows) share each step's activations in
 // LDS as [request][group][8-column block] 16-byte blocks, the block index
 // XOR-swizzled by the request's low four bits: the 64 lanes writing one
 // request's 1 KB of a step land in distinct banks, and the 16 requests read at
