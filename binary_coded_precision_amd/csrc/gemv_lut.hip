@@ -255,7 +255,7 @@ __device__ __forceinline__ float r_half_sum(const uint2 bw, uint32_t base) {
 // 8w..8w+7 look up window w.  At K = 4096 that is four wavefronts per SIMD,
 // enough to hide the LDS latency of the lookups, and every lane builds one
 // chunk's table.
-template <typename T, int NW, int P, int TMAX>
+template <typename T, int NW, int P, int TMAX, int RS = 1>
 __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
     const uint4 *__restrict__ bits, const T *__restrict__ alpha, const T *__restrict__ zero,
     const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT) {
@@ -282,7 +282,17 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   const int hs = (wave % kRWaves) * 4 + (lane >> 4);  // half-group slot 0..31
   const int gw = hs >> 1;                              // group within the window
   const int half = hs & 1;
-  const int nt = (MT - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // my tiles
+  // RS > 1 (one tile per workgroup, few tiles): RS workgroups share tile
+  // blockIdx.x / RS, each taking 16 / RS of its rows; lane (r, hs) takes row
+  // r % (16 / RS) of that part and planes PC * (r / (16 / RS)) ..  + PC - 1,
+  // so the lookups of a tile spread over RS times as many compute units.
+  static_assert(RS == 1 || TMAX == 1, "row parts only for one tile per workgroup");
+  constexpr int kPartRows = kTileRows / RS;
+  constexpr int PC = (P + RS - 1) / RS;  // planes per lane
+  const int rl = r % kPartRows;          // row within the part
+  const int ph = r / kPartRows;          // plane part of this lane
+  const int prow = ((int)blockIdx.x % RS) * kPartRows + rl;  // row within the tile
+  const int nt = RS > 1 ? 1 : (MT - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const size_t plane_stride = (size_t)MT * G * kTileRows;  // in uint4
   const size_t MG = (size_t)M * G;
   const uint2 *bits2 = reinterpret_cast<const uint2 *>(bits);
@@ -310,8 +320,10 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   for (int u = 0; u < kPerThread; ++u) {
     const int n = min(u * kParts + spart, kPairs - 1);
     const int k = n / (P + 1), a = n % (P + 1);
-    const int row =
-        min(((int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x) * kTileRows + srow, M - 1);
+    const int row = min((RS > 1 ? (int)blockIdx.x / RS
+                                : (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x) *
+                                kTileRows + srow,
+                        M - 1);
     const T *src = a < P ? alpha + a * MG : zero;
     sv[u] = load_raw(src + (size_t)row * G + sgc);
   }
@@ -322,10 +334,18 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   uint2 tiles[2][P];
   const int js = min(win * kG1Ksub + gw, G - 1);
   auto fetch = [&](int k, uint2 (&o)[P]) {
-    const int t = (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x;
-    const size_t q = (((size_t)t * G + js) * kTileRows + r) * 2 + half;  // uint2 index
+    if constexpr (RS > 1) {
+      const int t = (int)blockIdx.x / RS;
+      const size_t q = (((size_t)t * G + js) * kTileRows + prow) * 2 + half;
 #pragma unroll
-    for (int i = 0; i < P; ++i) o[i] = bits2[i * plane_stride * 2 + q];
+      for (int u = 0; u < PC; ++u)
+        o[u] = bits2[(size_t)min(ph * PC + u, P - 1) * plane_stride * 2 + q];
+    } else {
+      const int t = (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x;
+      const size_t q = (((size_t)t * G + js) * kTileRows + r) * 2 + half;  // uint2 index
+#pragma unroll
+      for (int i = 0; i < P; ++i) o[i] = bits2[i * plane_stride * 2 + q];
+    }
   };
   // tile 0's sign words after the scales (the barrier below waits for those);
   // later tiles' are requested after the barrier, one ahead of the tile being
@@ -371,10 +391,21 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   auto consume = [&](int k, const uint2 (&o)[P]) -> float {
     float a = 0.f;
     if (j < G) {
+      if constexpr (RS > 1) {
+        // a plane index past P (P not a multiple of RS) looks up with scale 0
 #pragma unroll
-      for (int i = 0; i < P; ++i)
-        a = fmaf(raw_to_float<T>(scl[k][i][r][j]), r_half_sum(o[i], base), a);
-      if (half == 0) a = fmaf(raw_to_float<T>(scl[k][P][r][j]), gsum[j], a);
+        for (int u = 0; u < PC; ++u) {
+          const int i = ph * PC + u;
+          const float sc = i < P ? raw_to_float<T>(scl[k][min(i, P - 1)][prow][j]) : 0.f;
+          a = fmaf(sc, r_half_sum(o[u], base), a);
+        }
+        if (half == 0 && ph == 0) a = fmaf(raw_to_float<T>(scl[k][P][prow][j]), gsum[j], a);
+      } else {
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+          a = fmaf(raw_to_float<T>(scl[k][i][r][j]), r_half_sum(o[i], base), a);
+        if (half == 0) a = fmaf(raw_to_float<T>(scl[k][P][r][j]), gsum[j], a);
+      }
     }
     return a;
   };
@@ -392,17 +423,21 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   for (int k = 0; k < TMAX; ++k) {
     acc[k] += __shfl_xor(acc[k], 16);
     acc[k] += __shfl_xor(acc[k], 32);
+#pragma unroll
+    for (int m = kPartRows; m < kTileRows; m <<= 1) acc[k] += __shfl_xor(acc[k], m);  // plane parts
     if (lane < 16) part[wave][k][lane] = acc[k];
   }
   __syncthreads();
   if (tid < TMAX * kTileRows) {
     const int k = tid / kTileRows;
-    const int rr = tid % kTileRows;
-    const int mm = ((int)blockIdx.x + k * (int)gridDim.x) * kTileRows + rr;
+    const int rr = tid % kTileRows;  // lane rr holds row rr (RS = 1) or part row rr
+    const int mm = RS > 1 ? ((int)blockIdx.x / RS) * kTileRows +
+                                ((int)blockIdx.x % RS) * kPartRows + rr
+                          : ((int)blockIdx.x + k * (int)gridDim.x) * kTileRows + rr;
     float sum = 0.f;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) sum += part[v][k][rr];
-    if (k < nt && mm < M) y[mm] = (T)sum;
+    if (k < nt && rr < kPartRows && mm < M) y[mm] = (T)sum;
   }
 }
 
@@ -720,35 +755,43 @@ int compute_units() {
   return n;
 }
 
-template <typename T, int NW, int TMAX>
+template <typename T, int NW, int TMAX, int RS = 1>
 void gemv_res_launch(dim3 grid, hipStream_t s, const uint4 *b4, const T *a, const T *z,
                      const T *xx, T *yy, int M, int G, int MT, int p) {
   switch (p) {
     case 1:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 1, TMAX>), grid, dim3(kRThreads * NW), 0, s, b4, a,
-                         z, xx, yy, M, G, MT);
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 1, TMAX, RS>), grid, dim3(kRThreads * NW), 0, s,
+                         b4, a, z, xx, yy, M, G, MT);
       break;
     case 2:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 2, TMAX>), grid, dim3(kRThreads * NW), 0, s, b4, a,
-                         z, xx, yy, M, G, MT);
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 2, TMAX, RS>), grid, dim3(kRThreads * NW), 0, s,
+                         b4, a, z, xx, yy, M, G, MT);
       break;
     case 3:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 3, TMAX>), grid, dim3(kRThreads * NW), 0, s, b4, a,
-                         z, xx, yy, M, G, MT);
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 3, TMAX, RS>), grid, dim3(kRThreads * NW), 0, s,
+                         b4, a, z, xx, yy, M, G, MT);
       break;
     default:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 4, TMAX>), grid, dim3(kRThreads * NW), 0, s, b4, a,
-                         z, xx, yy, M, G, MT);
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 4, TMAX, RS>), grid, dim3(kRThreads * NW), 0, s,
+                         b4, a, z, xx, yy, M, G, MT);
       break;
   }
 }
 
+// At most one tile per compute unit: with a quarter (half) of the compute
+// units or fewer holding a tile, each tile's rows are split over 4 (2)
+// workgroups.  More tiles than compute units: tiles dealt round-robin, up to 4
+// per workgroup.
 template <typename T, int NW>
 void gemv_res_tiles(hipStream_t s, const uint4 *b4, const T *a, const T *z, const T *xx, T *yy,
                     int M, int G, int MT, int p) {
   const int cus = compute_units();
   const int tmax = (MT + cus - 1) / cus;
-  if (tmax <= 1)
+  if (4 * MT <= cus)
+    gemv_res_launch<T, NW, 1, 4>(dim3(MT * 4), s, b4, a, z, xx, yy, M, G, MT, p);
+  else if (2 * MT <= cus)
+    gemv_res_launch<T, NW, 1, 2>(dim3(MT * 2), s, b4, a, z, xx, yy, M, G, MT, p);
+  else if (tmax <= 1)
     gemv_res_launch<T, NW, 1>(dim3(MT), s, b4, a, z, xx, yy, M, G, MT, p);
   else if (tmax <= 2)
     gemv_res_launch<T, NW, 2>(dim3((MT + 1) / 2), s, b4, a, z, xx, yy, M, G, MT, p);
