@@ -54,10 +54,20 @@ def mixed_bytes(M: int, K: int, p_req, elem: int = 2, g: int = 128) -> int:
     return pmax * M * K // 8 + pmax * M * G * elem + M * G * elem + b * K * elem + b * M * elem
 
 
+def code_hash(text: str) -> str:
+    """Hash of C/HIP source with comments and whitespace removed."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
+
+
 def source_sha() -> str:
-    """Hash of the batch-1 kernel source (ties stored counter readings to a kernel version)."""
+    """Code hash of the batch-1 kernel source (ties stored counter readings to a
+    kernel version; comment edits keep it)."""
     path = os.path.join(ROOT, "binary_coded_precision_amd", "csrc", "gemv_lut.hip")
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    return code_hash(open(path, encoding="utf-8").read())
 
 
 def stored_traffic():

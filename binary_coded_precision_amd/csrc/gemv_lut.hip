@@ -190,7 +190,9 @@ constexpr int kG1ChunkStride = 80;  // bytes per chunk table: 16 entries + 16 B 
 // tiles (tile blockIdx.x + k * gridDim.x), loading the next tile's sign words
 // while it looks up the current one, and reduces all its tiles at the end.  With
 // grid = min(row tiles, CUs) every CU holds one workgroup that streams several
-// tiles, so table builds are amortised and loads overlap lookups.
+// tiles, so table builds are amortised and loads overlap lookups.  With few
+// tiles (RS = 2 or 4 workgroups per tile, see gemv_res_tiles) each workgroup
+// takes 16 / RS rows of one tile and its lanes split the planes instead.
 //
 // Lane (r, hs) of wavefronts 8w..8w+7: row r of the tile, half-group slot
 // hs = 0..31 of window w (group hs/2, columns 64*(hs%2) .. +63).  A wavefront's four slots are two

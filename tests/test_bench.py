@@ -64,6 +64,12 @@ def test_source_sha_is_a_stable_hash_of_the_kernel_file():
     assert len(bench.source_sha()) == 16 and int(bench.source_sha(), 16) >= 0
 
 
+def test_code_hash_ignores_comments_and_layout_only():
+    src = "int f(int a) {\n  return a + 1;  // one more\n}\n"
+    assert bench.code_hash(src) == bench.code_hash("/* doc */ int f(int a) { return a + 1; }")
+    assert bench.code_hash(src) != bench.code_hash("int f(int a) { return a + 2; }")
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
