@@ -244,6 +244,49 @@ def secondary(args, bcq, torch, bcq_synth):
         rows["gemv_%dx%d_b1" % (M, K)] = r
         del rot, ys
 
+    # the MLP's gate and up projections as one gate/up store (2 x 14336 rows,
+    # bcq_gemv_gate_up) with the silu(gate) * up epilogue in the same launch,
+    # next to the two separate 14336x4096 products timed above (which would
+    # still need the epilogue as a third kernel)
+    print("[bench] secondary gate/up", file=sys.stderr, flush=True)
+    Mo = 14336
+    w = bcq_synth.make(2 * Mo, 4096, 4, seed=9, name="gate_up_28672x4096_b1")
+    rot = Rotation(w, ROTATE_BYTES, bcq, torch)
+    ys = [torch.empty(Mo, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+    r = {}
+    for p in (2, 3, 4):
+        d = time_calls(torch, lambda i, p=p: bcq.bcq_gemv_gate_up(rot.stores[i % rot.n], p,
+                                                                  rot.x[i % rot.n][0],
+                                                                  ys[i % rot.n]),
+                       n, 10)
+        nb = algorithmic_bytes(2 * Mo, 4096, p) - Mo * 2  # Mo outputs, not 2 * Mo
+        r[str(p)] = {"us": round(d * 1e3, 3),
+                     "GBps": round(nb / (d * 1e-3) / 1e9, 1),
+                     "two_products_us": round(2 * rows["gemv_14336x4096_b1"][str(p)]["us"], 3)}
+    rows["gate_up_fused_28672x4096_b1"] = r
+    del rot, ys
+
+    # q, k and v (4096 + 1024 + 1024 rows over one 4096-wide input) as one
+    # concatenated 6144-row store, next to the three separate products
+    print("[bench] secondary q/k/v", file=sys.stderr, flush=True)
+    r = {}
+    stores = {}
+    for M in (6144, 4096, 1024):
+        w = bcq_synth.make(M, 4096, 4, seed=10 + M, name="qkv_%dx4096_b1" % M)
+        rot = Rotation(w, ROTATE_BYTES, bcq, torch)
+        ys = [torch.empty(M, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+        stores[M] = {p: time_calls(torch, lambda i, p=p: bcq.bcq_gemv(rot.stores[i % rot.n], p,
+                                                                     rot.x[i % rot.n][0],
+                                                                     ys[i % rot.n]), n, 10)
+                     for p in (2, 3, 4)}
+        del rot, ys
+    for p in (2, 3, 4):
+        nb = algorithmic_bytes(6144, 4096, p)
+        d = stores[6144][p]
+        r[str(p)] = {"us": round(d * 1e3, 3), "GBps": round(nb / (d * 1e-3) / 1e9, 1),
+                     "three_products_us": round((stores[4096][p] + 2 * stores[1024][p]) * 1e3, 3)}
+    rows["qkv_concatenated_6144x4096_b1"] = r
+
     # 4096x4096 at batch 1 with one store repeated (planes served from the
     # Infinity Cache after the first call): context for the cold numbers
     w = bcq_synth.config(2)

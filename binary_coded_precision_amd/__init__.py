@@ -40,6 +40,7 @@ EXPORTS = (
     "bcq_pack_planes",
     "bcq_unpack_planes",
     "bcq_gemv",
+    "bcq_gemv_gate_up",
     "bcq_gemm_skinny",
     "bcq_workspace_bytes",
     "bcq_gemv_mixed_p",
@@ -90,6 +91,7 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         "bcq_pack_planes": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
         "bcq_unpack_planes": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
         "bcq_gemv": (ctypes.c_int, [st, i32, vp, ctypes.c_int, vp, ctypes.c_int, vp]),
+        "bcq_gemv_gate_up": (ctypes.c_int, [st, i32, vp, ctypes.c_int, vp, ctypes.c_int, vp]),
         "bcq_gemm_skinny": (ctypes.c_int, [st, i32, vp, i32, i32, ctypes.c_int, vp, i32,
                                            ctypes.c_int, vp, sz, vp]),
         "bcq_workspace_bytes": (sz, [st, i32]),
@@ -158,6 +160,14 @@ def bcq_gemv(store: "Store", p: int, x, y, stream=None) -> None:
     """``y[M] = product at precision p`` of the device vector ``x[K]``."""
     _check("bcq_gemv", load().bcq_gemv(store.ref(), p, _ptr(x), _dtype_code(x), _ptr(y),
                                        _dtype_code(y), _stream(stream)))
+
+
+def bcq_gemv_gate_up(store: "Store", p: int, x, y, stream=None) -> None:
+    """``y[M/2] = silu(gate . x) * (up . x)`` for a store whose 16-row tiles hold
+    8 gate rows then the matching 8 up rows (see ``include/bcq.h``)."""
+    _check("bcq_gemv_gate_up", load().bcq_gemv_gate_up(store.ref(), p, _ptr(x), _dtype_code(x),
+                                                       _ptr(y), _dtype_code(y),
+                                                       _stream(stream)))
 
 
 def bcq_workspace_bytes(store: "Store", b: int) -> int:

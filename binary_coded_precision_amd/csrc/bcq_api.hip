@@ -186,6 +186,19 @@ bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype 
                                          store->zero[p], x, y, store->scale_dtype, stream));
 }
 
+bcq_status bcq_gemv_gate_up(const bcq_store *store, int32_t p, const void *x, bcq_dtype x_dtype,
+                            void *y, bcq_dtype y_dtype, hipStream_t stream) {
+  BCQ_TRY(check_store(store));
+  BCQ_TRY(check_precision(store, p));
+  BCQ_TRY(check_dtypes(store, x_dtype, y_dtype));
+  if (store->M % bcq::kTileRows != 0) return BCQ_ERR_INVALID_ARG;
+  if (x == nullptr || y == nullptr) return BCQ_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, dtype_size(y_dtype))) return BCQ_ERR_ALIGNMENT;
+  return hip_status(bcq::launch_gemv_gate_up(store->bits, store->M, store->K, p,
+                                             store->alpha[p], store->zero[p], x, y,
+                                             store->scale_dtype, stream));
+}
+
 size_t bcq_workspace_bytes(const bcq_store *store, int32_t b) {
   if (check_store(store) != BCQ_OK || b < 1 || b > BCQ_MAX_BATCH) return 0;
   if (!on_matrix_cores(store, b)) return 0;

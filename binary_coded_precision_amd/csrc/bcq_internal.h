@@ -44,6 +44,11 @@ hipError_t launch_unpack(const uint32_t *packed, int P, int M, int K, uint32_t *
 hipError_t launch_gemv_lut(const uint32_t *bits, int M, int K, int p, const void *alpha,
                            const void *zero, const void *x, void *y, bcq_dtype dt,
                            hipStream_t s);
+// Gate/up store (rows interleaved in 8-row halves of each tile): y[j] =
+// silu(gate_j . x) * (up_j . x) for j < M / 2.
+hipError_t launch_gemv_gate_up(const uint32_t *bits, int M, int K, int p, const void *alpha,
+                           const void *zero, const void *x, void *y, bcq_dtype dt,
+                           hipStream_t s);
 
 // Batched products with 2..8 requests per launch (vector ALUs, shared tables).
 // x rows at x + r*ldx, y rows at y + r*ldy, r < nreq; p_max = max of t.p[].

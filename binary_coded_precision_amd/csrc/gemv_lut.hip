@@ -181,6 +181,15 @@ __device__ __forceinline__ float sum8_lanes(float v) {
 constexpr int kG1Ksub = 16;         // groups per window of tables
 constexpr int kG1ChunkStride = 80;  // bytes per chunk table: 16 entries + 16 B pad
 
+// Gate/up stores (bcq_gemv_gate_up): rows 0..7 of every 16-row tile t are gate
+// rows 8t..8t+7 and rows 8..15 the up rows of the same outputs, so a tile's
+// writeback holds both products of its 8 outputs: out = silu(g) * u with
+// silu(g) = g / (1 + exp(-g)), from the fp32 sums, rounded once.
+constexpr int kGuRows = kTileRows / 2;
+__device__ __forceinline__ float gate_up_out(float g, float u) {
+  return g / (1.f + expf(-g)) * u;
+}
+
 // ------------------------------------------------ batch 1, whole-K tables
 //
 // For K <= 4096 the tables of all of K stay resident in LDS (NW <= 2 windows of
@@ -257,7 +266,7 @@ __device__ __forceinline__ float r_half_sum(const uint2 bw, uint32_t base) {
 // 8w..8w+7 look up window w.  At K = 4096 that is four wavefronts per SIMD,
 // enough to hide the LDS latency of the lookups, and every lane builds one
 // chunk's table.
-template <typename T, int NW, int P, int TMAX, int RS = 1>
+template <typename T, int NW, int P, int TMAX, int RS = 1, bool GU = false>
 __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
     const uint4 *__restrict__ bits, const T *__restrict__ alpha, const T *__restrict__ zero,
     const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT) {
@@ -289,6 +298,7 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   // r % (16 / RS) of that part and planes PC * (r / (16 / RS)) ..  + PC - 1,
   // so the lookups of a tile spread over RS times as many compute units.
   static_assert(RS == 1 || TMAX == 1, "row parts only for one tile per workgroup");
+  static_assert(!GU || RS == 1, "a gate/up tile's two halves must meet in one workgroup");
   constexpr int kPartRows = kTileRows / RS;
   constexpr int PC = (P + RS - 1) / RS;  // planes per lane
   const int rl = r % kPartRows;          // row within the part
@@ -430,7 +440,20 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
     if (lane < 16) part[wave][k][lane] = acc[k];
   }
   __syncthreads();
-  if (tid < TMAX * kTileRows) {
+  if constexpr (GU) {
+    if (tid < TMAX * kGuRows) {
+      const int k = tid / kGuRows;
+      const int rr = tid % kGuRows;
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        g += part[v][k][rr];
+        u += part[v][k][rr + kGuRows];
+      }
+      const int jo = ((int)blockIdx.x + k * (int)gridDim.x) * kGuRows + rr;
+      if (k < nt && jo < M / 2) y[jo] = (T)gate_up_out(g, u);
+    }
+  } else if (tid < TMAX * kTileRows) {
     const int k = tid / kTileRows;
     const int rr = tid % kTileRows;  // lane rr holds row rr (RS = 1) or part row rr
     const int mm = RS > 1 ? ((int)blockIdx.x / RS) * kTileRows +
@@ -471,7 +494,7 @@ struct StreamSlot {
   uint32_t sc[4];                  // four scales or offsets this lane stages
 };
 
-template <typename T, int P>
+template <typename T, int P, bool GU = false>
 __global__ __launch_bounds__(kRThreads) void gemv_stream_kernel(
     const uint4 *__restrict__ bits, const T *__restrict__ alpha, const T *__restrict__ zero,
     const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT) {
@@ -583,7 +606,18 @@ __global__ __launch_bounds__(kRThreads) void gemv_stream_kernel(
   acc += __shfl_xor(acc, 32);
   if (lane < 16) part[wave][lane] = acc;
   __syncthreads();
-  if (tid < kTileRows) {
+  if constexpr (GU) {
+    if (tid < kGuRows) {
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int v = 0; v < kRWaves; ++v) {
+        g += part[v][tid];
+        u += part[v][tid + kGuRows];
+      }
+      const int jo = tile * kGuRows + tid;
+      if (jo < M / 2) y[jo] = (T)gate_up_out(g, u);
+    }
+  } else if (tid < kTileRows) {
     float sum = 0.f;
 #pragma unroll
     for (int v = 0; v < kRWaves; ++v) sum += part[v][tid];
@@ -718,7 +752,7 @@ __device__ __forceinline__ void stream_half(StreamShared<T, P> &sm, const uint4 
   if (lane < 16) sm.part[(UPPER ? kRWaves : 0) + wave][lane] = acc;
 }
 
-template <typename T, int P>
+template <typename T, int P, bool GU = false>
 __global__ __launch_bounds__(2 * kRThreads) void gemv_stream2_kernel(
     const uint4 *__restrict__ bits, const T *__restrict__ alpha, const T *__restrict__ zero,
     const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT) {
@@ -730,7 +764,18 @@ __global__ __launch_bounds__(2 * kRThreads) void gemv_stream2_kernel(
     stream_half<T, P, true>(sm, bits, alpha, zero, x, M, G, MT, tid - kRThreads);
   // ---- reduce the 64 slot partials of each row in a fixed order
   __syncthreads();
-  if (tid < kTileRows) {
+  if constexpr (GU) {
+    if (tid < kGuRows) {
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int v = 0; v < 2 * kRWaves; ++v) {
+        g += sm.part[v][tid];
+        u += sm.part[v][tid + kGuRows];
+      }
+      const int jo = (int)blockIdx.x * kGuRows + tid;
+      if (jo < M / 2) y[jo] = (T)gate_up_out(g, u);
+    }
+  } else if (tid < kTileRows) {
     float sum = 0.f;
 #pragma unroll
     for (int v = 0; v < 2 * kRWaves; ++v) sum += sm.part[v][tid];
@@ -757,24 +802,24 @@ int compute_units() {
   return n;
 }
 
-template <typename T, int NW, int TMAX, int RS = 1>
+template <typename T, int NW, int TMAX, int RS = 1, bool GU = false>
 void gemv_res_launch(dim3 grid, hipStream_t s, const uint4 *b4, const T *a, const T *z,
                      const T *xx, T *yy, int M, int G, int MT, int p) {
   switch (p) {
     case 1:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 1, TMAX, RS>), grid, dim3(kRThreads * NW), 0, s,
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 1, TMAX, RS, GU>), grid, dim3(kRThreads * NW), 0, s,
                          b4, a, z, xx, yy, M, G, MT);
       break;
     case 2:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 2, TMAX, RS>), grid, dim3(kRThreads * NW), 0, s,
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 2, TMAX, RS, GU>), grid, dim3(kRThreads * NW), 0, s,
                          b4, a, z, xx, yy, M, G, MT);
       break;
     case 3:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 3, TMAX, RS>), grid, dim3(kRThreads * NW), 0, s,
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 3, TMAX, RS, GU>), grid, dim3(kRThreads * NW), 0, s,
                          b4, a, z, xx, yy, M, G, MT);
       break;
     default:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 4, TMAX, RS>), grid, dim3(kRThreads * NW), 0, s,
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 4, TMAX, RS, GU>), grid, dim3(kRThreads * NW), 0, s,
                          b4, a, z, xx, yy, M, G, MT);
       break;
   }
@@ -784,25 +829,25 @@ void gemv_res_launch(dim3 grid, hipStream_t s, const uint4 *b4, const T *a, cons
 // units or fewer holding a tile, each tile's rows are split over 4 (2)
 // workgroups.  More tiles than compute units: tiles dealt round-robin, up to 4
 // per workgroup.
-template <typename T, int NW>
+template <typename T, int NW, bool GU>
 void gemv_res_tiles(hipStream_t s, const uint4 *b4, const T *a, const T *z, const T *xx, T *yy,
                     int M, int G, int MT, int p) {
   const int cus = compute_units();
   const int tmax = (MT + cus - 1) / cus;
-  if (4 * MT <= cus)
+  if (!GU && 4 * MT <= cus)
     gemv_res_launch<T, NW, 1, 4>(dim3(MT * 4), s, b4, a, z, xx, yy, M, G, MT, p);
-  else if (2 * MT <= cus)
+  else if (!GU && 2 * MT <= cus)
     gemv_res_launch<T, NW, 1, 2>(dim3(MT * 2), s, b4, a, z, xx, yy, M, G, MT, p);
   else if (tmax <= 1)
-    gemv_res_launch<T, NW, 1>(dim3(MT), s, b4, a, z, xx, yy, M, G, MT, p);
+    gemv_res_launch<T, NW, 1, 1, GU>(dim3(MT), s, b4, a, z, xx, yy, M, G, MT, p);
   else if (tmax <= 2)
-    gemv_res_launch<T, NW, 2>(dim3((MT + 1) / 2), s, b4, a, z, xx, yy, M, G, MT, p);
+    gemv_res_launch<T, NW, 2, 1, GU>(dim3((MT + 1) / 2), s, b4, a, z, xx, yy, M, G, MT, p);
   else
-    gemv_res_launch<T, NW, 4>(dim3((MT + 3) / 4 > cus ? (MT + 3) / 4 : cus), s, b4, a, z, xx, yy,
-                              M, G, MT, p);
+    gemv_res_launch<T, NW, 4, 1, GU>(dim3((MT + 3) / 4 > cus ? (MT + 3) / 4 : cus), s, b4, a, z,
+                                     xx, yy, M, G, MT, p);
 }
 
-template <typename T>
+template <typename T, bool GU>
 hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *alpha,
                          const void *zero, const void *x, void *y, hipStream_t s) {
   const int G = K / kGroup;
@@ -814,29 +859,29 @@ hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *
   const T *xx = static_cast<const T *>(x);
   T *yy = static_cast<T *>(y);
   if (nwin <= 1) {
-    gemv_res_tiles<T, 1>(s, b4, a, z, xx, yy, M, G, MT, p);
+    gemv_res_tiles<T, 1, GU>(s, b4, a, z, xx, yy, M, G, MT, p);
     return hipGetLastError();
   }
   if (nwin <= 2) {
-    gemv_res_tiles<T, 2>(s, b4, a, z, xx, yy, M, G, MT, p);
+    gemv_res_tiles<T, 2, GU>(s, b4, a, z, xx, yy, M, G, MT, p);
     return hipGetLastError();
   }
   // larger K: one tile per workgroup, tables streamed window by window
   dim3 grid(MT), block(kRThreads), block2(2 * kRThreads);
   switch (p) {
     case 1:
-      hipLaunchKernelGGL((gemv_stream_kernel<T, 1>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT);
+      hipLaunchKernelGGL((gemv_stream_kernel<T, 1, GU>), grid, block, 0, s, b4, a, z, xx, yy, M, G, MT);
       break;
     case 2:
-      hipLaunchKernelGGL((gemv_stream2_kernel<T, 2>), grid, block2, 0, s, b4, a, z, xx, yy, M, G,
+      hipLaunchKernelGGL((gemv_stream2_kernel<T, 2, GU>), grid, block2, 0, s, b4, a, z, xx, yy, M, G,
                          MT);
       break;
     case 3:
-      hipLaunchKernelGGL((gemv_stream2_kernel<T, 3>), grid, block2, 0, s, b4, a, z, xx, yy, M, G,
+      hipLaunchKernelGGL((gemv_stream2_kernel<T, 3, GU>), grid, block2, 0, s, b4, a, z, xx, yy, M, G,
                          MT);
       break;
     default:
-      hipLaunchKernelGGL((gemv_stream2_kernel<T, 4>), grid, block2, 0, s, b4, a, z, xx, yy, M, G,
+      hipLaunchKernelGGL((gemv_stream2_kernel<T, 4, GU>), grid, block2, 0, s, b4, a, z, xx, yy, M, G,
                          MT);
       break;
   }
@@ -1251,8 +1296,15 @@ hipError_t skinny_dispatch(const uint32_t *bits, int M, int K, int p_max, const 
 hipError_t launch_gemv_lut(const uint32_t *bits, int M, int K, int p, const void *alpha,
                            const void *zero, const void *x, void *y, bcq_dtype dt,
                            hipStream_t s) {
-  if (dt == BCQ_F16) return gemv_dispatch<half_t>(bits, M, K, p, alpha, zero, x, y, s);
-  return gemv_dispatch<float>(bits, M, K, p, alpha, zero, x, y, s);
+  if (dt == BCQ_F16) return gemv_dispatch<half_t, false>(bits, M, K, p, alpha, zero, x, y, s);
+  return gemv_dispatch<float, false>(bits, M, K, p, alpha, zero, x, y, s);
+}
+
+hipError_t launch_gemv_gate_up(const uint32_t *bits, int M, int K, int p, const void *alpha,
+                               const void *zero, const void *x, void *y, bcq_dtype dt,
+                               hipStream_t s) {
+  if (dt == BCQ_F16) return gemv_dispatch<half_t, true>(bits, M, K, p, alpha, zero, x, y, s);
+  return gemv_dispatch<float, true>(bits, M, K, p, alpha, zero, x, y, s);
 }
 
 hipError_t launch_skinny_lut(const uint32_t *bits, int M, int K, int p_max, const ReqTables &t,

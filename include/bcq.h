@@ -122,6 +122,24 @@ bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype 
                     void *y, bcq_dtype y_dtype, hipStream_t stream);
 
 /*
+ * Gated-MLP epilogue fused into one product at batch 1: y[j] = silu(g_j) * u_j
+ * with g_j and u_j the BCQ products (precision p) of gate row j and up row j,
+ * and silu(g) = g / (1 + exp(-g)), evaluated in fp32 on the fp32 sums and
+ * rounded once.  This is the consumer of the gate and up projections of the
+ * MLP-shaped workload (two products of the same x); one launch serves both,
+ * sharing the activation tables.
+ * store: 2 * Mo rows, Mo a multiple of 8 (store->M a multiple of 16), packed
+ *   so that rows 0..7 of every 16-row tile t are gate rows 8t..8t+7 and rows
+ *   8..15 the up rows 8t..8t+7 (canonical row 16t + i holds gate row 8t + i,
+ *   row 16t + 8 + i up row 8t + i, before bcq_pack_planes); the scale and
+ *   offset tables follow the same row order.  Otherwise BCQ_ERR_INVALID_ARG.
+ * x: [K], 16-byte aligned.  y: [Mo] = [store->M / 2], element aligned.
+ * Dtypes, validation and stream behaviour as in bcq_gemv.
+ */
+bcq_status bcq_gemv_gate_up(const bcq_store *store, int32_t p, const void *x, bcq_dtype x_dtype,
+                            void *y, bcq_dtype y_dtype, hipStream_t stream);
+
+/*
  * Y[r] = BCQ product at precision p for each of b activation rows X[r].
  * X: [b][ldx] (row r starts at X + r*ldx elements), 16-byte aligned, so ldx*size
  * must be a multiple of 16 bytes; ldx >= K.  Y: [b][ldy], ldy >= M, element

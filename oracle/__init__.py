@@ -12,7 +12,8 @@ fp16 and fp32 value is a float64 value).
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``
 (worked example from the BiLoCo page, dense dequantise-then-matmul, brute force
-over all sign patterns, closed forms, prefix invariant, linearity).
+over all sign patterns, closed forms, prefix invariant, linearity; the gate/up
+epilogue by silu's closed-form points and a dense per-tile reconstruction).
 """
 
 from __future__ import annotations
@@ -113,6 +114,34 @@ def gemv_requests(signs, x, p_req: Sequence[int], alpha_for, zero_for, g: int = 
     out = [gemv(signs, alpha_for(int(p)), zero_for(int(p)), x[r], int(p), g)
            for r, p in enumerate(p_req)]
     return np.stack(out)
+
+
+def silu_mul(g, u) -> np.ndarray:
+    """The gated-MLP epilogue in float64: silu(g) * u with silu(g) = g / (1 + exp(-g))."""
+    g = _f64(g)
+    u = _f64(u)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+def gate_up_rows(j):
+    """Store rows of the gate and up products of outputs ``j`` in a gate/up store:
+    16-row tile t holds gate rows 8t..8t+7, then up rows 8t..8t+7."""
+    j = np.asarray(j, dtype=np.int64)
+    tile, i = j // 8, j % 8
+    return 16 * tile + i, 16 * tile + 8 + i
+
+
+def gemv_gate_up(signs, alpha, zero, x, p: int, g: int = 128) -> np.ndarray:
+    """``y[j] = silu(gate_j . x) * (up_j . x)`` for a gate/up store of 2 * Mo rows.
+
+    Returns float64 ``y`` [Mo] (Mo = rows of ``signs`` / 2, rows a multiple of 16).
+    """
+    y = gemv(signs, alpha, zero, x, p, g)
+    if y.shape[0] % 16:
+        raise ValueError("a gate/up store has a multiple of 16 rows")
+    gr, ur = gate_up_rows(np.arange(y.shape[0] // 2))
+    return silu_mul(y[gr], y[ur])
 
 
 def dequant(signs, alpha, zero, p: int, K: int, g: int = 128) -> np.ndarray:

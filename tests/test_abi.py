@@ -68,6 +68,11 @@ def gemv(st, p=2, x=FAKE, y=FAKE, xdt=bcq.BCQ_F16, ydt=bcq.BCQ_F16):
     return bcq.load().bcq_gemv(ref, p, x, xdt, y, ydt, None)
 
 
+def gate_up(st, p=2, x=FAKE, y=FAKE, xdt=bcq.BCQ_F16, ydt=bcq.BCQ_F16):
+    ref = None if st is None else ctypes.byref(st)
+    return bcq.load().bcq_gemv_gate_up(ref, p, x, xdt, y, ydt, None)
+
+
 def skinny(st, p=2, X=FAKE, b=4, ldx=None, Y=FAKE, ldy=None, dt=bcq.BCQ_F16, ws=None, wsb=0):
     ldx = st.K if ldx is None else ldx
     ldy = st.M if ldy is None else ldy
@@ -107,6 +112,13 @@ E_ARG, E_UNS, E_ALN = bcq.BCQ_ERR_INVALID_ARG, bcq.BCQ_ERR_UNSUPPORTED, bcq.BCQ_
     (lambda: gemv(make_store(), ydt=bcq.BCQ_F32), E_UNS),
     (lambda: gemv(make_store(), xdt=3), E_ARG),
     (lambda: gemv(make_store(dtype=9)), E_ARG),
+    (lambda: gate_up(None), E_ARG),
+    (lambda: gate_up(make_store(M=24)), E_ARG),  # gate/up stores have whole 16-row tiles
+    (lambda: gate_up(make_store(M=40)), E_ARG),
+    (lambda: gate_up(make_store(), p=5), E_ARG),
+    (lambda: gate_up(make_store(), x=0), E_ARG),
+    (lambda: gate_up(make_store(), y=FAKE + 1), E_ALN),
+    (lambda: gate_up(make_store(), xdt=bcq.BCQ_F32), E_UNS),
     (lambda: skinny(make_store(), b=0), E_ARG),
     (lambda: skinny(make_store(), b=257), E_ARG),
     (lambda: skinny(make_store(), ldx=255), E_ARG),

@@ -726,3 +726,75 @@ def test_wide_random_sweep_with_padding_and_offsets():
             ref = np.asarray(oracle_y(w, w.x, w.p_req, rows))
             check(Yb[:, :M].cpu().numpy()[:, rows], ref, tol, (case, "mixed"))
             assert (Yb[:, M:].float() == 3.0).all(), (case, "mixed")
+
+
+# ---------------------------------------------------------------- gated-MLP epilogue
+
+@pytest.mark.parametrize("Mo,K,P,dt", [
+    (32, 1024, 4, np.float16),    # one table window, one tile per workgroup
+    (2048, 4096, 4, np.float16),  # two windows, 256 tiles
+    (5000, 4096, 3, np.float16),  # several tiles per workgroup
+    (256, 6144, 4, np.float16),   # K past the resident tables: streamed windows
+    (16, 512, 2, np.float32),
+    (264, 8320, 3, np.float32),
+])
+def test_gate_up_fused_epilogue(Mo, K, P, dt):
+    """bcq_gemv_gate_up: silu(gate . x) * (up . x) from one store whose tiles
+    hold 8 gate rows then the matching 8 up rows; every precision."""
+    w = bcq_synth.make(2 * Mo, K, P, dtype=dt, seed=Mo + K, outlier_frac=0.01)
+    st = store_of(w)
+    x = dev(w.x[0])
+    tdt = torch.float16 if dt == np.float16 else torch.float32
+    outs = sample_rows(Mo, 256)
+    gr, ur = oracle.gate_up_rows(outs)
+    for p in range(1, P + 1):
+        say("gate_up", Mo, K, P, p, np.dtype(dt).name)
+        y = torch.full((Mo + 8,), 5.0, dtype=tdt, device="cuda")
+        bcq.bcq_gemv_gate_up(st, p, x, y[:Mo])
+        yr = oracle_y(w, w.x[:1], [p], np.concatenate([gr, ur]))[0]
+        ref = oracle.silu_mul(yr[:len(outs)], yr[len(outs):])
+        got = y[:Mo].cpu().numpy()[outs]
+        assert rel_l2(got, ref) <= TOL[np.dtype(dt)], p
+        assert (y[Mo:].float() == 5.0).all()
+
+
+def test_gate_up_mlp_shape_sampled():
+    """The MLP gate/up pair of the 14336x4096 workload as one 28672-row store
+    at p = 3, sampled outputs."""
+    Mo, K = 14336, 4096
+    w = bcq_synth.make(2 * Mo, K, 4, dtype=np.float16, seed=77, outlier_frac=0.01)
+    st = store_of(w)
+    y = torch.empty(Mo, dtype=torch.float16, device="cuda")
+    say("gate_up mlp", Mo, K)
+    bcq.bcq_gemv_gate_up(st, 3, dev(w.x[0]), y)
+    outs = sample_rows(Mo, 384)
+    gr, ur = oracle.gate_up_rows(outs)
+    yr = oracle_y(w, w.x[:1], [3], np.concatenate([gr, ur]))[0]
+    ref = oracle.silu_mul(yr[:len(outs)], yr[len(outs):])
+    assert rel_l2(y.cpu().numpy()[outs], ref) <= 2e-3
+
+
+def test_qkv_concatenated_store():
+    """q, k and v projections (4096, 1024 and 1024 rows of one 4096-column
+    input) as one 6144-row store: one bcq_gemv call equals the three separate
+    products, each against the oracle."""
+    K = 4096
+    w = bcq_synth.make(6144, K, 4, dtype=np.float16, seed=61, outlier_frac=0.01)
+    st = store_of(w)
+    x = dev(w.x[0])
+    parts = [(0, 4096), (4096, 5120), (5120, 6144)]
+    rows = sample_rows(6144, 384)
+    for p in (2, 3, 4):
+        say("qkv", p)
+        y = torch.empty(6144, dtype=torch.float16, device="cuda")
+        bcq.bcq_gemv(st, p, x, y)
+        ref = oracle_y(w, w.x[:1], [p], rows)[0]
+        assert rel_l2(y.cpu().numpy()[rows], ref) <= 2e-3, p
+        for lo, hi in parts:
+            sub = bcq.Store.from_host(np.ascontiguousarray(w.signs[:, lo:hi]),
+                                      np.ascontiguousarray(w.alpha[:, lo:hi]),
+                                      np.ascontiguousarray(w.zero[lo:hi]))
+            ys = torch.empty(hi - lo, dtype=torch.float16, device="cuda")
+            bcq.bcq_gemv(sub, p, x, ys)
+            r = rows[(rows >= lo) & (rows < hi)]
+            assert rel_l2(ys.cpu().numpy()[r - lo], oracle_y(w, w.x[:1], [p], r)[0]) <= 2e-3

@@ -239,3 +239,46 @@ def test_rejects_bad_precision():
         oracle.gemv(w.signs, w.alpha, w.zero, w.x[0], 0)
     with pytest.raises(ValueError):
         oracle.gemv(w.signs, w.alpha, w.zero, w.x[0], 3)
+
+
+# ---------------------------------------------------------------- gated-MLP epilogue
+
+def test_silu_mul_closed_form_points():
+    """silu(g) = g / (1 + exp(-g)): 0 at 0, 3g/4 at ln 3, g/4 at -ln 3, g and 0 in the limits."""
+    g = np.array([0.0, np.log(3.0), -np.log(3.0), 40.0, -40.0, 2.0])
+    u = np.array([5.0, 2.0, 2.0, 0.5, 3.0, -1.0])
+    got = oracle.silu_mul(g, u)
+    assert got[0] == 0.0
+    assert abs(got[1] - 0.75 * np.log(3.0) * 2.0) < 1e-15
+    assert abs(got[2] + 0.25 * np.log(3.0) * 2.0) < 1e-15  # silu(-ln 3) = -ln3 / 4
+    assert abs(got[3] - 40.0 * 0.5) < 1e-12 and abs(got[4]) < 1e-15
+    assert abs(got[5] - (-2.0 / (1.0 + np.exp(-2.0)))) < 1e-15
+
+
+def test_gate_up_rows_interleave():
+    gr, ur = oracle.gate_up_rows(np.arange(20))
+    assert list(gr[:10]) == [0, 1, 2, 3, 4, 5, 6, 7, 16, 17]
+    assert list(ur[:10]) == [8, 9, 10, 11, 12, 13, 14, 15, 24, 25]
+    assert sorted(np.concatenate([gr[:16], ur[:16]])) == list(range(32))
+
+
+def test_gate_up_matches_dense_tile_by_tile():
+    """Dense NumPy reconstruction, then each tile's gate and up rows paired by hand."""
+    w = bcq_synth.make(48, 256, 3, seed=41, outlier_frac=0.01)
+    x = w.x[0].astype(np.float64)
+    for p in (1, 2, 3):
+        yd = dense_numpy(w.signs, w.alpha, w.zero, p, w.K) @ x
+        want = []
+        for t in range(3):
+            for i in range(8):
+                gg, uu = yd[16 * t + i], yd[16 * t + 8 + i]
+                want.append(gg / (1.0 + np.exp(-gg)) * uu)
+        got = oracle.gemv_gate_up(w.signs, w.alpha, w.zero, x, p)
+        assert got.shape == (24,)
+        assert rel(got, want) < 1e-12
+
+
+def test_gate_up_rejects_partial_tiles():
+    w = bcq_synth.make(40, 128, 2, seed=3)
+    with pytest.raises(ValueError):
+        oracle.gemv_gate_up(w.signs, w.alpha, w.zero, w.x[0], 2)
