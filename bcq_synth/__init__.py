@@ -227,3 +227,25 @@ def sweep_cases() -> List[dict]:
     """Configuration 5: decoder-layer shapes at batch 1, 16, 32, 64 and p = 4."""
     return [dict(shape=s, M=M, K=K, b=b, p=4)
             for s, (M, K) in LAYER_SHAPES.items() for b in (1, 16, 32, 64)]
+
+
+class LowRank:
+    """Inputs of a binary low-rank correction y += sum_r alpha_r u_r (v_r . x)."""
+
+    def __init__(self, u, v, alpha, x, y0):
+        self.u, self.v, self.alpha, self.x, self.y0 = u, v, alpha, x, y0
+        self.M, self.R = y0.shape[0], alpha.shape[0]
+        self.K = x.shape[0]
+
+
+def lowrank(M: int, K: int, R: int, dtype=np.float16, seed: int = 0) -> LowRank:
+    """Seeded synthetic low-rank correction terms: u [M][ceil(R/32)] and
+    v [R][K/32] uniformly random sign words, alpha_r = |N(0, 0.02)| / sqrt(R),
+    x ~ N(0, 1) and y0 ~ N(0, 1) (the output being corrected)."""
+    rng = _rng(seed)
+    u = rng.integers(0, 2 ** 32, size=(M, (R + 31) // 32), dtype=np.uint64).astype(np.uint32)
+    v = rng.integers(0, 2 ** 32, size=(R, K // 32), dtype=np.uint64).astype(np.uint32)
+    alpha = (np.abs(rng.normal(0.0, 0.02, size=R)) / np.sqrt(R)).astype(dtype)
+    x = rng.normal(0.0, 1.0, size=K).astype(dtype)
+    y0 = rng.normal(0.0, 1.0, size=M).astype(dtype)
+    return LowRank(u, v, alpha, x, y0)

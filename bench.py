@@ -287,6 +287,23 @@ def secondary(args, bcq, torch, bcq_synth):
                      "three_products_us": round((stores[4096][p] + 2 * stores[1024][p]) * 1e3, 3)}
     rows["qkv_concatenated_6144x4096_b1"] = r
 
+    # binary low-rank correction y += sum_r alpha_r u_r (v_r . x) on a 4096x4096
+    # output (BiLoCo's ranks 16..512); each timed call adds to the same y
+    print("[bench] secondary low-rank", file=sys.stderr, flush=True)
+    r = {}
+    for R in (16, 128, 512):
+        lr = bcq_synth.lowrank(4096, 4096, R, seed=R)
+        u = torch.from_numpy(lr.u.view(np.int32)).cuda()
+        v = torch.from_numpy(lr.v.view(np.int32)).cuda()
+        a = torch.from_numpy(lr.alpha).cuda()
+        xx = torch.from_numpy(lr.x).cuda()
+        yy = torch.from_numpy(lr.y0).cuda()
+        zz = torch.empty(R, dtype=torch.float32, device="cuda")
+        d = time_calls(torch, lambda i: bcq.bcq_lowrank_correct(u, v, a, xx, yy, zz), n, 10)
+        sign_bytes = 4096 * ((R + 31) // 32) * 4 + R * 4096 // 8
+        r["rank_%d" % R] = {"us": round(d * 1e3, 3), "sign_bytes": sign_bytes}
+    rows["lowrank_correction_4096x4096_b1"] = r
+
     # 4096x4096 at batch 1 with one store repeated (planes served from the
     # Infinity Cache after the first call): context for the cold numbers
     w = bcq_synth.config(2)

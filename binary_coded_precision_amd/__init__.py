@@ -44,6 +44,7 @@ EXPORTS = (
     "bcq_gemm_skinny",
     "bcq_workspace_bytes",
     "bcq_gemv_mixed_p",
+    "bcq_lowrank_correct",
     "bcq_status_string",
 )
 
@@ -97,6 +98,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         "bcq_workspace_bytes": (sz, [st, i32]),
         "bcq_gemv_mixed_p": (ctypes.c_int, [st, vp, vp, i32, i32, ctypes.c_int, vp, i32,
                                             ctypes.c_int, vp, sz, vp]),
+        "bcq_lowrank_correct": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp, ctypes.c_int,
+                                               vp, vp]),
         "bcq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -168,6 +171,25 @@ def bcq_gemv_gate_up(store: "Store", p: int, x, y, stream=None) -> None:
     _check("bcq_gemv_gate_up", load().bcq_gemv_gate_up(store.ref(), p, _ptr(x), _dtype_code(x),
                                                        _ptr(y), _dtype_code(y),
                                                        _stream(stream)))
+
+
+def bcq_lowrank_correct(u_signs, v_signs, alpha, x, y, z=None, stream=None) -> None:
+    """``y[M] += sum_r alpha[r] * u[:, r] * (v[r] . x)`` in place (see ``include/bcq.h``).
+
+    ``u_signs`` [M][ceil(R/32)] and ``v_signs`` [R][K/32] are device int32/uint32
+    sign words; ``alpha`` [R], ``x`` [K] and ``y`` [M] share one dtype; ``z`` is
+    an R-float device workspace (allocated through torch when None)."""
+    import torch
+
+    R, M, K = alpha.numel(), y.numel(), x.numel()
+    if not (x.dtype == y.dtype == alpha.dtype):
+        raise ValueError("alpha, x and y must share one dtype")
+    if z is None:
+        z = torch.empty(R, dtype=torch.float32, device=y.device)
+    _check("bcq_lowrank_correct",
+           load().bcq_lowrank_correct(_ptr(u_signs), _ptr(v_signs), _ptr(alpha), R, M, K,
+                                      _ptr(x), _ptr(y), _dtype_code(y), _ptr(z),
+                                      _stream(stream)))
 
 
 def bcq_workspace_bytes(store: "Store", b: int) -> int:

@@ -199,6 +199,22 @@ bcq_status bcq_gemv_gate_up(const bcq_store *store, int32_t p, const void *x, bc
                                              store->scale_dtype, stream));
 }
 
+bcq_status bcq_lowrank_correct(const uint32_t *u_signs, const uint32_t *v_signs,
+                               const void *alpha, int32_t R, int32_t M, int32_t K, const void *x,
+                               void *y, bcq_dtype dtype, float *z, hipStream_t stream) {
+  if (dtype != BCQ_F16 && dtype != BCQ_F32) return BCQ_ERR_INVALID_ARG;
+  if (R < 1 || R > BCQ_LOWRANK_MAX_RANK || M < 1 || K < 32 || K % 32 != 0)
+    return BCQ_ERR_INVALID_ARG;
+  if (u_signs == nullptr || v_signs == nullptr || alpha == nullptr || x == nullptr ||
+      y == nullptr || z == nullptr)
+    return BCQ_ERR_INVALID_ARG;
+  const size_t es = dtype_size(dtype);
+  if (!aligned(u_signs, 4) || !aligned(v_signs, 4) || !aligned(z, 4) || !aligned(alpha, es) ||
+      !aligned(x, 16) || !aligned(y, es))
+    return BCQ_ERR_ALIGNMENT;
+  return hip_status(bcq::launch_lowrank(u_signs, v_signs, alpha, R, M, K, x, y, dtype, z, stream));
+}
+
 size_t bcq_workspace_bytes(const bcq_store *store, int32_t b) {
   if (check_store(store) != BCQ_OK || b < 1 || b > BCQ_MAX_BATCH) return 0;
   if (!on_matrix_cores(store, b)) return 0;

@@ -50,6 +50,11 @@ hipError_t launch_gemv_gate_up(const uint32_t *bits, int M, int K, int p, const 
                            const void *zero, const void *x, void *y, bcq_dtype dt,
                            hipStream_t s);
 
+// Binary low-rank correction (bcq_lowrank_correct): y += sum_r alpha_r u_r (v_r . x).
+constexpr int kLrMaxRank = BCQ_LOWRANK_MAX_RANK;
+hipError_t launch_lowrank(const uint32_t *u, const uint32_t *v, const void *alpha, int R, int M,
+                          int K, const void *x, void *y, bcq_dtype dt, float *z, hipStream_t s);
+
 // Batched products with 2..8 requests per launch (vector ALUs, shared tables).
 // x rows at x + r*ldx, y rows at y + r*ldy, r < nreq; p_max = max of t.p[].
 hipError_t launch_skinny_lut(const uint32_t *bits, int M, int K, int p_max, const ReqTables &t,

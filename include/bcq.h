@@ -51,6 +51,8 @@ extern "C" {
 #define BCQ_TILE_ROWS 16
 /* Largest batch accepted by bcq_gemm_skinny / bcq_gemv_mixed_p in one call. */
 #define BCQ_MAX_BATCH 256
+/* Largest rank accepted by bcq_lowrank_correct. */
+#define BCQ_LOWRANK_MAX_RANK 4096
 
 typedef enum {
   BCQ_OK = 0,
@@ -195,6 +197,28 @@ bcq_status bcq_gemv_mixed_p(const bcq_store *store, const int32_t *p_host, const
                             int32_t b, int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,
                             bcq_dtype y_dtype, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/*
+ * Binary low-rank correction, added in place to a product's output:
+ *     y[m] += sum_{r<R} alpha[r] * u[m][r] * (v[r] . x)
+ * with u and v in {-1,+1} (BiLoCo summary, "core idea": every rank-one term
+ * is a scale times two sign vectors, so v . x takes only additions and
+ * subtractions).  z_r = alpha_r (v_r . x) is formed in fp32; y is read, the
+ * correction added in fp32 and the sum rounded once (to nearest even).
+ * u_signs: [M][ceil(R/32)] uint32, bit r mod 32 of word [m][r/32] set = +1
+ *   (bits past R ignored), 4-byte aligned.
+ * v_signs: [R][K/32] uint32, bit k mod 32 of word [r][k/32] set = +1, 4-byte
+ *   aligned.  K must be a positive multiple of 32.
+ * alpha: [R], x: [K], y: [M] (read and written), all of one dtype (BCQ_F16 or
+ *   BCQ_F32); x 16-byte aligned, alpha and y element aligned.
+ * z: device workspace of R floats, 4-byte aligned, clobbered (calls that may
+ *   run at the same time need separate ones).
+ * 1 <= R <= BCQ_LOWRANK_MAX_RANK, M >= 1.  Validation and stream behaviour as
+ * in bcq_gemv: a rejected call enqueues nothing.
+ */
+bcq_status bcq_lowrank_correct(const uint32_t *u_signs, const uint32_t *v_signs,
+                               const void *alpha, int32_t R, int32_t M, int32_t K, const void *x,
+                               void *y, bcq_dtype dtype, float *z, hipStream_t stream);
 
 /* Static text for a status code (never null). */
 const char *bcq_status_string(bcq_status status);

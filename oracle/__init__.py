@@ -13,7 +13,9 @@ fp16 and fp32 value is a float64 value).
 Parity status: every function here is pinned by ``tests/test_oracle.py``
 (worked example from the BiLoCo page, dense dequantise-then-matmul, brute force
 over all sign patterns, closed forms, prefix invariant, linearity; the gate/up
-epilogue by silu's closed-form points and a dense per-tile reconstruction).
+epilogue by silu's closed-form points and a dense per-tile reconstruction; the
+low-rank correction by the BiLoCo page's worked example, closed forms and a
+loop-by-loop brute force).
 """
 
 from __future__ import annotations
@@ -142,6 +144,25 @@ def gemv_gate_up(signs, alpha, zero, x, p: int, g: int = 128) -> np.ndarray:
         raise ValueError("a gate/up store has a multiple of 16 rows")
     gr, ur = gate_up_rows(np.arange(y.shape[0] // 2))
     return silu_mul(y[gr], y[ur])
+
+
+def _signs_pm1(words, n: int) -> np.ndarray:
+    """{-1,+1} float64 [rows][n] from sign words (bit j mod 32 of word j/32, set = +1)."""
+    w = np.ascontiguousarray(np.asarray(words).astype("<u4"))
+    bits = np.unpackbits(w.view(np.uint8).reshape(w.shape[0], -1), axis=-1, bitorder="little")
+    return bits[:, :n].astype(np.float64) * 2.0 - 1.0
+
+
+def lowrank_correct(u_signs, v_signs, alpha, x, y0) -> np.ndarray:
+    """Binary low-rank correction in float64 (BiLoCo summary, "core idea"):
+    ``y0 + sum_r alpha_r u_r (v_r . x)`` with u [M][R] and v [R][K] sign words."""
+    alpha = _f64(alpha).reshape(-1)
+    x = _f64(x).reshape(-1)
+    R, K = alpha.shape[0], x.shape[0]
+    u = _signs_pm1(u_signs, R)
+    v = _signs_pm1(v_signs, K)
+    z = alpha * (v @ x)
+    return _f64(y0).reshape(-1) + u @ z
 
 
 def dequant(signs, alpha, zero, p: int, K: int, g: int = 128) -> np.ndarray:

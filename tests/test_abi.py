@@ -73,6 +73,10 @@ def gate_up(st, p=2, x=FAKE, y=FAKE, xdt=bcq.BCQ_F16, ydt=bcq.BCQ_F16):
     return bcq.load().bcq_gemv_gate_up(ref, p, x, xdt, y, ydt, None)
 
 
+def lowrank(u=FAKE, v=FAKE, a=FAKE, R=16, M=64, K=256, x=FAKE, y=FAKE, dt=bcq.BCQ_F16, z=FAKE):
+    return bcq.load().bcq_lowrank_correct(u, v, a, R, M, K, x, y, dt, z, None)
+
+
 def skinny(st, p=2, X=FAKE, b=4, ldx=None, Y=FAKE, ldy=None, dt=bcq.BCQ_F16, ws=None, wsb=0):
     ldx = st.K if ldx is None else ldx
     ldy = st.M if ldy is None else ldy
@@ -119,6 +123,17 @@ E_ARG, E_UNS, E_ALN = bcq.BCQ_ERR_INVALID_ARG, bcq.BCQ_ERR_UNSUPPORTED, bcq.BCQ_
     (lambda: gate_up(make_store(), x=0), E_ARG),
     (lambda: gate_up(make_store(), y=FAKE + 1), E_ALN),
     (lambda: gate_up(make_store(), xdt=bcq.BCQ_F32), E_UNS),
+    (lambda: lowrank(R=0), E_ARG),
+    (lambda: lowrank(R=4097), E_ARG),
+    (lambda: lowrank(M=0), E_ARG),
+    (lambda: lowrank(K=48), E_ARG),  # K must be whole 32-column words
+    (lambda: lowrank(dt=3), E_ARG),
+    (lambda: lowrank(z=0), E_ARG),
+    (lambda: lowrank(u=0), E_ARG),
+    (lambda: lowrank(u=FAKE + 2), E_ALN),
+    (lambda: lowrank(z=FAKE + 2), E_ALN),
+    (lambda: lowrank(y=FAKE + 1), E_ALN),
+    (lambda: lowrank(x=FAKE + 8), E_ALN),
     (lambda: skinny(make_store(), b=0), E_ARG),
     (lambda: skinny(make_store(), b=257), E_ARG),
     (lambda: skinny(make_store(), ldx=255), E_ARG),

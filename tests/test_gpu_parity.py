@@ -798,3 +798,23 @@ def test_qkv_concatenated_store():
             bcq.bcq_gemv(sub, p, x, ys)
             r = rows[(rows >= lo) & (rows < hi)]
             assert rel_l2(ys.cpu().numpy()[r - lo], oracle_y(w, w.x[:1], [p], r)[0]) <= 2e-3
+
+
+# ---------------------------------------------------------------- binary low-rank correction
+
+@pytest.mark.parametrize("M,K,R,dt", [
+    (4096, 4096, 16, np.float16), (4096, 4096, 128, np.float16), (4096, 4096, 512, np.float16),
+    (1000, 2048, 37, np.float16), (5120, 5120, 512, np.float16), (64, 32, 1, np.float32),
+    (300, 4096, 4096, np.float32), (4096, 4096, 128, np.float32),
+])
+def test_lowrank_correction(M, K, R, dt):
+    """bcq_lowrank_correct: y += sum_r alpha_r u_r (v_r . x) in place, every
+    output against the float64 oracle; a ragged row count, ranks that are not
+    a multiple of 4 or 32, the largest rank and the smallest K."""
+    w = bcq_synth.lowrank(M, K, R, dtype=dt, seed=M + K + R)
+    say("lowrank", M, K, R, np.dtype(dt).name)
+    y = dev(w.y0)
+    bcq.bcq_lowrank_correct(dev(w.u.view(np.int32)), dev(w.v.view(np.int32)), dev(w.alpha),
+                            dev(w.x), y)
+    ref = oracle.lowrank_correct(w.u, w.v, w.alpha, w.x, w.y0)
+    assert rel_l2(y.cpu().numpy(), ref) <= TOL[np.dtype(dt)]

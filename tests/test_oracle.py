@@ -282,3 +282,49 @@ def test_gate_up_rejects_partial_tiles():
     w = bcq_synth.make(40, 128, 2, seed=3)
     with pytest.raises(ValueError):
         oracle.gemv_gate_up(w.signs, w.alpha, w.zero, w.x[0], 2)
+
+
+# ---------------------------------------------------------------- binary low-rank correction
+
+def test_lowrank_worked_example():
+    """The BiLoCo page's v.x = 3.4 as a rank-1 correction of one output."""
+    ex = json.load(open(os.path.join(GOLDEN, "biloco_vx_example.json")))
+    x = np.array(ex["x"])
+    vword = sum(1 << k for k, s in enumerate(ex["v"]) if s > 0)
+    v = np.array([[vword]], dtype=np.uint32)
+    for uword, a, y0, want in ((1, 1.0, 0.0, 3.4), (0, 1.0, 0.0, -3.4), (1, 2.0, 1.0, 7.8)):
+        y = oracle.lowrank_correct(np.array([[uword]], np.uint32), v, [a], x, [y0])
+        assert abs(y[0] - want) < 1e-12
+    assert ex["expected"] == 3.4
+
+
+def test_lowrank_closed_forms():
+    w = bcq_synth.lowrank(5, 64, 7, dtype=np.float64, seed=2)
+    ones_u = np.full_like(w.u, 0xFFFFFFFF)
+    ones_v = np.full_like(w.v, 0xFFFFFFFF)
+    zeros_v = np.zeros_like(w.v)
+    sa, sx = np.sum(w.alpha), np.sum(w.x)
+    y = oracle.lowrank_correct(ones_u, ones_v, w.alpha, w.x, w.y0)
+    assert np.allclose(y, w.y0 + sa * sx, rtol=0, atol=1e-12)
+    y = oracle.lowrank_correct(np.zeros_like(w.u), zeros_v, w.alpha, w.x, w.y0)  # (-1)(-1)
+    assert np.allclose(y, w.y0 + sa * sx, rtol=0, atol=1e-12)
+    y = oracle.lowrank_correct(ones_u, zeros_v, w.alpha, w.x, w.y0)
+    assert np.allclose(y, w.y0 - sa * sx, rtol=0, atol=1e-12)
+
+
+def test_lowrank_brute_force_loops():
+    """Bit-by-bit Python loops over ranks, rows and columns."""
+    w = bcq_synth.lowrank(6, 64, 37, dtype=np.float64, seed=5)
+    want = []
+    for m in range(w.M):
+        acc = float(w.y0[m])
+        for r in range(w.R):
+            dot = 0.0
+            for k in range(w.K):
+                bit = (int(w.v[r][k // 32]) >> (k % 32)) & 1
+                dot += w.x[k] if bit else -w.x[k]
+            ub = (int(w.u[m][r // 32]) >> (r % 32)) & 1
+            acc += float(w.alpha[r]) * (1.0 if ub else -1.0) * dot
+        want.append(acc)
+    got = oracle.lowrank_correct(w.u, w.v, w.alpha, w.x, w.y0)
+    assert np.max(np.abs(got - np.array(want))) < 1e-12
