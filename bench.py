@@ -304,6 +304,25 @@ def secondary(args, bcq, torch, bcq_synth):
         r["rank_%d" % R] = {"us": round(d * 1e3, 3), "sign_bytes": sign_bytes}
     rows["lowrank_correction_4096x4096_b1"] = r
 
+    # dense reconstruction export (bcq_dequantize) of the 4096x4096 store, the
+    # route for batches past the matrix-core kernels: an HBM stream that reads
+    # the planes and scales and writes M x K fp16
+    print("[bench] secondary dequantize", file=sys.stderr, flush=True)
+    w = bcq_synth.config(2)
+    rot = Rotation(w, ROTATE_BYTES, bcq, torch)
+    # distinct outputs, more of them together than the Infinity Cache holds
+    nw = ROTATE_BYTES // (w.M * w.K * 2) + 1
+    Wd = [torch.empty((w.M, w.K), dtype=torch.float16, device="cuda") for _ in range(nw)]
+    r = {}
+    for p in (2, 3, 4):
+        d = time_calls(torch, lambda i, p=p: bcq.bcq_dequantize(rot.stores[i % rot.n], p,
+                                                                Wd[i % nw]), n, 10)
+        nb = algorithmic_bytes(w.M, w.K, p, b=0) + w.M * w.K * 2  # planes + scales read, W written
+        r[str(p)] = {"us": round(d * 1e3, 3), "GBps": round(nb / (d * 1e-3) / 1e9, 1),
+                     "frac_of_peak": round(nb / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    rows["dequantize_4096x4096"] = r
+    del rot, Wd
+
     # 4096x4096 at batch 1 with one store repeated (planes served from the
     # Infinity Cache after the first call): context for the cold numbers
     w = bcq_synth.config(2)

@@ -45,6 +45,7 @@ EXPORTS = (
     "bcq_workspace_bytes",
     "bcq_gemv_mixed_p",
     "bcq_lowrank_correct",
+    "bcq_dequantize",
     "bcq_status_string",
 )
 
@@ -100,6 +101,7 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
                                             ctypes.c_int, vp, sz, vp]),
         "bcq_lowrank_correct": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp, ctypes.c_int,
                                                vp, vp]),
+        "bcq_dequantize": (ctypes.c_int, [st, i32, vp, i32, ctypes.c_int, vp]),
         "bcq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -190,6 +192,13 @@ def bcq_lowrank_correct(u_signs, v_signs, alpha, x, y, z=None, stream=None) -> N
            load().bcq_lowrank_correct(_ptr(u_signs), _ptr(v_signs), _ptr(alpha), R, M, K,
                                       _ptr(x), _ptr(y), _dtype_code(y), _ptr(z),
                                       _stream(stream)))
+
+
+def bcq_dequantize(store: "Store", p: int, W, stream=None) -> None:
+    """Dense ``W[M][K]`` (a device tensor, rows possibly padded: ``W.stride(0)``
+    is the leading dimension) at precision ``p``, in the store's scale dtype."""
+    _check("bcq_dequantize", load().bcq_dequantize(store.ref(), p, _ptr(W), W.stride(0),
+                                                   _dtype_code(W), _stream(stream)))
 
 
 def bcq_workspace_bytes(store: "Store", b: int) -> int:

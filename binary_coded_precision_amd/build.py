@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbcq.so")
-SOURCES = ["bcq_api.hip", "pack.hip", "gemv_lut.hip", "gemm_mfma.hip", "lowrank.hip"]
+SOURCES = ["bcq_api.hip", "pack.hip", "gemv_lut.hip", "gemm_mfma.hip", "lowrank.hip", "dequant.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are kept out of every kernel: hipcc would otherwise

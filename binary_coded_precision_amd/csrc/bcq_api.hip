@@ -199,6 +199,18 @@ bcq_status bcq_gemv_gate_up(const bcq_store *store, int32_t p, const void *x, bc
                                              store->scale_dtype, stream));
 }
 
+bcq_status bcq_dequantize(const bcq_store *store, int32_t p, void *W, int32_t ldw,
+                          bcq_dtype w_dtype, hipStream_t stream) {
+  BCQ_TRY(check_store(store));
+  BCQ_TRY(check_precision(store, p));
+  if (w_dtype != BCQ_F16 && w_dtype != BCQ_F32) return BCQ_ERR_INVALID_ARG;
+  if (w_dtype != store->scale_dtype) return BCQ_ERR_UNSUPPORTED;
+  if (W == nullptr || ldw < store->K) return BCQ_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || ((size_t)ldw * dtype_size(w_dtype)) % 16 != 0) return BCQ_ERR_ALIGNMENT;
+  return hip_status(bcq::launch_dequant(store->bits, store->M, store->K, p, store->alpha[p],
+                                        store->zero[p], W, ldw, w_dtype, stream));
+}
+
 bcq_status bcq_lowrank_correct(const uint32_t *u_signs, const uint32_t *v_signs,
                                const void *alpha, int32_t R, int32_t M, int32_t K, const void *x,
                                void *y, bcq_dtype dtype, float *z, hipStream_t stream) {

@@ -50,6 +50,10 @@ hipError_t launch_gemv_gate_up(const uint32_t *bits, int M, int K, int p, const 
                            const void *zero, const void *x, void *y, bcq_dtype dt,
                            hipStream_t s);
 
+// Dense reconstruction W[m][k] = z + sum_{i<p} alpha_i s_i (bcq_dequantize).
+hipError_t launch_dequant(const uint32_t *bits, int M, int K, int p, const void *alpha,
+                          const void *zero, void *W, int ldw, bcq_dtype dt, hipStream_t s);
+
 // Binary low-rank correction (bcq_lowrank_correct): y += sum_r alpha_r u_r (v_r . x).
 constexpr int kLrMaxRank = BCQ_LOWRANK_MAX_RANK;
 hipError_t launch_lowrank(const uint32_t *u, const uint32_t *v, const void *alpha, int R, int M,

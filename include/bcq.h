@@ -199,6 +199,21 @@ bcq_status bcq_gemv_mixed_p(const bcq_store *store, const int32_t *p_host, const
                             hipStream_t stream);
 
 /*
+ * Dense reconstruction of the weights at precision p (AnyBCQ paper notes,
+ * "Method / key designs": a weight is the offset plus each plane's sign times
+ * its scale), for large batches that go through a dense matrix product:
+ *     W[m][k] = zero_p[m][k/128] + sum_{i<p} alpha_p[i][m][k/128] * s_i[m][k]
+ * formed in fp32 as zero, then + or - each alpha in plane order, and rounded
+ * once (to nearest even) to w_dtype.
+ * W: [M][ldw] (row m starts at W + m*ldw elements), ldw >= K, 16-byte aligned
+ *   with ldw*size a multiple of 16 bytes; columns past K are not written.
+ * w_dtype must equal store->scale_dtype.  Validation and stream behaviour as
+ * in bcq_gemv.
+ */
+bcq_status bcq_dequantize(const bcq_store *store, int32_t p, void *W, int32_t ldw,
+                          bcq_dtype w_dtype, hipStream_t stream);
+
+/*
  * Binary low-rank correction, added in place to a product's output:
  *     y[m] += sum_{r<R} alpha[r] * u[m][r] * (v[r] . x)
  * with u and v in {-1,+1} (BiLoCo summary, "core idea": every rank-one term

@@ -73,6 +73,12 @@ def gate_up(st, p=2, x=FAKE, y=FAKE, xdt=bcq.BCQ_F16, ydt=bcq.BCQ_F16):
     return bcq.load().bcq_gemv_gate_up(ref, p, x, xdt, y, ydt, None)
 
 
+def dequant(st, p=2, W=FAKE, ldw=None, dt=bcq.BCQ_F16):
+    ref = None if st is None else ctypes.byref(st)
+    ldw = (st.K if st is not None else 256) if ldw is None else ldw
+    return bcq.load().bcq_dequantize(ref, p, W, ldw, dt, None)
+
+
 def lowrank(u=FAKE, v=FAKE, a=FAKE, R=16, M=64, K=256, x=FAKE, y=FAKE, dt=bcq.BCQ_F16, z=FAKE):
     return bcq.load().bcq_lowrank_correct(u, v, a, R, M, K, x, y, dt, z, None)
 
@@ -123,6 +129,13 @@ E_ARG, E_UNS, E_ALN = bcq.BCQ_ERR_INVALID_ARG, bcq.BCQ_ERR_UNSUPPORTED, bcq.BCQ_
     (lambda: gate_up(make_store(), x=0), E_ARG),
     (lambda: gate_up(make_store(), y=FAKE + 1), E_ALN),
     (lambda: gate_up(make_store(), xdt=bcq.BCQ_F32), E_UNS),
+    (lambda: dequant(None), E_ARG),
+    (lambda: dequant(make_store(), p=5), E_ARG),
+    (lambda: dequant(make_store(), W=0), E_ARG),
+    (lambda: dequant(make_store(), ldw=255), E_ARG),
+    (lambda: dequant(make_store(), W=FAKE + 8), E_ALN),
+    (lambda: dequant(make_store(), ldw=260), E_ALN),  # 520-byte rows
+    (lambda: dequant(make_store(), dt=bcq.BCQ_F32), E_UNS),
     (lambda: lowrank(R=0), E_ARG),
     (lambda: lowrank(R=4097), E_ARG),
     (lambda: lowrank(M=0), E_ARG),

@@ -818,3 +818,38 @@ def test_lowrank_correction(M, K, R, dt):
                             dev(w.x), y)
     ref = oracle.lowrank_correct(w.u, w.v, w.alpha, w.x, w.y0)
     assert rel_l2(y.cpu().numpy(), ref) <= TOL[np.dtype(dt)]
+
+
+# ---------------------------------------------------------------- dense reconstruction export
+
+@pytest.mark.parametrize("M,K,P,dt,pad", [
+    (4096, 4096, 4, np.float16, 0), (100, 640, 3, np.float16, 8), (33, 128, 2, np.float32, 4),
+    (1000, 14336, 4, np.float16, 0),
+])
+def test_dequantize_export(M, K, P, dt, pad):
+    """bcq_dequantize against the oracle's dense reconstruction at every
+    precision (each weight formed in fp32 and rounded once), padded row
+    columns untouched, and the dense product W . x against the oracle's
+    product (the large-batch route through a dense matrix product)."""
+    w = bcq_synth.make(M, K, P, dtype=dt, seed=M + K, outlier_frac=0.01)
+    st = store_of(w)
+    tdt = torch.float16 if dt == np.float16 else torch.float32
+    for p in range(1, P + 1):
+        say("dequant", M, K, P, p, np.dtype(dt).name, pad)
+        Wb = torch.full((M, K + pad), 9.0, dtype=tdt, device="cuda")
+        bcq.bcq_dequantize(st, p, Wb[:, :K] if pad else Wb)
+        got = Wb[:, :K].cpu().numpy().astype(np.float64)
+        ref = oracle.dequant(w.signs, w.alpha, w.zero, p, K)
+        # |z| + sum |alpha_i| per weight: every sign +1 on the absolute scales
+        mag = oracle.dequant(np.full_like(w.signs, 0xFFFFFFFF), np.abs(w.alpha.astype(np.float64)),
+                             np.abs(w.zero.astype(np.float64)), p, K)
+        # p fp32 additions (sequential-sum bound) then one rounding to the output type
+        u_out = 2.0 ** -11 if dt == np.float16 else 0.0
+        bound = 1.01 * (p * 2.0 ** -24 * mag + u_out * np.abs(ref)) + 2.0 ** -25
+        assert np.all(np.abs(got - ref) <= bound), p
+        if dt == np.float16:  # fp16 scales sum exactly in fp32: the oracle's rounding
+            assert np.mean(got == ref.astype(dt).astype(np.float64)) > 0.999, p
+        if pad:
+            assert (Wb[:, K:].float() == 9.0).all()
+        x = w.x[0].astype(np.float64)
+        assert rel_l2(got @ x, oracle.gemv(w.signs, w.alpha, w.zero, w.x[0], p)) <= TOL[np.dtype(dt)]
