@@ -321,7 +321,35 @@ def secondary(args, bcq, torch, bcq_synth):
         r[str(p)] = {"us": round(d * 1e3, 3), "GBps": round(nb / (d * 1e-3) / 1e9, 1),
                      "frac_of_peak": round(nb / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     rows["dequantize_4096x4096"] = r
-    del rot, Wd
+    del rot
+
+    # prefill through the dense route (bcq_dequantize, then fp16 F.linear on
+    # hipBLASLt) against the matrix-core kernels at the largest batch they take,
+    # and at a batch past it; 4096x4096, p = 4
+    print("[bench] secondary prefill routes", file=sys.stderr, flush=True)
+    F = torch.nn.functional
+    r = {}
+    for b in (256, 1024):
+        w = bcq_synth.make(4096, 4096, 4, b=b, seed=7)
+        rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
+        Y = [torch.empty((b, w.M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+
+        def dense(i):
+            bcq.bcq_dequantize(rot.stores[i % rot.n], 4, Wd[i % nw])
+            torch.mm(rot.x[i % rot.n], Wd[i % nw].t(), out=Y[i % rot.n])
+
+        row = {"dequant_then_gemm_us": round(time_calls(torch, dense, n, 10) * 1e3, 3),
+               "gemm_only_us": round(time_calls(torch, lambda i: torch.mm(
+                   rot.x[i % rot.n], Wd[i % nw].t(), out=Y[i % rot.n]), n, 10) * 1e3, 3)}
+        if b <= bcq.BCQ_MAX_BATCH:
+            ws = bcq.new_workspace(rot.stores[0], b)
+            row["bcq_matrix_cores_us"] = round(time_calls(torch, lambda i: bcq.bcq_gemm_skinny(
+                rot.stores[i % rot.n], 4, rot.x[i % rot.n], Y[i % rot.n], workspace=ws), n, 10) * 1e3, 3)
+            del ws
+        r["b%d" % b] = row
+        del rot, Y
+    rows["prefill_routes_4096x4096_p4"] = r
+    del Wd
 
     # 4096x4096 at batch 1 with one store repeated (planes served from the
     # Infinity Cache after the first call): context for the cold numbers
