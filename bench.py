@@ -4,8 +4,11 @@
 A step is one pass of the batch-1 hot path over one batch of synthetic input:
 ``bcq_gemv`` on the 4096x4096 q_proj-shaped store at p = 2, 3 and 4 (the
 configuration the headline metric is quoted on).  The stores rotate over enough
-distinct copies (> 512 MB) that the 256 MB Infinity Cache cannot hold them, so
-every call reads its planes from HBM.
+distinct copies (> 512 MB) that the 256 MB Infinity Cache cannot hold them:
+every call of a timed region reads its own copy (call c of a replay uses copy
+c mod n, and a per-precision replay makes at least n calls, so every copy is
+cycled), and a 512 MB read-modify-write of a scratch buffer runs right before
+each timed replay, so no copy is cached when timing starts.
 
 Printed: one JSON line with the headline value (GB/s of algorithmic bytes over
 the timed region), a roofline object for the batch-1 kernel (per-launch HIP
@@ -89,6 +92,17 @@ def stored_traffic():
         return None
 
 
+class Flush:
+    """A scratch buffer of twice the Infinity Cache; flush() reads and writes
+    all of it, evicting whatever the caches held."""
+
+    def __init__(self, torch):
+        self.buf = torch.zeros(2 * MALL_BYTES // 4, dtype=torch.int32, device="cuda")
+
+    def __call__(self):
+        self.buf.add_(1)
+
+
 class Rotation:
     """Distinct device copies of one store (and its x/y buffers), used round-robin."""
 
@@ -126,15 +140,18 @@ def capture(torch, body):
     return g
 
 
-def time_calls(torch, launch, n_calls: int, n_warm: int):
+def time_calls(torch, launch, n_calls: int, n_warm: int, flush=None):
     """Average duration (ms) of one launch: n_calls launches (launch(i) for
     i < n_calls) are captured into a HIP graph, replayed once untimed, then
-    timed by HIP events around one replay on the launch stream."""
+    (after flush(), when given) timed by HIP events around one replay on the
+    launch stream."""
     stream = torch.cuda.current_stream()
     for i in range(n_warm):
         launch(i)
     g = capture(torch, lambda: [launch(i) for i in range(n_calls)])
     g.replay()
+    if flush is not None:
+        flush()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -145,7 +162,12 @@ def time_calls(torch, launch, n_calls: int, n_warm: int):
     return t0.elapsed_time(t1) / n_calls
 
 
-def headline(args, bcq, torch, bcq_synth):
+def rotating_calls(torch, rot, launch, n_calls: int, n_warm: int, flush):
+    """time_calls over a rotation: launch(c) reads copy c; every copy is cycled."""
+    return time_calls(torch, lambda i: launch(i % rot.n), max(n_calls, rot.n), n_warm, flush)
+
+
+def headline(args, bcq, torch, bcq_synth, flush):
     w = bcq_synth.config(2)
     rot = Rotation(w, ROTATE_BYTES, bcq, torch)
     M, K = w.M, w.K
@@ -154,18 +176,21 @@ def headline(args, bcq, torch, bcq_synth):
     stream = torch.cuda.current_stream()
 
     def step(s):
-        c = s % rot.n
-        for p in ps:
+        # call k of step s reads copy (3s + k) mod n: no two calls of a step
+        # share a copy, and a copy is read again only n calls later
+        for k, p in enumerate(ps):
+            c = (len(ps) * s + k) % rot.n
             bcq.bcq_gemv(rot.stores[c], p, rot.x[c][0], ys[c])
 
-    # The K timed steps are captured once into a HIP graph (step s uses copy
-    # s mod n); replaying it keeps the GPU queue full, so the timed region
-    # measures the kernels rather than Python's launch rate.  Warmup: W eager
-    # steps, then one untimed replay (the first replay uploads the graph).
+    # The K timed steps are captured once into a HIP graph; replaying it keeps
+    # the GPU queue full, so the timed region measures the kernels rather than
+    # Python's launch rate.  Warmup: W eager steps, then one untimed replay
+    # (the first replay uploads the graph), then the cache flush.
     graph = capture(torch, lambda: [step(s) for s in range(args.steps)])
     for s in range(args.warmup):
         step(s)
     graph.replay()
+    flush()
     torch.cuda.synchronize()
     n_steps = args.steps
     e0 = torch.cuda.Event(enable_timing=True)
@@ -183,9 +208,9 @@ def headline(args, bcq, torch, bcq_synth):
     per_p = {}
     dur = {}
     for p in ps:
-        d = time_calls(torch, lambda i, p=p: bcq.bcq_gemv(rot.stores[i % rot.n], p,
-                                                          rot.x[i % rot.n][0], ys[i % rot.n]),
-                       args.steps, args.warmup)
+        d = rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_gemv(rot.stores[c], p, rot.x[c][0],
+                                                                   ys[c]),
+                           args.steps, args.warmup, flush)
         nb = algorithmic_bytes(M, K, p)
         dur[p] = d
         per_p[str(p)] = {
@@ -213,16 +238,61 @@ def headline(args, bcq, torch, bcq_synth):
             "bytes_per_launch": algorithmic_bytes(M, K, 4),
             "launch_us": round(dur[4] * 1e3, 3),
         },
-        "rotation": {"copies": rot.n, "bytes": rot.bytes},
+        "rotation": {"copies": rot.n, "bytes": rot.bytes,
+                     "headline_calls_timed": len(ps) * n_steps,
+                     "per_p_calls_timed": max(args.steps, rot.n)},
         "workload": w,
     }
     return out
 
 
-def secondary(args, bcq, torch, bcq_synth):
-    """Context rows: the other configurations (not the headline value)."""
+def floor_row(torch, flush, n):
+    """Floors of one launch on this GPU, measured in the same run: an empty
+    kernel, and a plain streaming read (probe kernels, not the BCQ library)
+    of the 4096x4096 and 14336x4096 p = 4 call sizes, cold (distinct buffers
+    over > 512 MB, flushed before the timed replay), best over grid sizes."""
+    import ctypes
+
+    from binary_coded_precision_amd import build as hb
+
+    lib = ctypes.CDLL(hb.PROBE_LIB)
+    lib.bcq_probe_empty.argtypes = [ctypes.c_void_p]
+    lib.bcq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    row = {"empty_launch_us": round(time_calls(
+        torch, lambda i: lib.bcq_probe_empty(st()), max(n, 100), 10) * 1e3, 3)}
+    for nb in (algorithmic_bytes(4096, 4096, 4), algorithmic_bytes(14336, 4096, 4)):
+        nb16 = -(-nb // 16) * 16
+        copies = -(-ROTATE_BYTES // nb16)
+        bufs = [torch.empty(nb16 // 4, dtype=torch.int32, device="cuda").fill_(c)
+                for c in range(copies)]
+        best = None
+        sweep = {}
+        for blocks in (256, 512, 1024, 2048, 4096):
+            d = time_calls(torch, lambda i, blocks=blocks: lib.bcq_probe_read(
+                ctypes.c_void_p(bufs[i % copies].data_ptr()), nb16, blocks,
+                ctypes.c_void_p(sink.data_ptr()), st()), max(n, copies), 10, flush)
+            sweep[str(blocks)] = round(d * 1e3, 3)
+            best = d if best is None else min(best, d)
+        row["read_%d_bytes" % nb] = {"us": round(best * 1e3, 3),
+                                     "GBps": round(nb / (best * 1e-3) / 1e9, 1),
+                                     "frac_of_peak": round(nb / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                     "us_by_workgroups": sweep}
+        del bufs
+    return row
+
+
+def secondary(args, bcq, torch, bcq_synth, flush):
+    """Context rows: the other configurations (not the headline value).  Rows
+    over a rotation are cold like the headline; the warm-cache row and the
+    low-rank correction (one buffer set) are labelled as such."""
     rows = {}
     n = max(20, args.steps // 4)
+
+    print("[bench] secondary floor", file=sys.stderr, flush=True)
+    rows["floor"] = floor_row(torch, flush, n)
 
     # MLP shapes at batch 1, p = 2/3/4: 14336x4096 (gate/up projection, the
     # large-shape target row) and 4096x14336 (down projection, whose K exceeds
@@ -234,9 +304,9 @@ def secondary(args, bcq, torch, bcq_synth):
         ys = [torch.empty(w.M, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
         r = {}
         for p in (2, 3, 4):
-            d = time_calls(torch, lambda i, p=p: bcq.bcq_gemv(rot.stores[i % rot.n], p,
-                                                              rot.x[i % rot.n][0], ys[i % rot.n]),
-                           n, 10)
+            d = rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_gemv(rot.stores[c], p,
+                                                                       rot.x[c][0], ys[c]),
+                               n, 10, flush)
             nb = algorithmic_bytes(w.M, w.K, p)
             r[str(p)] = {"us": round(d * 1e3, 3),
                          "GBps": round(nb / (d * 1e-3) / 1e9, 1),
@@ -255,10 +325,9 @@ def secondary(args, bcq, torch, bcq_synth):
     ys = [torch.empty(Mo, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
     r = {}
     for p in (2, 3, 4):
-        d = time_calls(torch, lambda i, p=p: bcq.bcq_gemv_gate_up(rot.stores[i % rot.n], p,
-                                                                  rot.x[i % rot.n][0],
-                                                                  ys[i % rot.n]),
-                       n, 10)
+        d = rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_gemv_gate_up(rot.stores[c], p,
+                                                                           rot.x[c][0], ys[c]),
+                           n, 10, flush)
         nb = algorithmic_bytes(2 * Mo, 4096, p) - Mo * 2  # Mo outputs, not 2 * Mo
         r[str(p)] = {"us": round(d * 1e3, 3),
                      "GBps": round(nb / (d * 1e-3) / 1e9, 1),
@@ -275,10 +344,8 @@ def secondary(args, bcq, torch, bcq_synth):
         w = bcq_synth.make(M, 4096, 4, seed=10 + M, name="qkv_%dx4096_b1" % M)
         rot = Rotation(w, ROTATE_BYTES, bcq, torch)
         ys = [torch.empty(M, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
-        stores[M] = {p: time_calls(torch, lambda i, p=p: bcq.bcq_gemv(rot.stores[i % rot.n], p,
-                                                                     rot.x[i % rot.n][0],
-                                                                     ys[i % rot.n]), n, 10)
-                     for p in (2, 3, 4)}
+        stores[M] = {p: rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_gemv(
+            rot.stores[c], p, rot.x[c][0], ys[c]), n, 10, flush) for p in (2, 3, 4)}
         del rot, ys
     for p in (2, 3, 4):
         nb = algorithmic_bytes(6144, 4096, p)
@@ -288,7 +355,8 @@ def secondary(args, bcq, torch, bcq_synth):
     rows["qkv_concatenated_6144x4096_b1"] = r
 
     # binary low-rank correction y += sum_r alpha_r u_r (v_r . x) on a 4096x4096
-    # output (BiLoCo's ranks 16..512); each timed call adds to the same y
+    # output (BiLoCo's ranks 16..512); each timed call adds to the same y, so
+    # its sign vectors stay cached (warm)
     print("[bench] secondary low-rank", file=sys.stderr, flush=True)
     r = {}
     for R in (16, 128, 512):
@@ -301,7 +369,7 @@ def secondary(args, bcq, torch, bcq_synth):
         zz = torch.empty(R, dtype=torch.float32, device="cuda")
         d = time_calls(torch, lambda i: bcq.bcq_lowrank_correct(u, v, a, xx, yy, zz), n, 10)
         sign_bytes = 4096 * ((R + 31) // 32) * 4 + R * 4096 // 8
-        r["rank_%d" % R] = {"us": round(d * 1e3, 3), "sign_bytes": sign_bytes}
+        r["rank_%d" % R] = {"us": round(d * 1e3, 3), "sign_bytes": sign_bytes, "cache": "warm"}
     rows["lowrank_correction_4096x4096_b1"] = r
 
     # dense reconstruction export (bcq_dequantize) of the 4096x4096 store, the
@@ -315,8 +383,9 @@ def secondary(args, bcq, torch, bcq_synth):
     Wd = [torch.empty((w.M, w.K), dtype=torch.float16, device="cuda") for _ in range(nw)]
     r = {}
     for p in (2, 3, 4):
-        d = time_calls(torch, lambda i, p=p: bcq.bcq_dequantize(rot.stores[i % rot.n], p,
-                                                                Wd[i % nw]), n, 10)
+        d = rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_dequantize(rot.stores[c], p,
+                                                                         Wd[c % nw]),
+                           n, 10, flush)
         nb = algorithmic_bytes(w.M, w.K, p, b=0) + w.M * w.K * 2  # planes + scales read, W written
         r[str(p)] = {"us": round(d * 1e3, 3), "GBps": round(nb / (d * 1e-3) / 1e9, 1),
                      "frac_of_peak": round(nb / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -327,24 +396,24 @@ def secondary(args, bcq, torch, bcq_synth):
     # hipBLASLt) against the matrix-core kernels at the largest batch they take,
     # and at a batch past it; 4096x4096, p = 4
     print("[bench] secondary prefill routes", file=sys.stderr, flush=True)
-    F = torch.nn.functional
     r = {}
     for b in (256, 1024):
         w = bcq_synth.make(4096, 4096, 4, b=b, seed=7)
         rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
         Y = [torch.empty((b, w.M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
 
-        def dense(i):
-            bcq.bcq_dequantize(rot.stores[i % rot.n], 4, Wd[i % nw])
-            torch.mm(rot.x[i % rot.n], Wd[i % nw].t(), out=Y[i % rot.n])
+        def dense(c):
+            bcq.bcq_dequantize(rot.stores[c], 4, Wd[c % nw])
+            torch.mm(rot.x[c], Wd[c % nw].t(), out=Y[c])
 
-        row = {"dequant_then_gemm_us": round(time_calls(torch, dense, n, 10) * 1e3, 3),
-               "gemm_only_us": round(time_calls(torch, lambda i: torch.mm(
-                   rot.x[i % rot.n], Wd[i % nw].t(), out=Y[i % rot.n]), n, 10) * 1e3, 3)}
+        row = {"dequant_then_gemm_us": round(rotating_calls(torch, rot, dense, n, 10, flush)
+                                             * 1e3, 3),
+               "gemm_only_us": round(rotating_calls(torch, rot, lambda c: torch.mm(
+                   rot.x[c], Wd[c % nw].t(), out=Y[c]), n, 10, flush) * 1e3, 3)}
         if b <= bcq.BCQ_MAX_BATCH:
             ws = bcq.new_workspace(rot.stores[0], b)
-            row["bcq_matrix_cores_us"] = round(time_calls(torch, lambda i: bcq.bcq_gemm_skinny(
-                rot.stores[i % rot.n], 4, rot.x[i % rot.n], Y[i % rot.n], workspace=ws), n, 10) * 1e3, 3)
+            row["bcq_matrix_cores_us"] = round(rotating_calls(torch, rot, lambda c: bcq.bcq_gemm_skinny(
+                rot.stores[c], 4, rot.x[c], Y[c], workspace=ws), n, 10, flush) * 1e3, 3)
             del ws
         r["b%d" % b] = row
         del rot, Y
@@ -368,14 +437,10 @@ def secondary(args, bcq, torch, bcq_synth):
     Y = [torch.empty((w.b, w.M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
     pr = [int(p) for p in w.p_req]
     ws = bcq.new_workspace(rot.stores[0], w.b)
-    d_mixed = time_calls(torch, lambda i: bcq.bcq_gemv_mixed_p(rot.stores[i % rot.n], pr,
-                                                              rot.x[i % rot.n], Y[i % rot.n],
-                                                              workspace=ws),
-                         n, 10)
-    d_uni = time_calls(torch, lambda i: bcq.bcq_gemm_skinny(rot.stores[i % rot.n], max(pr),
-                                                           rot.x[i % rot.n], Y[i % rot.n],
-                                                           workspace=ws),
-                       n, 10)
+    d_mixed = rotating_calls(torch, rot, lambda c: bcq.bcq_gemv_mixed_p(
+        rot.stores[c], pr, rot.x[c], Y[c], workspace=ws), n, 10, flush)
+    d_uni = rotating_calls(torch, rot, lambda c: bcq.bcq_gemm_skinny(
+        rot.stores[c], max(pr), rot.x[c], Y[c], workspace=ws), n, 10, flush)
     nb = mixed_bytes(w.M, w.K, pr)
     rows["mixed_p_4096x4096_b8"] = {
         "p_req": pr,
@@ -385,7 +450,9 @@ def secondary(args, bcq, torch, bcq_synth):
     }
     del rot, Y, ws
 
-    # small batches (MLP shapes, p = 3) and matrix-core batches (p = 4)
+    # small batches (MLP shapes, p = 3) and matrix-core batches (p = 4).  The
+    # batches of 2..15 are timed on both routes (BCQ_FORCE_PATH=lut: vector-ALU
+    # tables; =mfma: matrix cores); "us" is the default route's time.
     for (M, K), b, p in [((4096, 4096), 2, 4), ((4096, 4096), 4, 4), ((4096, 4096), 8, 4),
                          ((14336, 4096), 4, 3), ((14336, 4096), 8, 3), ((4096, 14336), 4, 3),
                          ((4096, 14336), 8, 3),
@@ -395,38 +462,145 @@ def secondary(args, bcq, torch, bcq_synth):
         w = bcq_synth.make(M, K, 4, b=b, seed=5)
         rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
         Y = [torch.empty((b, M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
-        ws = bcq.new_workspace(rot.stores[0], b)  # None where the call needs none
-        d = time_calls(torch, lambda i: bcq.bcq_gemm_skinny(rot.stores[i % rot.n], p,
-                                                           rot.x[i % rot.n], Y[i % rot.n],
-                                                           workspace=ws), n, 10)
-        t = d * 1e-3
         nb = algorithmic_bytes(M, K, p, b)
-        row = {"us": round(t * 1e6, 3), "GBps": round(nb / t / 1e9, 1)}
-        if b >= 16:
-            row["mfma_util"] = round(2.0 * M * K * b / t / 2.5e15, 4)
+        row = {}
+        for route in ((None, "lut", "mfma") if b < 16 else (None,)):
+            with force_path(route):
+                ws = bcq.new_workspace(rot.stores[0], b)  # None where the call needs none
+                d = rotating_calls(torch, rot, lambda c: bcq.bcq_gemm_skinny(
+                    rot.stores[c], p, rot.x[c], Y[c], workspace=ws), n, 10, flush)
+                del ws
+            t = d * 1e-3
+            key = "us" if route is None else "us_" + route
+            row[key] = round(t * 1e6, 3)
+            if route is None:
+                row["GBps"] = round(nb / t / 1e9, 1)
+                if b >= 16:
+                    row["mfma_util"] = round(2.0 * M * K * b / t / 2.5e15, 4)
         rows["skinny_%dx%d_b%d_p%d" % (M, K, b, p)] = row
-        del rot, Y, ws
+        del rot, Y
     return rows
 
 
+class force_path:
+    """Sets BCQ_FORCE_PATH for the duration of a with-block (None: unset)."""
+
+    def __init__(self, route):
+        self.route = route
+
+    def __enter__(self):
+        self.old = os.environ.pop("BCQ_FORCE_PATH", None)
+        if self.route is not None:
+            os.environ["BCQ_FORCE_PATH"] = self.route
+
+    def __exit__(self, *exc):
+        os.environ.pop("BCQ_FORCE_PATH", None)
+        if self.old is not None:
+            os.environ["BCQ_FORCE_PATH"] = self.old
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s: float):
-    """The float64 oracle as it stands, single-threaded, on full 4096x4096 calls."""
+    """The float64 oracle as it stands, on full 4096x4096 calls at p = 2, 3, 4:
+    single-threaded, then row-partitioned over the host's cores (one thread per
+    core, each calling the unchanged oracle on its rows; ctypes releases the
+    interpreter lock during the call).  The headline figure is the all-core
+    leg; the single-thread one is reported beside it."""
+    import concurrent.futures as cf
+
     import oracle
 
     oracle.gemv(w.signs, w.alpha, w.zero, w.x[0], 2)  # load / build outside the timing
-    t0 = time.perf_counter()
-    reps, nbytes = 0, 0
-    while True:
-        for p in (2, 3, 4):
-            oracle.gemv(w.signs, w.alpha, w.zero, w.x[0], p)
-            nbytes += algorithmic_bytes(w.M, w.K, p)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
+
+    def run(call, seconds):
+        t0 = time.perf_counter()
+        reps, nbytes = 0, 0
+        while True:
+            for p in (2, 3, 4):
+                call(p)
+                nbytes += algorithmic_bytes(w.M, w.K, p)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        return reps, nbytes, time.perf_counter() - t0
+
+    reps1, b1, t1 = run(lambda p: oracle.gemv(w.signs, w.alpha, w.zero, w.x[0], p), budget_s / 2)
+    # the GPU box gives one GPU's job 16 cores whatever the host reports
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    bounds = np.linspace(0, w.M, nthreads + 1).astype(int)
+    parts = [(np.ascontiguousarray(w.signs[:, lo:hi]), np.ascontiguousarray(w.alpha[:, lo:hi]),
+              np.ascontiguousarray(w.zero[lo:hi])) for lo, hi in zip(bounds[:-1], bounds[1:])]
+    x0 = w.x[0]
+    with cf.ThreadPoolExecutor(max_workers=nthreads) as ex:
+        def all_cores(p):
+            list(ex.map(lambda part: oracle.gemv(part[0], part[1], part[2], x0, p), parts))
+        all_cores(2)
+        repsn, bn, tn = run(all_cores, budget_s / 2)
+    return {"value": round(bn / tn / 1e9, 4), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": "%d full steps (bcq_gemv 4096x4096 at p=2,3,4) in %.1f s, float64 C loops, "
+                      "rows split over %d threads; single thread: %d steps in %.1f s = %.4f GB/s"
+                      % (repsn, tn, nthreads, reps1, t1, b1 / t1 / 1e9),
+            "single_thread_value": round(b1 / t1 / 1e9, 4),
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def trace_summary(path: str, last: int) -> None:
+    """Per-kernel duration statistics from a rocprofv3 kernel-trace CSV: for
+    each (kernel, grid) with at least 10 dispatches, count, mean, median, p10
+    and p90 in microseconds over all its dispatches, and over the last `last`
+    dispatches of its longest run of consecutive dispatches (in a bench run,
+    the timed replay of a cold per-precision graph)."""
+    import csv
+
+    rows = list(csv.DictReader(open(path, newline="")))
+    key_name = "Kernel_Name"
+    grid_keys = [k for k in ("Grid_Size", "Grid_Size_X") if rows and k in rows[0]]
+    seq = []
+    for r in rows:
+        name = r[key_name]
+        grid = r[grid_keys[0]] if grid_keys else "?"
+        t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+        seq.append((int(r.get("Dispatch_Id", len(seq))), name, grid, t))
+    seq.sort()
+
+    def stats(v):
+        v = np.sort(np.asarray(v))
+        return {"n": int(v.size), "mean": round(float(v.mean()), 3),
+                "median": round(float(np.median(v)), 3),
+                "p10": round(float(np.percentile(v, 10)), 3),
+                "p90": round(float(np.percentile(v, 90)), 3)}
+
+    groups = {}
+    runs = {}
+    prev, cur = None, []
+    for _, name, grid, t in seq + [(None, None, None, None)]:
+        k = (name, grid)
+        if k != prev and prev is not None:
+            if len(cur) > len(runs.get(prev, [])):
+                runs[prev] = cur
+            cur = []
+        if name is None:
             break
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d full steps (bcq_gemv 4096x4096 at p=2,3,4), %.1f s, float64 C loops, "
-                      "1 thread" % (reps, dt)}
+        groups.setdefault(k, []).append(t)
+        cur.append(t)
+        prev = k
+    for k, v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        if len(v) < 10:
+            continue
+        out = {"kernel": k[0][:160], "grid": k[1], "all": stats(v)}
+        run = runs.get(k, [])
+        if len(run) >= 10:
+            out["longest_run_last"] = stats(run[-last:])
+        print(json.dumps(out))
 
 
 def main():
@@ -444,7 +618,15 @@ def main():
                          "on the 4096x4096 store (for per-dispatch HBM counters)")
     ap.add_argument("--counter-batch", type=int, default=1, metavar="B",
                     help="with --counter-run: run bcq_gemm_skinny at batch B (p = 4) instead")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="only summarise a rocprofv3 kernel-trace CSV (no GPU needed)")
+    ap.add_argument("--trace-last", type=int, default=58,
+                    help="with --trace-summary: dispatches taken from the end of each "
+                         "kernel's longest run")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.trace_last)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the BCQ product runs on a single MI355X "
               "(sharding across GPUs is not implemented); use --gpus 1", file=sys.stderr)
@@ -487,13 +669,14 @@ def main():
                           "copies": rot.n}))
         return
 
+    flush = Flush(torch)
     print("[bench] headline", file=sys.stderr, flush=True)
-    h = headline(args, bcq, torch, bcq_synth)
+    h = headline(args, bcq, torch, bcq_synth, flush)
     w = h.pop("workload")
     sec = None
     if not args.no_secondary:
         print("[bench] secondary", file=sys.stderr, flush=True)
-        sec = secondary(args, bcq, torch, bcq_synth)
+        sec = secondary(args, bcq, torch, bcq_synth, flush)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
@@ -509,7 +692,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {
             "workload": "bcq_gemv q_proj-shaped 4096x4096, batch 1, one 4-plane store at "
@@ -518,6 +701,9 @@ def main():
             "M": 4096, "K": 4096, "b": 1, "p": [2, 3, 4], "planes_stored": 4,
             "rotating_copies": h["rotation"]["copies"],
             "rotating_bytes": h["rotation"]["bytes"],
+            "headline_calls_timed": h["rotation"]["headline_calls_timed"],
+            "per_p_calls_timed": h["rotation"]["per_p_calls_timed"],
+            "cache_flush_bytes": 2 * MALL_BYTES,
         },
         "per_p": h["per_p"],
         "roofline": h["roofline"],

@@ -138,6 +138,48 @@ def _ptr(t) -> ctypes.c_void_p:
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
+def _need_vec(name: str, t, n: int) -> None:
+    """t is a device tensor with unit inner stride holding at least n elements
+    from its first element on."""
+    if t is None:
+        raise ValueError("%s is None" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dim() > 1 and t.stride(-1) != 1:
+        raise ValueError("%s must have unit inner stride" % name)
+    if t.dim() <= 1 and t.numel() > 1 and t.stride(0) != 1:
+        raise ValueError("%s must be contiguous" % name)
+    if t.numel() < n:
+        raise ValueError("%s holds %d elements, %d needed" % (name, t.numel(), n))
+
+
+def _need_mat(name: str, t, rows: int, cols: int) -> None:
+    """t is a 2-D device tensor of at least rows x cols with unit inner stride
+    (rows may be padded: stride(0) is the leading dimension)."""
+    if t is None or t.dim() != 2:
+        raise ValueError("%s must be a 2-D tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.stride(1) != 1:
+        raise ValueError("%s must have unit inner stride" % name)
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError("%s is %dx%d, at least %dx%d needed" % (name, t.shape[0], t.shape[1],
+                                                                rows, cols))
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError("%s rows overlap (stride(0) < shape[1])" % name)
+
+
+def _check_store_tensors(store: "Store", ps) -> None:
+    """The store's buffers are as large as the descriptor says for precisions ps."""
+    _need_vec("store.bits", store.bits,
+              bcq_packed_bytes(store.planes, store.M, store.K) // store.bits.element_size())
+    G = store.K // BCQ_GROUP
+    for p in set(int(v) for v in ps):
+        if 1 <= p <= store.planes and p in store.alpha and p in store.zero:
+            _need_vec("store.alpha[%d]" % p, store.alpha[p], p * store.M * G)
+            _need_vec("store.zero[%d]" % p, store.zero[p], store.M * G)
+
+
 # ----------------------------------------------------------------------------- C names
 
 
@@ -152,17 +194,28 @@ def bcq_packed_bytes(P: int, M: int, K: int) -> int:
 def bcq_pack_planes(signs, P: int, M: int, K: int, packed, stream=None) -> None:
     """``signs``: int32/uint32 device tensor [P][M][K/32]; ``packed``: device tensor of
     ``bcq_packed_bytes(P, M, K)`` bytes."""
+    n = bcq_packed_bytes(P, M, K)
+    if n:
+        _need_vec("signs", signs, P * M * (K // 32))
+        _need_vec("packed", packed, n // packed.element_size())
     _check("bcq_pack_planes",
            load().bcq_pack_planes(_ptr(signs), P, M, K, _ptr(packed), _stream(stream)))
 
 
 def bcq_unpack_planes(packed, P: int, M: int, K: int, signs, stream=None) -> None:
+    n = bcq_packed_bytes(P, M, K)
+    if n:
+        _need_vec("packed", packed, n // packed.element_size())
+        _need_vec("signs", signs, P * M * (K // 32))
     _check("bcq_unpack_planes",
            load().bcq_unpack_planes(_ptr(packed), P, M, K, _ptr(signs), _stream(stream)))
 
 
 def bcq_gemv(store: "Store", p: int, x, y, stream=None) -> None:
     """``y[M] = product at precision p`` of the device vector ``x[K]``."""
+    _need_vec("x", x, store.K)
+    _need_vec("y", y, store.M)
+    _check_store_tensors(store, [p])
     _check("bcq_gemv", load().bcq_gemv(store.ref(), p, _ptr(x), _dtype_code(x), _ptr(y),
                                        _dtype_code(y), _stream(stream)))
 
@@ -170,6 +223,9 @@ def bcq_gemv(store: "Store", p: int, x, y, stream=None) -> None:
 def bcq_gemv_gate_up(store: "Store", p: int, x, y, stream=None) -> None:
     """``y[M/2] = silu(gate . x) * (up . x)`` for a store whose 16-row tiles hold
     8 gate rows then the matching 8 up rows (see ``include/bcq.h``)."""
+    _need_vec("x", x, store.K)
+    _need_vec("y", y, store.M // 2)
+    _check_store_tensors(store, [p])
     _check("bcq_gemv_gate_up", load().bcq_gemv_gate_up(store.ref(), p, _ptr(x), _dtype_code(x),
                                                        _ptr(y), _dtype_code(y),
                                                        _stream(stream)))
@@ -188,6 +244,9 @@ def bcq_lowrank_correct(u_signs, v_signs, alpha, x, y, z=None, stream=None) -> N
         raise ValueError("alpha, x and y must share one dtype")
     if z is None:
         z = torch.empty(R, dtype=torch.float32, device=y.device)
+    _need_vec("u_signs", u_signs, M * ((R + 31) // 32))
+    _need_vec("v_signs", v_signs, R * (K // 32))
+    _need_vec("z", z, R)
     _check("bcq_lowrank_correct",
            load().bcq_lowrank_correct(_ptr(u_signs), _ptr(v_signs), _ptr(alpha), R, M, K,
                                       _ptr(x), _ptr(y), _dtype_code(y), _ptr(z),
@@ -197,6 +256,8 @@ def bcq_lowrank_correct(u_signs, v_signs, alpha, x, y, z=None, stream=None) -> N
 def bcq_dequantize(store: "Store", p: int, W, stream=None) -> None:
     """Dense ``W[M][K]`` (a device tensor, rows possibly padded: ``W.stride(0)``
     is the leading dimension) at precision ``p``, in the store's scale dtype."""
+    _need_mat("W", W, store.M, store.K)
+    _check_store_tensors(store, [p])
     _check("bcq_dequantize", load().bcq_dequantize(store.ref(), p, _ptr(W), W.stride(0),
                                                    _dtype_code(W), _stream(stream)))
 
@@ -224,6 +285,9 @@ def bcq_gemm_skinny(store: "Store", p: int, X, Y, workspace=None, stream=None) -
     ``workspace=None`` allocates the workspace the call needs (through torch);
     pass one from :func:`new_workspace` to keep allocation out of a hot loop."""
     b = X.shape[0]
+    _need_mat("X", X, b, store.K)
+    _need_mat("Y", Y, b, store.M)
+    _check_store_tensors(store, [p])
     if workspace is None:
         workspace = new_workspace(store, b)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -237,6 +301,11 @@ def bcq_gemv_mixed_p(store: "Store", p_host: Sequence[int], X, Y, workspace=None
                      stream=None) -> None:
     """Request r at its own precision ``p_host[r]`` (workspace as in :func:`bcq_gemm_skinny`)."""
     b = X.shape[0]
+    if len(p_host) != b:
+        raise ValueError("p_host has %d entries for %d requests" % (len(p_host), b))
+    _need_mat("X", X, b, store.K)
+    _need_mat("Y", Y, b, store.M)
+    _check_store_tensors(store, p_host)
     ps = (ctypes.c_int32 * b)(*[int(v) for v in p_host])
     if workspace is None:
         workspace = new_workspace(store, b)
@@ -295,22 +364,27 @@ class Store:
         """
         import torch
 
+        import contextlib
+
         P, M, W = signs.shape
         K = W * 32
         nbytes = bcq_packed_bytes(P, M, K)
         if nbytes == 0:
             raise BCQError("bcq_packed_bytes", BCQ_ERR_INVALID_ARG)
-        dsigns = torch.from_numpy(np.ascontiguousarray(signs).view(np.int32)).to(device)
-        packed = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
-        bcq_pack_planes(dsigns, P, M, K, packed, stream)
-        if alpha_p is None:
-            a = torch.from_numpy(np.ascontiguousarray(alpha)).to(device)
-            z = torch.from_numpy(np.ascontiguousarray(zero)).to(device)
-            at = {p: a for p in range(1, P + 1)}
-            zt = {p: z for p in range(1, P + 1)}
-        else:
-            at = {p: torch.from_numpy(np.ascontiguousarray(alpha_p[p])).to(device)
-                  for p in range(1, P + 1)}
-            zt = {p: torch.from_numpy(np.ascontiguousarray(zero_p[p])).to(device)
-                  for p in range(1, P + 1)}
+        # uploads and the pack run on one stream, in that order
+        ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            dsigns = torch.from_numpy(np.ascontiguousarray(signs).view(np.int32)).to(device)
+            packed = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
+            bcq_pack_planes(dsigns, P, M, K, packed)
+            if alpha_p is None:
+                a = torch.from_numpy(np.ascontiguousarray(alpha)).to(device)
+                z = torch.from_numpy(np.ascontiguousarray(zero)).to(device)
+                at = {p: a for p in range(1, P + 1)}
+                zt = {p: z for p in range(1, P + 1)}
+            else:
+                at = {p: torch.from_numpy(np.ascontiguousarray(alpha_p[p])).to(device)
+                      for p in alpha_p}
+                zt = {p: torch.from_numpy(np.ascontiguousarray(zero_p[p])).to(device)
+                      for p in zero_p}
         return cls(M, K, P, packed, at, zt)

@@ -17,6 +17,10 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbcq.so")
 SOURCES = ["bcq_api.hip", "pack.hip", "gemv_lut.hip", "gemm_mfma.hip", "lowrank.hip", "dequant.hip"]
+# Measurement kernels of the benchmark's floor row (empty launch, plain
+# streaming read): a library of their own, outside the BCQ ABI.
+PROBE_LIB = os.path.join(HERE, "libbcq_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are kept out of every kernel: hipcc would otherwise
@@ -47,19 +51,26 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), verbose: bool = False) -> str:
-    """Compile every source and link ``libbcq.so``; returns the library path."""
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra_flags), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+def _link(lib: str, objs) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + list(objs)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(extra_flags=(), verbose: bool = False) -> str:
+    """Compile every source, link ``libbcq.so`` (and the benchmark's
+    ``libbcq_probe.so``); returns the BCQ library's path."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, extra_flags), srcs)))
+    _link(LIB, [objs[s] for s in SOURCES])
+    _link(PROBE_LIB, [objs[s] for s in PROBE_SOURCES])
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -2,6 +2,9 @@
 // the kernels.  Every check runs before any HIP call, so a rejected call
 // enqueues nothing and touches no device state.
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "bcq_internal.h"
 
@@ -21,9 +24,41 @@ constexpr int32_t kMaxK = 1 << 20;
 // faster (4096x14336: 20.0 vs 22.6 us; 2048x2048: 5.2 vs 6.1 us).
 constexpr int32_t kMfMinBatch = 3;
 
+// Route switch for A/B measurement: BCQ_FORCE_PATH=lut sends every batched
+// fp16 call (2 requests and more) to the vector-ALU table kernel, =mfma sends
+// it to the matrix cores; unset or any other value keeps the rule below.
+// Read at every call, so a process can compare both routes.  fp32 batches
+// always use the tables (the matrix-core kernels take fp16 only) and batch 1
+// always uses the batch-1 kernel.
+enum class Route { kRule, kTables, kMatrixCores };
+
+Route forced_route() {
+  const char *v = getenv("BCQ_FORCE_PATH");
+  if (v == nullptr) return Route::kRule;
+  if (strcmp(v, "lut") == 0) return Route::kTables;
+  if (strcmp(v, "mfma") == 0) return Route::kMatrixCores;
+  return Route::kRule;
+}
+
 bool on_matrix_cores(const bcq_store *st, int32_t b) {
-  return st->scale_dtype == BCQ_F16 &&
-         (b >= kMfMinBatch || (b == 2 && st->K > 2048 && bcq::mfma_whole_k(st->M, st->K, b)));
+  if (st->scale_dtype != BCQ_F16 || b < 2) return false;
+  switch (forced_route()) {
+    case Route::kTables:
+      return false;
+    case Route::kMatrixCores:
+      return true;
+    case Route::kRule:
+      break;
+  }
+  return b >= kMfMinBatch || (b == 2 && st->K > 2048 && bcq::mfma_whole_k(st->M, st->K, b));
+}
+
+// BCQ_LOG=1 prints each product call's route to stderr.
+void log_route(const char *fn, const bcq_store *st, int32_t b, const char *route) {
+  const char *v = getenv("BCQ_LOG");
+  if (v == nullptr || strcmp(v, "1") != 0) return;
+  fprintf(stderr, "[bcq] %s M=%d K=%d b=%d dtype=%s -> %s\n", fn, st->M, st->K, b,
+          st->scale_dtype == BCQ_F16 ? "f16" : "f32", route);
 }
 
 size_t dtype_size(bcq_dtype d) { return d == BCQ_F16 ? 2 : 4; }
@@ -182,6 +217,7 @@ bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype 
   BCQ_TRY(check_dtypes(store, x_dtype, y_dtype));
   if (x == nullptr || y == nullptr) return BCQ_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(y, dtype_size(y_dtype))) return BCQ_ERR_ALIGNMENT;
+  log_route("bcq_gemv", store, 1, "batch-1 tables");
   return hip_status(bcq::launch_gemv_lut(store->bits, store->M, store->K, p, store->alpha[p],
                                          store->zero[p], x, y, store->scale_dtype, stream));
 }
@@ -244,9 +280,15 @@ bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int
   BCQ_TRY(check_workspace(store, b, workspace, workspace_bytes));
   const char *Xc = static_cast<const char *>(X);
   char *Yc = static_cast<char *>(Y);
-  if (on_matrix_cores(store, b))
+  if (on_matrix_cores(store, b)) {
+    log_route("bcq_gemm_skinny", store, b,
+              bcq::mfma_whole_k(store->M, store->K, b < bcq::kMfMaxBatch ? b : bcq::kMfMaxBatch)
+                  ? "matrix cores, whole K"
+                  : "matrix cores, split K");
     return run_mfma_batches(store, p, nullptr, Xc, b, ldx, Yc, ldy, workspace, bcq::kMfMaxBatch,
                             stream);
+  }
+  log_route("bcq_gemm_skinny", store, b, b == 1 ? "batch-1 tables" : "vector-ALU tables");
   int32_t ps[BCQ_MAX_BATCH];
   for (int32_t r = 0; r < b; ++r) ps[r] = p;
   return run_table_batches(store, ps, Xc, b, ldx, Yc, ldy, stream);
@@ -274,9 +316,12 @@ bcq_status bcq_gemv_mixed_p(const bcq_store *store, const int32_t *p_host, const
   for (int32_t r = 0; r < b; ++r)
     shared = shared && store->alpha[p_host[r]] == store->alpha[pmax] &&
              store->zero[p_host[r]] == store->zero[pmax];
-  if (on_matrix_cores(store, b) && shared)
+  if (on_matrix_cores(store, b) && shared) {
+    log_route("bcq_gemv_mixed_p", store, b, "matrix cores, per-plane accumulators");
     return run_mfma_batches(store, pmax, p_host, Xc, b, ldx, Yc, ldy, workspace,
                             bcq::kMfMaxMixed, stream);
+  }
+  log_route("bcq_gemv_mixed_p", store, b, "vector-ALU tables, per-request scale slots");
   return run_table_batches(store, p_host, Xc, b, ldx, Yc, ldy, stream);
 }
 

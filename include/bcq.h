@@ -103,6 +103,12 @@ size_t bcq_packed_bytes(int32_t P, int32_t M, int32_t K);
 
 /*
  * Pack canonical sign planes into the device layout.
+ * Defined by: AnyBCQ paper notes, "Method / key designs" (direct bit-plane
+ * kernel): the planes are consumed one at a time and a precision-p product
+ * loads only the first p of them, so each plane is stored as its own
+ * contiguous array and the first p planes form a prefix of the buffer.  The
+ * planes hold -1/+1 entries ("Method / key designs", the weight as a sum of
+ * scaled binary planes), one bit each.
  * signs:  [P][M][K/32] uint32; column k of plane i, row m is bit (k mod 32),
  *         least significant first, of word [i][m][k/32]; set = +1, clear = -1.
  *         4-byte aligned.
@@ -112,13 +118,29 @@ size_t bcq_packed_bytes(int32_t P, int32_t M, int32_t K);
 bcq_status bcq_pack_planes(const uint32_t *signs, int32_t P, int32_t M, int32_t K,
                            uint32_t *packed, hipStream_t stream);
 
-/* Inverse of bcq_pack_planes (for tests and inspection). */
+/*
+ * Inverse of bcq_pack_planes (for tests and inspection): the canonical
+ * [P][M][K/32] sign words back from the device layout, bit-exact.  Same
+ * source as bcq_pack_planes (AnyBCQ paper notes, "Method / key designs": one
+ * bit per -1/+1 plane entry).  signs is fully overwritten; alignment and
+ * validation as in bcq_pack_planes.
+ */
 bcq_status bcq_unpack_planes(const uint32_t *packed, int32_t P, int32_t M, int32_t K,
                              uint32_t *signs, hipStream_t stream);
 
 /*
  * y = BCQ product at precision p for one activation vector (batch 1).
+ * Defined by: AnyBCQ paper notes, "Method / key designs" (direct bit-plane
+ * kernel): for each of the first p planes the product with x is additions and
+ * subtractions of activations, scaled by that plane's factor and accumulated;
+ * the output is written once the p-th plane is done, and a lower precision
+ * reads fewer planes.  The group-wise offset term comes from "Training
+ * strategy" (asymmetric BCQ, g = 128).  The mlsanity page's AnyBCQ abstract
+ * states the same kernel goal: compute directly on the bit-planes and touch
+ * only the planes of the precision a request asks for.
  * x: [K], 16-byte aligned.  y: [M], element aligned; every element written.
+ * Rejected arguments (null pointers, p outside [1, planes], a missing table
+ * for p, mixed dtypes, misalignment) return an error and enqueue nothing.
  */
 bcq_status bcq_gemv(const bcq_store *store, int32_t p, const void *x, bcq_dtype x_dtype,
                     void *y, bcq_dtype y_dtype, hipStream_t stream);
@@ -143,6 +165,11 @@ bcq_status bcq_gemv_gate_up(const bcq_store *store, int32_t p, const void *x, bc
 
 /*
  * Y[r] = BCQ product at precision p for each of b activation rows X[r].
+ * Defined by: the product of bcq_gemv (AnyBCQ paper notes, "Method / key
+ * designs") applied to every row of a decode batch; one read of the first p
+ * planes serves all b requests.  The BiLoCo summary ("results: speed") notes
+ * that add/subtract work grows with the batch while the weight read does not,
+ * which is why larger batches decode weights for the matrix cores.
  * X: [b][ldx] (row r starts at X + r*ldx elements), 16-byte aligned, so ldx*size
  * must be a multiple of 16 bytes; ldx >= K.  Y: [b][ldy], ldy >= M, element
  * aligned.  1 <= b <= BCQ_MAX_BATCH.
@@ -163,6 +190,12 @@ bcq_status bcq_gemv_gate_up(const bcq_store *store, int32_t p, const void *x, bc
  * clobbered by the call, so calls that may run at the same time need separate
  * workspaces.  workspace may be NULL when that size is 0; a smaller workspace
  * gives BCQ_ERR_INVALID_ARG.
+ * Accuracy of the summed decode (fp16, launches of more than 16 requests at
+ * one precision): every decoded weight z + sum +-alpha is rounded to fp16
+ * (relative error up to 2^-11 of the weight) before the contraction, so an
+ * output whose terms nearly cancel carries an absolute error of about
+ * 2^-11 * sum_k |w_k x_k| rather than a small fraction of its own size; the
+ * other routes use exact fp16 operands or fp32 tables.
  */
 bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int32_t b,
                            int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,
@@ -177,7 +210,12 @@ size_t bcq_workspace_bytes(const bcq_store *store, int32_t b);
 
 /*
  * Per-request precision: Y[r] = BCQ product of X[r] at precision p_host[r],
- * using alpha[p_host[r]] and zero[p_host[r]].  Every plane up to the largest
+ * using alpha[p_host[r]] and zero[p_host[r]].
+ * Defined by: AnyBCQ paper notes, "overall framework" (online inference loads
+ * the bit-planes a request needs and lets each request pick its precision)
+ * and "key designs" (per-precision scales refitted over shared planes); the
+ * mlsanity page's AnyBCQ abstract names per-request precision selection with
+ * negligible switching overhead.  Every plane up to the largest
  * requested precision is read once per launch for all its requests, so mixing
  * precisions costs no extra plane traffic.  When every requested precision's
  * tables alias those of the largest one (one shared [P][M][G] scale array and

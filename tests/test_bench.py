@@ -75,3 +75,33 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_trace_summary_statistics(tmp_path, capsys):
+    """--trace-summary: per (kernel, grid) statistics over all dispatches and
+    over the last N of the longest consecutive run, from a kernel-trace CSV."""
+    import json
+
+    path = tmp_path / "kernel_trace.csv"
+    lines = ["Dispatch_Id,Kernel_Name,Grid_Size,Start_Timestamp,End_Timestamp"]
+    d = 0
+    # an interleaved stretch (runs of one), then a run of 20 of kernel A
+    for i in range(12):
+        for name, dur in (("A", 5000), ("B", 7000)):
+            d += 1
+            lines.append("%d,%s,256,%d,%d" % (d, name, 1000 * d, 1000 * d + dur))
+    for i in range(20):
+        d += 1
+        lines.append("%d,A,256,%d,%d" % (d, 1000 * d, 1000 * d + 3000 + 100 * i))
+    path.write_text("\n".join(lines) + "\n")
+    bench.trace_summary(str(path), 10)
+    rows = [json.loads(l) for l in capsys.readouterr().out.splitlines()]
+    a = next(r for r in rows if r["kernel"] == "A")
+    assert a["all"]["n"] == 32
+    last = a["longest_run_last"]
+    assert last["n"] == 10
+    # the last ten of the run: 4.0 .. 4.9 us
+    assert abs(last["median"] - 4.45) < 1e-9 and abs(last["mean"] - 4.45) < 1e-9
+    b = next(r for r in rows if r["kernel"] == "B")
+    assert b["all"]["n"] == 12 and b["all"]["median"] == 7.0
+    assert "longest_run_last" not in b  # its longest run is one dispatch
