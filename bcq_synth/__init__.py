@@ -249,3 +249,12 @@ def lowrank(M: int, K: int, R: int, dtype=np.float16, seed: int = 0) -> LowRank:
     x = rng.normal(0.0, 1.0, size=K).astype(dtype)
     y0 = rng.normal(0.0, 1.0, size=M).astype(dtype)
     return LowRank(u, v, alpha, x, y0)
+
+
+def weights(M: int, K: int, dtype=np.float16, seed: int = 0) -> np.ndarray:
+    """A seeded synthetic weight matrix [M][K] for the quantizer: heavy-tailed
+    like trained LLM projection weights (no trained weights are used), each
+    entry 0.02 * t_4 / sqrt(2) (Student's t with 4 degrees of freedom, scaled
+    to standard deviation 0.02), drawn in float64 and rounded once to dtype."""
+    rng = _rng(seed)
+    return np.ascontiguousarray((0.02 / np.sqrt(2.0) * rng.standard_t(4, size=(M, K))).astype(dtype))
