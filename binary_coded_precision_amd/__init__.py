@@ -27,12 +27,14 @@ BCQ_ERR_INVALID_ARG = -1
 BCQ_ERR_UNSUPPORTED = -2
 BCQ_ERR_ALIGNMENT = -3
 BCQ_ERR_HIP = -4
+BCQ_ERR_TOO_LARGE = -5
 BCQ_F16 = 1
 BCQ_F32 = 2
 BCQ_MAX_PLANES = 4
 BCQ_GROUP = 128
 BCQ_TILE_ROWS = 16
 BCQ_MAX_BATCH = 256
+BCQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 # Every symbol include/bcq.h declares.
 EXPORTS = (
@@ -42,6 +44,7 @@ EXPORTS = (
     "bcq_gemv",
     "bcq_gemv_gate_up",
     "bcq_gemm_skinny",
+    "bcq_gemm_skinny_noalloc",
     "bcq_workspace_bytes",
     "bcq_gemv_mixed_p",
     "bcq_lowrank_correct",
@@ -96,6 +99,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         "bcq_gemv_gate_up": (ctypes.c_int, [st, i32, vp, ctypes.c_int, vp, ctypes.c_int, vp]),
         "bcq_gemm_skinny": (ctypes.c_int, [st, i32, vp, i32, i32, ctypes.c_int, vp, i32,
                                            ctypes.c_int, vp, sz, vp]),
+        "bcq_gemm_skinny_noalloc": (ctypes.c_int, [st, i32, vp, i32, i32, ctypes.c_int, vp, i32,
+                                                   ctypes.c_int, vp]),
         "bcq_workspace_bytes": (sz, [st, i32]),
         "bcq_gemv_mixed_p": (ctypes.c_int, [st, vp, vp, i32, i32, ctypes.c_int, vp, i32,
                                             ctypes.c_int, vp, sz, vp]),
@@ -295,6 +300,20 @@ def bcq_gemm_skinny(store: "Store", p: int, X, Y, workspace=None, stream=None) -
            load().bcq_gemm_skinny(store.ref(), p, _ptr(X), b, X.stride(0), _dtype_code(X),
                                   _ptr(Y), Y.stride(0), _dtype_code(Y), _ptr(workspace),
                                   ws_bytes, _stream(stream)))
+
+
+def bcq_gemm_skinny_noalloc(store: "Store", p: int, X, Y, stream=None) -> None:
+    """:func:`bcq_gemm_skinny` with the library's own per-GPU scratch instead of a
+    workspace: nothing is allocated (see ``include/bcq.h`` for the limit and
+    the rule that calls sharing a GPU's scratch must not overlap)."""
+    b = X.shape[0]
+    _need_mat("X", X, b, store.K)
+    _need_mat("Y", Y, b, store.M)
+    _check_store_tensors(store, [p])
+    _check("bcq_gemm_skinny_noalloc",
+           load().bcq_gemm_skinny_noalloc(store.ref(), p, _ptr(X), b, X.stride(0),
+                                          _dtype_code(X), _ptr(Y), Y.stride(0), _dtype_code(Y),
+                                          _stream(stream)))
 
 
 def bcq_gemv_mixed_p(store: "Store", p_host: Sequence[int], X, Y, workspace=None,

@@ -6,7 +6,19 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "bcq_internal.h"
+
+// ---- scratch of the allocation-free entry point (bcq_gemm_skinny_noalloc)
+//
+// A fixed device array that stands in for the caller's workspace: the split-K
+// partial sums of the matrix-core kernels.  Every GPU the library runs on
+// holds its own copy from the first launch until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress, once per device, and only
+// that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[BCQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -325,6 +337,62 @@ bcq_status bcq_gemv_mixed_p(const bcq_store *store, const int32_t *p_host, const
   return run_table_batches(store, p_host, Xc, b, ldx, Yc, ldy, stream);
 }
 
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array (the current device, which
+// the stream must belong to), looked up once per device.  nullptr if HIP
+// reports an error.
+void *scratch_for_current_device(hipStream_t stream, bcq_status *err) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = BCQ_ERR_HIP;
+    return nullptr;
+  }
+  if (stream != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+      *err = BCQ_ERR_HIP;
+      return nullptr;
+    }
+    if (sdev != dev) {
+      *err = BCQ_ERR_INVALID_ARG;
+      return nullptr;
+    }
+  }
+  void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      *err = BCQ_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
+}  // namespace
+
+bcq_status bcq_gemm_skinny_noalloc(const bcq_store *store, int32_t p, const void *X, int32_t b,
+                                   int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,
+                                   bcq_dtype y_dtype, hipStream_t stream) {
+  BCQ_TRY(check_store(store));
+  BCQ_TRY(check_precision(store, p));
+  BCQ_TRY(check_dtypes(store, x_dtype, y_dtype));
+  BCQ_TRY(check_batch(store, X, b, ldx, Y, ldy));
+  const size_t need = bcq_workspace_bytes(store, b);
+  if (need > (size_t)BCQ_NOALLOC_SCRATCH_BYTES) return BCQ_ERR_TOO_LARGE;
+  void *ws = nullptr;
+  if (need > 0) {
+    bcq_status err = BCQ_OK;
+    ws = scratch_for_current_device(stream, &err);
+    if (ws == nullptr) return err;
+  }
+  return bcq_gemm_skinny(store, p, X, b, ldx, x_dtype, Y, ldy, y_dtype, ws, need, stream);
+}
+
 const char *bcq_status_string(bcq_status status) {
   switch (status) {
     case BCQ_OK:
@@ -337,6 +405,9 @@ const char *bcq_status_string(bcq_status status) {
       return "BCQ_ERR_ALIGNMENT: a pointer or leading dimension breaks the alignment rules";
     case BCQ_ERR_HIP:
       return "BCQ_ERR_HIP: the HIP runtime reported a launch error";
+    case BCQ_ERR_TOO_LARGE:
+      return "BCQ_ERR_TOO_LARGE: the call needs more device scratch than the allocation-free "
+             "entry point holds (BCQ_NOALLOC_SCRATCH_BYTES); use bcq_gemm_skinny with a workspace";
   }
   return "unknown bcq_status";
 }

@@ -53,13 +53,16 @@ extern "C" {
 #define BCQ_MAX_BATCH 256
 /* Largest rank accepted by bcq_lowrank_correct. */
 #define BCQ_LOWRANK_MAX_RANK 4096
+/* Device scratch held by the library for bcq_gemm_skinny_noalloc, per GPU. */
+#define BCQ_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 typedef enum {
   BCQ_OK = 0,
   BCQ_ERR_INVALID_ARG = -1, /* null pointer, bad shape, p out of range, bad leading dim */
   BCQ_ERR_UNSUPPORTED = -2, /* valid but not implemented: dtype pairing, group size != 128 */
   BCQ_ERR_ALIGNMENT = -3,   /* a pointer or leading dimension breaks the alignment rules */
-  BCQ_ERR_HIP = -4          /* the HIP runtime reported an error for a launch */
+  BCQ_ERR_HIP = -4,         /* the HIP runtime reported an error for a launch */
+  BCQ_ERR_TOO_LARGE = -5    /* bcq_gemm_skinny_noalloc: the call needs more scratch than it holds */
 } bcq_status;
 
 typedef enum { BCQ_F16 = 1, BCQ_F32 = 2 } bcq_dtype;
@@ -207,6 +210,29 @@ bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int
  * (0 when none), or 0 for an invalid store.
  */
 size_t bcq_workspace_bytes(const bcq_store *store, int32_t b);
+
+/*
+ * bcq_gemm_skinny without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same product, kernels, validation and
+ * results as bcq_gemm_skinny (bit for bit); where that call would need a
+ * workspace (bcq_workspace_bytes(store, b) > 0) this one uses a device array
+ * the library holds, BCQ_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, kept from
+ * the first use on that GPU until the process ends.  The call allocates
+ * nothing (no hipMalloc or allocating library routine, on any path).
+ * Limits and errors:
+ *  - a call needing more than BCQ_NOALLOC_SCRATCH_BYTES returns
+ *    BCQ_ERR_TOO_LARGE and enqueues nothing (every LLaMA-3.1-8B layer shape
+ *    needs at most 8 MiB at any batch);
+ *  - the stream must belong to the current device (BCQ_ERR_INVALID_ARG);
+ *  - all calls on one GPU share its one array: calls that may run at the same
+ *    time on that GPU (on different streams, or from different threads) race
+ *    on it and must be ordered by the caller.  Nothing in it needs clearing:
+ *    each call writes every partial sum before reading it.
+ */
+bcq_status bcq_gemm_skinny_noalloc(const bcq_store *store, int32_t p, const void *X, int32_t b,
+                                   int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,
+                                   bcq_dtype y_dtype, hipStream_t stream);
 
 /*
  * Per-request precision: Y[r] = BCQ product of X[r] at precision p_host[r],

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         s = bcq.bcq_status_string(code)
         assert s.startswith("BCQ_")
     assert "unknown" in bcq.bcq_status_string(7)
@@ -218,3 +218,22 @@ def test_workspace_sizes():
     f32 = make_store(M=4096, K=4096, dtype=bcq.BCQ_F32)
     assert lib.bcq_workspace_bytes(ctypes.byref(f32), 64) == 0  # fp32 uses the table path
     assert lib.bcq_workspace_bytes(None, 16) == 0
+
+
+def test_noalloc_entry_point_validates_and_rejects_oversized_calls_on_the_host():
+    """bcq_gemm_skinny_noalloc checks its arguments like bcq_gemm_skinny, and a
+    call whose split-K partial sums exceed the library's scratch returns
+    BCQ_ERR_TOO_LARGE before any HIP call."""
+    lib = bcq.load()
+    call = lambda st, b, ldx=None, ldy=None, X=FAKE, Y=FAKE: lib.bcq_gemm_skinny_noalloc(
+        ctypes.byref(st), 4, X, b, st.K if ldx is None else ldx, bcq.BCQ_F16, Y,
+        st.M if ldy is None else ldy, bcq.BCQ_F16, None)
+    st = make_store(M=64, K=256)
+    assert call(st, 0) == E_ARG
+    assert call(st, 2, X=None) == E_ARG
+    assert call(st, 2, ldx=100) == E_ARG
+    big = make_store(M=36864, K=65536)
+    need = lib.bcq_workspace_bytes(ctypes.byref(big), 64)
+    assert need > bcq.BCQ_NOALLOC_SCRATCH_BYTES
+    assert call(big, 64) == bcq.BCQ_ERR_TOO_LARGE
+    assert "BCQ_ERR_TOO_LARGE" in bcq.bcq_status_string(bcq.BCQ_ERR_TOO_LARGE)
