@@ -30,6 +30,7 @@ BCQ_ERR_HIP = -4
 BCQ_ERR_TOO_LARGE = -5
 BCQ_F16 = 1
 BCQ_F32 = 2
+BCQ_F64 = 3
 BCQ_MAX_PLANES = 4
 BCQ_GROUP = 128
 BCQ_TILE_ROWS = 16
@@ -49,6 +50,7 @@ EXPORTS = (
     "bcq_gemv_mixed_p",
     "bcq_lowrank_correct",
     "bcq_dequantize",
+    "bcq_quantize",
     "bcq_status_string",
 )
 
@@ -107,6 +109,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         "bcq_lowrank_correct": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp, ctypes.c_int,
                                                vp, vp]),
         "bcq_dequantize": (ctypes.c_int, [st, i32, vp, i32, ctypes.c_int, vp]),
+        "bcq_quantize": (ctypes.c_int, [vp, ctypes.c_int, i32, i32, i32, i32, i32, i32, vp, vp,
+                                        vp, ctypes.c_int, vp]),
         "bcq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -267,6 +271,41 @@ def bcq_dequantize(store: "Store", p: int, W, stream=None) -> None:
                                                    _dtype_code(W), _stream(stream)))
 
 
+def bcq_quantize(W, P: int, p_low: int = 2, iters: int = 20, out_dtype=None, stream=None):
+    """Quantize the device matrix ``W`` [M][K] (fp16 or fp32, rows may be
+    padded) into P sign planes and per-precision tables (see ``include/bcq.h``).
+
+    Returns ``(signs, alpha, zero)``: ``signs`` an int32 device tensor
+    [P][M][K/32] in the canonical format ``bcq_pack_planes`` takes, and dicts
+    ``alpha[p]`` [p][M][K/128], ``zero[p]`` [M][K/128] for p = p_low..P, views
+    of two device buffers of ``out_dtype`` (default: W's dtype)."""
+    import torch
+
+    M, K = W.shape
+    _need_mat("W", W, M, K)
+    out_dtype = W.dtype if out_dtype is None else out_dtype
+    codes = {torch.float16: BCQ_F16, torch.float32: BCQ_F32, torch.float64: BCQ_F64}
+    if out_dtype not in codes or W.dtype not in (torch.float16, torch.float32):
+        raise TypeError("W must be float16/float32 and out_dtype float16/32/64")
+    if K % BCQ_GROUP or not (1 <= p_low <= P <= BCQ_MAX_PLANES):
+        raise ValueError("K must be a multiple of 128 and 1 <= p_low <= P <= 4")
+    G = K // BCQ_GROUP
+    signs = torch.empty((P, M, K // 32), dtype=torch.int32, device=W.device)
+    n_alpha = sum(p for p in range(p_low, P + 1)) * M * G
+    abuf = torch.empty(n_alpha, dtype=out_dtype, device=W.device)
+    zbuf = torch.empty((P - p_low + 1, M, G), dtype=out_dtype, device=W.device)
+    _check("bcq_quantize",
+           load().bcq_quantize(_ptr(W), _dtype_code(W), M, K, W.stride(0), P, p_low, iters,
+                               _ptr(signs), _ptr(abuf), _ptr(zbuf), codes[out_dtype],
+                               _stream(stream)))
+    alpha, zero, off = {}, {}, 0
+    for p in range(p_low, P + 1):
+        alpha[p] = abuf[off:off + p * M * G].view(p, M, G)
+        zero[p] = zbuf[p - p_low]
+        off += p * M * G
+    return signs, alpha, zero
+
+
 def bcq_workspace_bytes(store: "Store", b: int) -> int:
     return int(load().bcq_workspace_bytes(store.ref(), b))
 
@@ -369,6 +408,20 @@ class Store:
 
     def ref(self):
         return ctypes.byref(self._st)
+
+    @classmethod
+    def from_quantized(cls, signs, alpha: Dict[int, object], zero: Dict[int, object],
+                       stream=None) -> "Store":
+        """A store from :func:`bcq_quantize`'s outputs (device tensors): packs the
+        canonical sign words; precision p reads ``alpha[p]`` / ``zero[p]``."""
+        import torch
+
+        P, M, W = signs.shape
+        K = W * 32
+        packed = torch.empty(bcq_packed_bytes(P, M, K) // 4, dtype=torch.int32,
+                             device=signs.device)
+        bcq_pack_planes(signs, P, M, K, packed, stream)
+        return cls(M, K, P, packed, alpha, zero)
 
     @classmethod
     def from_host(cls, signs: np.ndarray, alpha: np.ndarray, zero: np.ndarray, *,

@@ -16,7 +16,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbcq.so")
-SOURCES = ["bcq_api.hip", "pack.hip", "gemv_lut.hip", "gemm_mfma.hip", "lowrank.hip", "dequant.hip"]
+SOURCES = ["bcq_api.hip", "pack.hip", "gemv_lut.hip", "gemm_mfma.hip", "lowrank.hip", "dequant.hip",
+           "quantize.hip"]
+# Per-file flags: the quantizer takes its sign decisions on exactly rounded
+# fp64 values, so no multiply-add there is fused into one rounding.
+FILE_FLAGS = {"quantize.hip": ["-ffp-contract=off"]}
 # Measurement kernels of the benchmark's floor row (empty launch, plain
 # streaming read): a library of their own, outside the BCQ ABI.
 PROBE_LIB = os.path.join(HERE, "libbcq_probe.so")
@@ -44,7 +48,8 @@ def hipcc() -> str:
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + COMMON_FLAGS + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + COMMON_FLAGS + FILE_FLAGS.get(src, []) + list(extra) +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

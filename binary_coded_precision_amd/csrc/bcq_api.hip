@@ -337,6 +337,24 @@ bcq_status bcq_gemv_mixed_p(const bcq_store *store, const int32_t *p_host, const
   return run_table_batches(store, p_host, Xc, b, ldx, Yc, ldy, stream);
 }
 
+bcq_status bcq_quantize(const void *W, bcq_dtype w_dtype, int32_t M, int32_t K, int32_t ldw,
+                        int32_t P, int32_t p_low, int32_t iters, uint32_t *signs, void *alpha,
+                        void *zero, bcq_dtype out_dtype, hipStream_t stream) {
+  if (W == nullptr || signs == nullptr || alpha == nullptr || zero == nullptr)
+    return BCQ_ERR_INVALID_ARG;
+  if (w_dtype != BCQ_F16 && w_dtype != BCQ_F32) return BCQ_ERR_INVALID_ARG;
+  if (out_dtype != BCQ_F16 && out_dtype != BCQ_F32 && out_dtype != BCQ_F64)
+    return BCQ_ERR_INVALID_ARG;
+  BCQ_TRY(check_shape(P, M, K));
+  if (p_low < 1 || p_low > P || iters < 0 || iters > 1000 || ldw < K) return BCQ_ERR_INVALID_ARG;
+  const size_t ws = w_dtype == BCQ_F16 ? 2 : 4;
+  const size_t os = out_dtype == BCQ_F16 ? 2 : out_dtype == BCQ_F32 ? 4 : 8;
+  if (!aligned(W, ws) || !aligned(signs, 4) || !aligned(alpha, os) || !aligned(zero, os))
+    return BCQ_ERR_ALIGNMENT;
+  return hip_status(bcq::launch_quantize(W, w_dtype, ldw, M, K, P, p_low, iters, signs, alpha,
+                                         zero, out_dtype, stream));
+}
+
 namespace {
 
 constexpr int kMaxDevices = 64;

@@ -59,6 +59,13 @@ constexpr int kLrMaxRank = BCQ_LOWRANK_MAX_RANK;
 hipError_t launch_lowrank(const uint32_t *u, const uint32_t *v, const void *alpha, int R, int M,
                           int K, const void *x, void *y, bcq_dtype dt, float *z, hipStream_t s);
 
+// Progressive-precision quantizer (bcq_quantize): W [M][ldw] of w_dt (fp16 or
+// fp32) -> canonical signs [P][M][K/32] and the scale / offset tables of
+// precisions p_low..P in out_dt (fp16, fp32 or fp64).
+hipError_t launch_quantize(const void *W, bcq_dtype w_dt, int ldw, int M, int K, int P,
+                           int p_low, int iters, uint32_t *signs, void *alpha, void *zero,
+                           bcq_dtype out_dt, hipStream_t s);
+
 // Batched products with 2..8 requests per launch (vector ALUs, shared tables).
 // x rows at x + r*ldx, y rows at y + r*ldy, r < nreq; p_max = max of t.p[].
 hipError_t launch_skinny_lut(const uint32_t *bits, int M, int K, int p_max, const ReqTables &t,

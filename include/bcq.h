@@ -65,7 +65,8 @@ typedef enum {
   BCQ_ERR_TOO_LARGE = -5    /* bcq_gemm_skinny_noalloc: the call needs more scratch than it holds */
 } bcq_status;
 
-typedef enum { BCQ_F16 = 1, BCQ_F32 = 2 } bcq_dtype;
+/* BCQ_F64 is accepted only for bcq_quantize's scale and offset tables. */
+typedef enum { BCQ_F16 = 1, BCQ_F32 = 2, BCQ_F64 = 3 } bcq_dtype;
 
 /*
  * A packed store: the planes in device layout plus the scale tables.
@@ -298,6 +299,46 @@ bcq_status bcq_dequantize(const bcq_store *store, int32_t p, void *W, int32_t ld
 bcq_status bcq_lowrank_correct(const uint32_t *u_signs, const uint32_t *v_signs,
                                const void *alpha, int32_t R, int32_t M, int32_t K, const void *x,
                                void *y, bcq_dtype dtype, float *z, hipStream_t stream);
+
+/*
+ * Offline quantizer: a weight matrix W [M][K] becomes P shared sign planes and
+ * one scale and offset table per precision p = p_low..P, by AnyBCQ's
+ * progressive precision expansion (AnyBCQ paper notes, "Method / key
+ * designs": greedy start and alternating refinement -- a least-squares scale
+ * fit, then a search for each weight's best code -- at the base precision;
+ * then, per added plane, the earlier planes frozen, the new plane the sign of
+ * the residual and every scale refit by least squares; "Training strategy":
+ * asymmetric group-wise BCQ with g = 128).  Per (row, group of 128):
+ *  1. greedy start: offset = group mean; for each of the p_low planes,
+ *     plane = sign(residual) (sign(0) = +1), scale = mean |residual|, and the
+ *     scaled plane leaves the residual;
+ *  2. `iters` rounds of: least-squares fit of the p_low scales and the
+ *     offset, then every weight takes the code (one sign per plane) whose
+ *     level z + sum +-alpha_i is nearest (first code on a tie, code c giving
+ *     plane i the sign +1 when bit i of c is set); then a last fit;
+ *  3. for p = p_low..P-1: plane p+1 = sign(W - W_hat_p), earlier planes
+ *     unchanged, then a least-squares fit of all p+1 scales and the offset.
+ * Least squares solves the normal equations over the columns [planes, ones];
+ * a plane linearly dependent on the ones column and the earlier kept planes
+ * gets scale 0.  Sums over a group are pairwise (halving) sums in fp64 and
+ * no multiply-add is fused, so every decision is taken on fully specified
+ * values; the results are deterministic.
+ * W: [M][ldw] (row m at W + m*ldw), ldw >= K, w_dtype BCQ_F16 or BCQ_F32,
+ *   element aligned.  M >= 1, K a positive multiple of 128, 1 <= p_low <= P
+ *   <= 4, 0 <= iters <= 1000.
+ * signs: [P][M][K/32] uint32 in bcq_pack_planes' canonical input format
+ *   (4-byte aligned); fully overwritten.
+ * alpha: the tables of p = p_low..P one after another, table p being
+ *   [p][M][K/128] and starting (p(p-1)/2 - p_low(p_low-1)/2) * M * (K/128)
+ *   elements into the buffer; zero: [P - p_low + 1][M][K/128], the offsets of
+ *   precision p at table p - p_low.  out_dtype BCQ_F16, BCQ_F32 or BCQ_F64,
+ *   each value rounded once to nearest even from fp64; element aligned.
+ * Validation and stream behaviour as in bcq_gemv: a rejected call enqueues
+ * nothing.
+ */
+bcq_status bcq_quantize(const void *W, bcq_dtype w_dtype, int32_t M, int32_t K, int32_t ldw,
+                        int32_t P, int32_t p_low, int32_t iters, uint32_t *signs, void *alpha,
+                        void *zero, bcq_dtype out_dtype, hipStream_t stream);
 
 /* Static text for a status code (never null). */
 const char *bcq_status_string(bcq_status status);

@@ -237,3 +237,22 @@ def test_noalloc_entry_point_validates_and_rejects_oversized_calls_on_the_host()
     assert need > bcq.BCQ_NOALLOC_SCRATCH_BYTES
     assert call(big, 64) == bcq.BCQ_ERR_TOO_LARGE
     assert "BCQ_ERR_TOO_LARGE" in bcq.bcq_status_string(bcq.BCQ_ERR_TOO_LARGE)
+
+
+def test_quantize_validation_rejects_before_launch():
+    lib = bcq.load()
+    q = lambda W=FAKE, wdt=bcq.BCQ_F16, M=16, K=256, ldw=256, P=4, pl=2, it=20, s=FAKE, a=FAKE, \
+        z=FAKE, odt=bcq.BCQ_F16: lib.bcq_quantize(W, wdt, M, K, ldw, P, pl, it, s, a, z, odt, None)
+    assert q(W=None) == E_ARG
+    assert q(s=None) == E_ARG
+    assert q(wdt=bcq.BCQ_F64) == E_ARG
+    assert q(odt=7) == E_ARG
+    assert q(K=200, ldw=200) == E_ARG
+    assert q(ldw=128) == E_ARG
+    assert q(P=5) == E_ARG
+    assert q(pl=0) == E_ARG
+    assert q(pl=5, P=4) == E_ARG
+    assert q(it=-1) == E_ARG
+    assert q(W=FAKE + 1) == E_ALN
+    assert q(a=FAKE + 4, odt=bcq.BCQ_F64) == E_ALN
+    assert q(s=FAKE + 2) == E_ALN
