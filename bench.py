@@ -93,14 +93,31 @@ def stored_traffic():
 
 
 class Flush:
-    """A scratch buffer of twice the Infinity Cache; flush() reads and writes
-    all of it, evicting whatever the caches held."""
+    """A buffer of twice the Infinity Cache; flush() reads all of it with the
+    probe library's streaming read, so the caches end up holding its clean
+    lines and nothing of the stores (a write would leave dirty lines whose
+    write-back then competes with the timed reads)."""
 
     def __init__(self, torch):
-        self.buf = torch.zeros(2 * MALL_BYTES // 4, dtype=torch.int32, device="cuda")
+        import ctypes
+
+        from binary_coded_precision_amd import build as hb
+
+        self.torch = torch
+        self.lib = ctypes.CDLL(hb.PROBE_LIB)
+        self.lib.bcq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+        self.buf = torch.ones(2 * MALL_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
 
     def __call__(self):
-        self.buf.add_(1)
+        import ctypes
+
+        st = ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        rc = self.lib.bcq_probe_read(ctypes.c_void_p(self.buf.data_ptr()), 2 * MALL_BYTES, 4096,
+                                     ctypes.c_void_p(self.sink.data_ptr()), st)
+        if rc != 0:
+            raise RuntimeError("cache flush read failed: %d" % rc)
 
 
 class Rotation:
@@ -553,24 +570,40 @@ def cpu_baseline(w, budget_s: float):
             "nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
 
-def trace_summary(path: str, last: int) -> None:
-    """Per-kernel duration statistics from a rocprofv3 kernel-trace CSV: for
-    each (kernel, grid) with at least 10 dispatches, count, mean, median, p10
-    and p90 in microseconds over all its dispatches, and over the last `last`
-    dispatches of its longest run of consecutive dispatches (in a bench run,
-    the timed replay of a cold per-precision graph)."""
-    import csv
-
-    rows = list(csv.DictReader(open(path, newline="")))
-    key_name = "Kernel_Name"
-    grid_keys = [k for k in ("Grid_Size", "Grid_Size_X") if rows and k in rows[0]]
+def trace_dispatches(path: str):
+    """(dispatch id, kernel name, grid, duration in us) of every kernel
+    dispatch in a rocprofv3 kernel trace: a rocpd SQLite database (.db, the
+    default output) or a kernel-trace CSV."""
     seq = []
-    for r in rows:
-        name = r[key_name]
-        grid = r[grid_keys[0]] if grid_keys else "?"
-        t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
-        seq.append((int(r.get("Dispatch_Id", len(seq))), name, grid, t))
+    if path.endswith(".db"):
+        import sqlite3
+
+        con = sqlite3.connect(path)
+        for did, name, gx, gy, start, end in con.execute(
+                "select dispatch_id, name, grid_x, grid_y, start, end from kernels"):
+            seq.append((int(did), name, "%dx%d" % (gx, gy), (int(end) - int(start)) * 1e-3))
+        con.close()
+    else:
+        import csv
+
+        rows = list(csv.DictReader(open(path, newline="")))
+        grid_keys = [k for k in ("Grid_Size", "Grid_Size_X") if rows and k in rows[0]]
+        for r in rows:
+            grid = r[grid_keys[0]] if grid_keys else "?"
+            t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+            seq.append((int(r.get("Dispatch_Id", len(seq))), r["Kernel_Name"], grid, t))
     seq.sort()
+    return seq
+
+
+def trace_summary(path: str, last: int) -> None:
+    """Per-kernel duration statistics from a rocprofv3 kernel trace (see
+    trace_dispatches): for each (kernel, grid) with at least 10 dispatches,
+    count, mean, median, p10 and p90 in microseconds over all its dispatches,
+    and over the last `last` dispatches of its longest run of consecutive
+    dispatches (in a bench run, the timed replay of a cold per-precision
+    graph)."""
+    seq = trace_dispatches(path)
 
     def stats(v):
         v = np.sort(np.asarray(v))
