@@ -108,13 +108,13 @@ class Flush:
         self.lib.bcq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                             ctypes.c_void_p, ctypes.c_void_p]
         self.buf = torch.ones(2 * MALL_BYTES // 4, dtype=torch.int32, device="cuda")
-        self.sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+        self.sink = torch.zeros(2 * MALL_BYTES // (4096 * 8) + 1, dtype=torch.int32, device="cuda")
 
     def __call__(self):
         import ctypes
 
         st = ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
-        rc = self.lib.bcq_probe_read(ctypes.c_void_p(self.buf.data_ptr()), 2 * MALL_BYTES, 4096,
+        rc = self.lib.bcq_probe_read(ctypes.c_void_p(self.buf.data_ptr()), 2 * MALL_BYTES, 8,
                                      ctypes.c_void_p(self.sink.data_ptr()), st)
         if rc != 0:
             raise RuntimeError("cache flush read failed: %d" % rc)
@@ -277,7 +277,7 @@ def floor_row(torch, flush, n):
     lib.bcq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                    ctypes.c_void_p, ctypes.c_void_p]
     st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
     row = {"empty_launch_us": round(time_calls(
         torch, lambda i: lib.bcq_probe_empty(st()), max(n, 100), 10) * 1e3, 3)}
     for nb in (algorithmic_bytes(4096, 4096, 4), algorithmic_bytes(14336, 4096, 4)):
@@ -287,16 +287,16 @@ def floor_row(torch, flush, n):
                 for c in range(copies)]
         best = None
         sweep = {}
-        for blocks in (256, 512, 1024, 2048, 4096):
-            d = time_calls(torch, lambda i, blocks=blocks: lib.bcq_probe_read(
-                ctypes.c_void_p(bufs[i % copies].data_ptr()), nb16, blocks,
+        for per_lane in (1, 2, 4, 8, 16):
+            d = time_calls(torch, lambda i, per_lane=per_lane: lib.bcq_probe_read(
+                ctypes.c_void_p(bufs[i % copies].data_ptr()), nb16, per_lane,
                 ctypes.c_void_p(sink.data_ptr()), st()), max(n, copies), 10, flush)
-            sweep[str(blocks)] = round(d * 1e3, 3)
+            sweep[str(per_lane)] = round(d * 1e3, 3)
             best = d if best is None else min(best, d)
         row["read_%d_bytes" % nb] = {"us": round(best * 1e3, 3),
                                      "GBps": round(nb / (best * 1e-3) / 1e9, 1),
                                      "frac_of_peak": round(nb / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                     "us_by_workgroups": sweep}
+                                     "us_by_loads_per_lane": sweep}
         del bufs
     return row
 
@@ -307,195 +307,229 @@ def secondary(args, bcq, torch, bcq_synth, flush):
     low-rank correction (one buffer set) are labelled as such."""
     rows = {}
     n = max(20, args.steps // 4)
+    sel = [s for s in (args.rows or "").split(",") if s]
 
-    print("[bench] secondary floor", file=sys.stderr, flush=True)
-    rows["floor"] = floor_row(torch, flush, n)
+    def want(name):
+        # a row is run when a selected prefix names it (or a section holding it)
+        return not sel or any(name.startswith(s) or s.startswith(name) for s in sel)
 
-    # MLP shapes at batch 1, p = 2/3/4: 14336x4096 (gate/up projection, the
-    # large-shape target row) and 4096x14336 (down projection, whose K exceeds
-    # what one workgroup keeps resident, so its tables stream through LDS)
-    for M, K, seed in ((14336, 4096, 3), (4096, 14336, 6)):
-        print("[bench] secondary %dx%d b=1" % (M, K), file=sys.stderr, flush=True)
-        w = bcq_synth.make(M, K, 4, seed=seed, name="mlp_%dx%d_b1" % (M, K))
+    if want("floor"):
+        print("[bench] secondary floor", file=sys.stderr, flush=True)
+        rows["floor"] = floor_row(torch, flush, n)
+
+    if want('gemv_'):
+        # MLP shapes at batch 1, p = 2/3/4: 14336x4096 (gate/up projection, the
+        # large-shape target row) and 4096x14336 (down projection, whose K exceeds
+        # what one workgroup keeps resident, so its tables stream through LDS)
+        for M, K, seed in ((14336, 4096, 3), (4096, 14336, 6)):
+            if not want("gemv_%dx%d_b1" % (M, K)):
+                continue
+            print("[bench] secondary %dx%d b=1" % (M, K), file=sys.stderr, flush=True)
+            w = bcq_synth.make(M, K, 4, seed=seed, name="mlp_%dx%d_b1" % (M, K))
+            rot = Rotation(w, ROTATE_BYTES, bcq, torch)
+            ys = [torch.empty(w.M, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+            r = {}
+            for p in (2, 3, 4):
+                d = rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_gemv(rot.stores[c], p,
+                                                                           rot.x[c][0], ys[c]),
+                                   n, 10, flush)
+                nb = algorithmic_bytes(w.M, w.K, p)
+                r[str(p)] = {"us": round(d * 1e3, 3),
+                             "GBps": round(nb / (d * 1e-3) / 1e9, 1),
+                             "frac_of_peak": round(nb / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            rows["gemv_%dx%d_b1" % (M, K)] = r
+            del rot, ys
+
+    if want('gate_up_fused'):
+        # the MLP's gate and up projections as one gate/up store (2 x 14336 rows,
+        # bcq_gemv_gate_up) with the silu(gate) * up epilogue in the same launch,
+        # next to the two separate 14336x4096 products timed above (which would
+        # still need the epilogue as a third kernel)
+        print("[bench] secondary gate/up", file=sys.stderr, flush=True)
+        Mo = 14336
+        w = bcq_synth.make(2 * Mo, 4096, 4, seed=9, name="gate_up_28672x4096_b1")
         rot = Rotation(w, ROTATE_BYTES, bcq, torch)
-        ys = [torch.empty(w.M, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+        ys = [torch.empty(Mo, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
         r = {}
         for p in (2, 3, 4):
-            d = rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_gemv(rot.stores[c], p,
-                                                                       rot.x[c][0], ys[c]),
+            d = rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_gemv_gate_up(rot.stores[c], p,
+                                                                               rot.x[c][0], ys[c]),
                                n, 10, flush)
-            nb = algorithmic_bytes(w.M, w.K, p)
+            nb = algorithmic_bytes(2 * Mo, 4096, p) - Mo * 2  # Mo outputs, not 2 * Mo
             r[str(p)] = {"us": round(d * 1e3, 3),
                          "GBps": round(nb / (d * 1e-3) / 1e9, 1),
-                         "frac_of_peak": round(nb / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        rows["gemv_%dx%d_b1" % (M, K)] = r
+                         "two_products_us": round(2 * rows["gemv_14336x4096_b1"][str(p)]["us"], 3)}
+        rows["gate_up_fused_28672x4096_b1"] = r
         del rot, ys
 
-    # the MLP's gate and up projections as one gate/up store (2 x 14336 rows,
-    # bcq_gemv_gate_up) with the silu(gate) * up epilogue in the same launch,
-    # next to the two separate 14336x4096 products timed above (which would
-    # still need the epilogue as a third kernel)
-    print("[bench] secondary gate/up", file=sys.stderr, flush=True)
-    Mo = 14336
-    w = bcq_synth.make(2 * Mo, 4096, 4, seed=9, name="gate_up_28672x4096_b1")
-    rot = Rotation(w, ROTATE_BYTES, bcq, torch)
-    ys = [torch.empty(Mo, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
-    r = {}
-    for p in (2, 3, 4):
-        d = rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_gemv_gate_up(rot.stores[c], p,
-                                                                           rot.x[c][0], ys[c]),
-                           n, 10, flush)
-        nb = algorithmic_bytes(2 * Mo, 4096, p) - Mo * 2  # Mo outputs, not 2 * Mo
-        r[str(p)] = {"us": round(d * 1e3, 3),
-                     "GBps": round(nb / (d * 1e-3) / 1e9, 1),
-                     "two_products_us": round(2 * rows["gemv_14336x4096_b1"][str(p)]["us"], 3)}
-    rows["gate_up_fused_28672x4096_b1"] = r
-    del rot, ys
+    if want('qkv_concatenated'):
+        # q, k and v (4096 + 1024 + 1024 rows over one 4096-wide input) as one
+        # concatenated 6144-row store, next to the three separate products
+        print("[bench] secondary q/k/v", file=sys.stderr, flush=True)
+        r = {}
+        stores = {}
+        for M in (6144, 4096, 1024):
+            w = bcq_synth.make(M, 4096, 4, seed=10 + M, name="qkv_%dx4096_b1" % M)
+            rot = Rotation(w, ROTATE_BYTES, bcq, torch)
+            ys = [torch.empty(M, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+            stores[M] = {p: rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_gemv(
+                rot.stores[c], p, rot.x[c][0], ys[c]), n, 10, flush) for p in (2, 3, 4)}
+            del rot, ys
+        for p in (2, 3, 4):
+            nb = algorithmic_bytes(6144, 4096, p)
+            d = stores[6144][p]
+            r[str(p)] = {"us": round(d * 1e3, 3), "GBps": round(nb / (d * 1e-3) / 1e9, 1),
+                         "three_products_us": round((stores[4096][p] + 2 * stores[1024][p]) * 1e3, 3)}
+        rows["qkv_concatenated_6144x4096_b1"] = r
 
-    # q, k and v (4096 + 1024 + 1024 rows over one 4096-wide input) as one
-    # concatenated 6144-row store, next to the three separate products
-    print("[bench] secondary q/k/v", file=sys.stderr, flush=True)
-    r = {}
-    stores = {}
-    for M in (6144, 4096, 1024):
-        w = bcq_synth.make(M, 4096, 4, seed=10 + M, name="qkv_%dx4096_b1" % M)
+    if want('lowrank_correction'):
+        # binary low-rank correction y += sum_r alpha_r u_r (v_r . x) on a 4096x4096
+        # output (BiLoCo's ranks 16..512); each timed call adds to the same y, so
+        # its sign vectors stay cached (warm)
+        print("[bench] secondary low-rank", file=sys.stderr, flush=True)
+        r = {}
+        for R in (16, 128, 512):
+            lr = bcq_synth.lowrank(4096, 4096, R, seed=R)
+            u = torch.from_numpy(lr.u.view(np.int32)).cuda()
+            v = torch.from_numpy(lr.v.view(np.int32)).cuda()
+            a = torch.from_numpy(lr.alpha).cuda()
+            xx = torch.from_numpy(lr.x).cuda()
+            yy = torch.from_numpy(lr.y0).cuda()
+            zz = torch.empty(R, dtype=torch.float32, device="cuda")
+            d = time_calls(torch, lambda i: bcq.bcq_lowrank_correct(u, v, a, xx, yy, zz), n, 10)
+            sign_bytes = 4096 * ((R + 31) // 32) * 4 + R * 4096 // 8
+            r["rank_%d" % R] = {"us": round(d * 1e3, 3), "sign_bytes": sign_bytes, "cache": "warm"}
+        rows["lowrank_correction_4096x4096_b1"] = r
+
+    if want('dequantize'):
+        # dense reconstruction export (bcq_dequantize) of the 4096x4096 store, the
+        # route for batches past the matrix-core kernels: an HBM stream that reads
+        # the planes and scales and writes M x K fp16
+        print("[bench] secondary dequantize", file=sys.stderr, flush=True)
+        w = bcq_synth.config(2)
         rot = Rotation(w, ROTATE_BYTES, bcq, torch)
-        ys = [torch.empty(M, dtype=torch.float16, device="cuda") for _ in range(rot.n)]
-        stores[M] = {p: rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_gemv(
-            rot.stores[c], p, rot.x[c][0], ys[c]), n, 10, flush) for p in (2, 3, 4)}
-        del rot, ys
-    for p in (2, 3, 4):
-        nb = algorithmic_bytes(6144, 4096, p)
-        d = stores[6144][p]
-        r[str(p)] = {"us": round(d * 1e3, 3), "GBps": round(nb / (d * 1e-3) / 1e9, 1),
-                     "three_products_us": round((stores[4096][p] + 2 * stores[1024][p]) * 1e3, 3)}
-    rows["qkv_concatenated_6144x4096_b1"] = r
+        # distinct outputs, more of them together than the Infinity Cache holds
+        nw = ROTATE_BYTES // (w.M * w.K * 2) + 1
+        Wd = [torch.empty((w.M, w.K), dtype=torch.float16, device="cuda") for _ in range(nw)]
+        r = {}
+        for p in (2, 3, 4):
+            d = rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_dequantize(rot.stores[c], p,
+                                                                             Wd[c % nw]),
+                               n, 10, flush)
+            nb = algorithmic_bytes(w.M, w.K, p, b=0) + w.M * w.K * 2  # planes + scales read, W written
+            r[str(p)] = {"us": round(d * 1e3, 3), "GBps": round(nb / (d * 1e-3) / 1e9, 1),
+                         "frac_of_peak": round(nb / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        rows["dequantize_4096x4096"] = r
+        del rot, Wd
 
-    # binary low-rank correction y += sum_r alpha_r u_r (v_r . x) on a 4096x4096
-    # output (BiLoCo's ranks 16..512); each timed call adds to the same y, so
-    # its sign vectors stay cached (warm)
-    print("[bench] secondary low-rank", file=sys.stderr, flush=True)
-    r = {}
-    for R in (16, 128, 512):
-        lr = bcq_synth.lowrank(4096, 4096, R, seed=R)
-        u = torch.from_numpy(lr.u.view(np.int32)).cuda()
-        v = torch.from_numpy(lr.v.view(np.int32)).cuda()
-        a = torch.from_numpy(lr.alpha).cuda()
-        xx = torch.from_numpy(lr.x).cuda()
-        yy = torch.from_numpy(lr.y0).cuda()
-        zz = torch.empty(R, dtype=torch.float32, device="cuda")
-        d = time_calls(torch, lambda i: bcq.bcq_lowrank_correct(u, v, a, xx, yy, zz), n, 10)
-        sign_bytes = 4096 * ((R + 31) // 32) * 4 + R * 4096 // 8
-        r["rank_%d" % R] = {"us": round(d * 1e3, 3), "sign_bytes": sign_bytes, "cache": "warm"}
-    rows["lowrank_correction_4096x4096_b1"] = r
+    if want('prefill_routes'):
+        # prefill through the dense route (bcq_dequantize, then fp16 F.linear on
+        # hipBLASLt) against the matrix-core kernels at the largest batch they take,
+        # and at a batch past it; 4096x4096, p = 4
+        print("[bench] secondary prefill routes", file=sys.stderr, flush=True)
+        nw = ROTATE_BYTES // (4096 * 4096 * 2) + 1
+        Wd = [torch.empty((4096, 4096), dtype=torch.float16, device="cuda") for _ in range(nw)]
+        r = {}
+        for b in (256, 1024):
+            w = bcq_synth.make(4096, 4096, 4, b=b, seed=7)
+            rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
+            Y = [torch.empty((b, w.M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
 
-    # dense reconstruction export (bcq_dequantize) of the 4096x4096 store, the
-    # route for batches past the matrix-core kernels: an HBM stream that reads
-    # the planes and scales and writes M x K fp16
-    print("[bench] secondary dequantize", file=sys.stderr, flush=True)
-    w = bcq_synth.config(2)
-    rot = Rotation(w, ROTATE_BYTES, bcq, torch)
-    # distinct outputs, more of them together than the Infinity Cache holds
-    nw = ROTATE_BYTES // (w.M * w.K * 2) + 1
-    Wd = [torch.empty((w.M, w.K), dtype=torch.float16, device="cuda") for _ in range(nw)]
-    r = {}
-    for p in (2, 3, 4):
-        d = rotating_calls(torch, rot, lambda c, p=p: bcq.bcq_dequantize(rot.stores[c], p,
-                                                                         Wd[c % nw]),
-                           n, 10, flush)
-        nb = algorithmic_bytes(w.M, w.K, p, b=0) + w.M * w.K * 2  # planes + scales read, W written
-        r[str(p)] = {"us": round(d * 1e3, 3), "GBps": round(nb / (d * 1e-3) / 1e9, 1),
-                     "frac_of_peak": round(nb / (d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    rows["dequantize_4096x4096"] = r
-    del rot
+            def dense(c):
+                bcq.bcq_dequantize(rot.stores[c], 4, Wd[c % nw])
+                torch.mm(rot.x[c], Wd[c % nw].t(), out=Y[c])
 
-    # prefill through the dense route (bcq_dequantize, then fp16 F.linear on
-    # hipBLASLt) against the matrix-core kernels at the largest batch they take,
-    # and at a batch past it; 4096x4096, p = 4
-    print("[bench] secondary prefill routes", file=sys.stderr, flush=True)
-    r = {}
-    for b in (256, 1024):
-        w = bcq_synth.make(4096, 4096, 4, b=b, seed=7)
-        rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
-        Y = [torch.empty((b, w.M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
-
-        def dense(c):
-            bcq.bcq_dequantize(rot.stores[c], 4, Wd[c % nw])
-            torch.mm(rot.x[c], Wd[c % nw].t(), out=Y[c])
-
-        row = {"dequant_then_gemm_us": round(rotating_calls(torch, rot, dense, n, 10, flush)
-                                             * 1e3, 3),
-               "gemm_only_us": round(rotating_calls(torch, rot, lambda c: torch.mm(
-                   rot.x[c], Wd[c % nw].t(), out=Y[c]), n, 10, flush) * 1e3, 3)}
-        if b <= bcq.BCQ_MAX_BATCH:
-            ws = bcq.new_workspace(rot.stores[0], b)
-            row["bcq_matrix_cores_us"] = round(rotating_calls(torch, rot, lambda c: bcq.bcq_gemm_skinny(
-                rot.stores[c], 4, rot.x[c], Y[c], workspace=ws), n, 10, flush) * 1e3, 3)
-            del ws
-        r["b%d" % b] = row
-        del rot, Y
-    rows["prefill_routes_4096x4096_p4"] = r
-    del Wd
-
-    # 4096x4096 at batch 1 with one store repeated (planes served from the
-    # Infinity Cache after the first call): context for the cold numbers
-    w = bcq_synth.config(2)
-    st = bcq.Store.from_host(w.signs, w.alpha, w.zero)
-    x = torch.from_numpy(np.ascontiguousarray(w.x[0])).cuda()
-    y = torch.empty(w.M, dtype=torch.float16, device="cuda")
-    rows["gemv_4096x4096_b1_warm_cache_us"] = {
-        str(p): round(time_calls(torch, lambda i, p=p: bcq.bcq_gemv(st, p, x, y), n, 10) * 1e3, 3)
-        for p in (2, 3, 4)}
-    del st, x, y
-
-    # per-request precision, 8 requests on 4096x4096 vs the same call at uniform p = max
-    w = bcq_synth.config(4)
-    rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=w.b)
-    Y = [torch.empty((w.b, w.M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
-    pr = [int(p) for p in w.p_req]
-    ws = bcq.new_workspace(rot.stores[0], w.b)
-    d_mixed = rotating_calls(torch, rot, lambda c: bcq.bcq_gemv_mixed_p(
-        rot.stores[c], pr, rot.x[c], Y[c], workspace=ws), n, 10, flush)
-    d_uni = rotating_calls(torch, rot, lambda c: bcq.bcq_gemm_skinny(
-        rot.stores[c], max(pr), rot.x[c], Y[c], workspace=ws), n, 10, flush)
-    nb = mixed_bytes(w.M, w.K, pr)
-    rows["mixed_p_4096x4096_b8"] = {
-        "p_req": pr,
-        "us": round(d_mixed * 1e3, 3),
-        "uniform_pmax_us": round(d_uni * 1e3, 3),
-        "GBps": round(nb / (d_mixed * 1e-3) / 1e9, 1),
-    }
-    del rot, Y, ws
-
-    # small batches (MLP shapes, p = 3) and matrix-core batches (p = 4).  The
-    # batches of 2..15 are timed on both routes (BCQ_FORCE_PATH=lut: vector-ALU
-    # tables; =mfma: matrix cores); "us" is the default route's time.
-    for (M, K), b, p in [((4096, 4096), 2, 4), ((4096, 4096), 4, 4), ((4096, 4096), 8, 4),
-                         ((14336, 4096), 4, 3), ((14336, 4096), 8, 3), ((4096, 14336), 4, 3),
-                         ((4096, 14336), 8, 3),
-                         ((4096, 4096), 16, 4), ((4096, 4096), 32, 4), ((4096, 4096), 64, 4),
-                         ((14336, 4096), 64, 4)]:
-        print("[bench] secondary %dx%d b=%d p=%d" % (M, K, b, p), file=sys.stderr, flush=True)
-        w = bcq_synth.make(M, K, 4, b=b, seed=5)
-        rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
-        Y = [torch.empty((b, M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
-        nb = algorithmic_bytes(M, K, p, b)
-        row = {}
-        for route in ((None, "lut", "mfma") if b < 16 else (None,)):
-            with force_path(route):
-                ws = bcq.new_workspace(rot.stores[0], b)  # None where the call needs none
-                d = rotating_calls(torch, rot, lambda c: bcq.bcq_gemm_skinny(
-                    rot.stores[c], p, rot.x[c], Y[c], workspace=ws), n, 10, flush)
+            row = {"dequant_then_gemm_us": round(rotating_calls(torch, rot, dense, n, 10, flush)
+                                                 * 1e3, 3),
+                   "gemm_only_us": round(rotating_calls(torch, rot, lambda c: torch.mm(
+                       rot.x[c], Wd[c % nw].t(), out=Y[c]), n, 10, flush) * 1e3, 3)}
+            if b <= bcq.BCQ_MAX_BATCH:
+                ws = bcq.new_workspace(rot.stores[0], b)
+                row["bcq_matrix_cores_us"] = round(rotating_calls(torch, rot, lambda c: bcq.bcq_gemm_skinny(
+                    rot.stores[c], 4, rot.x[c], Y[c], workspace=ws), n, 10, flush) * 1e3, 3)
                 del ws
-            t = d * 1e-3
-            key = "us" if route is None else "us_" + route
-            row[key] = round(t * 1e6, 3)
-            if route is None:
-                row["GBps"] = round(nb / t / 1e9, 1)
-                if b >= 16:
-                    row["mfma_util"] = round(2.0 * M * K * b / t / 2.5e15, 4)
-        rows["skinny_%dx%d_b%d_p%d" % (M, K, b, p)] = row
-        del rot, Y
+            r["b%d" % b] = row
+            del rot, Y
+        rows["prefill_routes_4096x4096_p4"] = r
+        del Wd
+
+    if want('gemv_4096x4096_b1_warm_cache'):
+        # 4096x4096 at batch 1 with one store repeated (planes served from the
+        # Infinity Cache after the first call): context for the cold numbers
+        w = bcq_synth.config(2)
+        st = bcq.Store.from_host(w.signs, w.alpha, w.zero)
+        x = torch.from_numpy(np.ascontiguousarray(w.x[0])).cuda()
+        y = torch.empty(w.M, dtype=torch.float16, device="cuda")
+        rows["gemv_4096x4096_b1_warm_cache_us"] = {
+            str(p): round(time_calls(torch, lambda i, p=p: bcq.bcq_gemv(st, p, x, y), n, 10) * 1e3, 3)
+            for p in (2, 3, 4)}
+        del st, x, y
+
+    if want('mixed_p'):
+        # per-request precision, 8 requests on 4096x4096 vs the same call at uniform p = max
+        w = bcq_synth.config(4)
+        rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=w.b)
+        Y = [torch.empty((w.b, w.M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+        pr = [int(p) for p in w.p_req]
+        ws = bcq.new_workspace(rot.stores[0], w.b)
+        d_mixed = rotating_calls(torch, rot, lambda c: bcq.bcq_gemv_mixed_p(
+            rot.stores[c], pr, rot.x[c], Y[c], workspace=ws), n, 10, flush)
+        d_uni = rotating_calls(torch, rot, lambda c: bcq.bcq_gemm_skinny(
+            rot.stores[c], max(pr), rot.x[c], Y[c], workspace=ws), n, 10, flush)
+        nb = mixed_bytes(w.M, w.K, pr)
+        rows["mixed_p_4096x4096_b8"] = {
+            "p_req": pr,
+            "us": round(d_mixed * 1e3, 3),
+            "uniform_pmax_us": round(d_uni * 1e3, 3),
+            "GBps": round(nb / (d_mixed * 1e-3) / 1e9, 1),
+        }
+        del rot, Y, ws
+
+    if want('quantize'):
+        # the offline quantizer on one 4096x4096 fp16 weight matrix: 20
+        # refinement rounds at 2 planes, then expansion to 4 (fp16 tables)
+        print("[bench] secondary quantize", file=sys.stderr, flush=True)
+        W = torch.from_numpy(bcq_synth.weights(4096, 4096, seed=44)).cuda()
+        bcq.bcq_quantize(W, 4, 2, 20)
+        torch.cuda.synchronize()
+        d = time_calls(torch, lambda i: bcq.bcq_quantize(W, 4, 2, 20), 5, 1)
+        rows["quantize_4096x4096_P4_from2_20rounds"] = {
+            "us": round(d * 1e3, 1), "weights_per_s": round(4096 * 4096 / (d * 1e-3), 0)}
+        del W
+
+    if want('skinny'):
+        # small batches (MLP shapes, p = 3) and matrix-core batches (p = 4).  The
+        # batches of 2..15 are timed on both routes (BCQ_FORCE_PATH=lut: vector-ALU
+        # tables; =mfma: matrix cores); "us" is the default route's time.
+        for (M, K), b, p in [((4096, 4096), 2, 4), ((4096, 4096), 4, 4), ((4096, 4096), 8, 4),
+                             ((14336, 4096), 4, 3), ((14336, 4096), 8, 3), ((4096, 14336), 4, 3),
+                             ((4096, 14336), 8, 3),
+                             ((4096, 4096), 16, 4), ((4096, 4096), 32, 4), ((4096, 4096), 64, 4),
+                             ((14336, 4096), 64, 4)]:
+            if not want("skinny_%dx%d_b%d_p%d" % (M, K, b, p)):
+                continue
+            print("[bench] secondary %dx%d b=%d p=%d" % (M, K, b, p), file=sys.stderr, flush=True)
+            w = bcq_synth.make(M, K, 4, b=b, seed=5)
+            rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
+            Y = [torch.empty((b, M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+            nb = algorithmic_bytes(M, K, p, b)
+            row = {}
+            for route in ((None, "lut", "mfma") if b < 16 else (None,)):
+                with force_path(route):
+                    ws = bcq.new_workspace(rot.stores[0], b)  # None where the call needs none
+                    d = rotating_calls(torch, rot, lambda c: bcq.bcq_gemm_skinny(
+                        rot.stores[c], p, rot.x[c], Y[c], workspace=ws), n, 10, flush)
+                    del ws
+                t = d * 1e-3
+                key = "us" if route is None else "us_" + route
+                row[key] = round(t * 1e6, 3)
+                if route is None:
+                    row["GBps"] = round(nb / t / 1e9, 1)
+                    if b >= 16:
+                        row["mfma_util"] = round(2.0 * M * K * b / t / 2.5e15, 4)
+            rows["skinny_%dx%d_b%d_p%d" % (M, K, b, p)] = row
+            del rot, Y
+
     return rows
 
 
@@ -643,6 +677,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--rows", default="",
+                    help="comma-separated name prefixes of the secondary rows to run "
+                         "(default: all), e.g. floor,gemv_,skinny_14336")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for HBM counter calibration)")
@@ -651,6 +688,10 @@ def main():
                          "on the 4096x4096 store (for per-dispatch HBM counters)")
     ap.add_argument("--counter-batch", type=int, default=1, metavar="B",
                     help="with --counter-run: run bcq_gemm_skinny at batch B (p = 4) instead")
+    ap.add_argument("--counter-shape", default="4096x4096", metavar="MxK",
+                    help="with --counter-run: the store's shape")
+    ap.add_argument("--counter-p", default="", metavar="P[,P..]",
+                    help="with --counter-run: precisions (default 2,3,4 at batch 1, else 4)")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="only summarise a rocprofv3 kernel-trace CSV (no GPU needed)")
     ap.add_argument("--trace-last", type=int, default=58,
@@ -686,11 +727,17 @@ def main():
 
     if args.counter_run:
         b = args.counter_batch
-        w = bcq_synth.make(4096, 4096, 4, b=b, seed=2) if b > 1 else bcq_synth.config(2)
+        Mc, Kc = (int(v) for v in args.counter_shape.split("x"))
+        if b == 1 and (Mc, Kc) == (4096, 4096):
+            w = bcq_synth.config(2)
+        else:
+            w = bcq_synth.make(Mc, Kc, 4, b=b, seed=2)
         rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
         ys = [torch.empty((b, w.M), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
         ws = bcq.new_workspace(rot.stores[0], b) if b > 1 else None
-        for p in ((2, 3, 4) if b == 1 else (4,)):
+        plist = ([int(v) for v in args.counter_p.split(",")] if args.counter_p
+                 else ([2, 3, 4] if b == 1 else [4]))
+        for p in plist:
             for i in range(args.counter_run):
                 c = i % rot.n
                 if b == 1:
@@ -699,7 +746,8 @@ def main():
                     bcq.bcq_gemm_skinny(rot.stores[c], p, rot.x[c], ys[c], workspace=ws)
         torch.cuda.synchronize()
         print(json.dumps({"counter_run_calls_per_p": args.counter_run, "batch": b,
-                          "copies": rot.n}))
+                          "shape": [w.M, w.K], "p": plist, "copies": rot.n,
+                          "route": os.environ.get("BCQ_FORCE_PATH", "default")}))
         return
 
     flush = Flush(torch)

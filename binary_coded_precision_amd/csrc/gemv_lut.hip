@@ -176,6 +176,28 @@ __device__ __forceinline__ float sum8_lanes(float v) {
   return v;
 }
 
+// Sum over the 32 lanes of an aligned half-wavefront, returned in all 32:
+// sum8_lanes, then the other 8-lane block of the 16-lane row (DPP
+// row_mirror), then the other row of the half (ds_swizzle, xor 16 within 32
+// lanes).  No bounds checks or address arithmetic, unlike a generic shuffle.
+__device__ __forceinline__ float sum32_lanes(float v) {
+  v = sum8_lanes(v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF,
+                                                         0xF, true));  // row_mirror
+  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                            0x401F));  // xor 16
+  return v;
+}
+
+// v + the value of lane (lane xor 16) and lane (lane xor 32): the sum over the
+// four 16-lane rows at the same position, in all lanes.  xor32 is the LDS
+// byte address ((lane ^ 32) * 4) for ds_bpermute, computed once by the caller.
+__device__ __forceinline__ float sum_rows4(float v, int xor32) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xor32, __builtin_bit_cast(int, v)));
+  return v;
+}
+
 // ---------------------------------------------------------------- batch 1
 
 constexpr int kG1Ksub = 16;         // groups per window of tables
@@ -186,9 +208,7 @@ constexpr int kG1ChunkStride = 80;  // bytes per chunk table: 16 entries + 16 B 
 // writeback holds both products of its 8 outputs: out = silu(g) * u with
 // silu(g) = g / (1 + exp(-g)), from the fp32 sums, rounded once.
 constexpr int kGuRows = kTileRows / 2;
-__device__ __forceinline__ float gate_up_out(float g, float u) {
-  return g / (1.f + expf(-g)) * u;
-}
+__device__ __forceinline__ float gate_up_out(float g, float u) { return silu_mul(g, u); }
 
 // ------------------------------------------------ batch 1, whole-K tables
 //
@@ -310,11 +330,11 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   const uint2 *bits2 = reinterpret_cast<const uint2 *>(bits);
 
   // ---- activations for the tables: thread tid builds chunk tid % 512 of
-  // window tid / 512
+  // window tid / 512 (a 32-bit offset from the uniform base x)
   const int bc = tid % kChunksPerGroup;
   const int bj = tid / kChunksPerGroup;  // group of K whose chunk this thread builds
   const typename Act<T>::raw xr = Act<T>::load(
-      x + (size_t)min(bj, G - 1) * kGroup + chunk_base(bc), chunk_parity(bc));
+      x + (unsigned)(min(bj, G - 1) * kGroup + chunk_base(bc)), chunk_parity(bc));
 
   // ---- scales and offsets of every tile.  Thread (row, group) =
   // ((tid % kPos) / kMaxG, tid % kMaxG) owns one position of a tile's 16 x G
@@ -343,20 +363,26 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   // ---- sign words of this lane's half group, one uint2 per plane.  Past my
   // last tile a fetch re-reads my own last tile (lines already in flight), so
   // the load phase stays branch-free.
+  // A tile's block of one plane is G * 16 uint4 (G * 32 uint2) from a base
+  // that is uniform across the workgroup; a lane's uint2 within it is the
+  // 32-bit lq, so each load is a scalar base plus a vector 32-bit offset.
   uint2 tiles[2][P];
   const int js = min(win * kG1Ksub + gw, G - 1);
+  const unsigned lq = (unsigned)((js * kTileRows + (RS > 1 ? prow : r)) * 2 + half);
   auto fetch = [&](int k, uint2 (&o)[P]) {
     if constexpr (RS > 1) {
-      const int t = (int)blockIdx.x / RS;
-      const size_t q = (((size_t)t * G + js) * kTileRows + prow) * 2 + half;
+      const uint2 *tb = bits2 + (size_t)((int)blockIdx.x / RS) * G * (kTileRows * 2);
 #pragma unroll
       for (int u = 0; u < PC; ++u)
-        o[u] = bits2[(size_t)min(ph * PC + u, P - 1) * plane_stride * 2 + q];
+        o[u] = tb[(size_t)min(ph * PC + u, P - 1) * plane_stride * 2 + lq];
     } else {
       const int t = (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x;
-      const size_t q = (((size_t)t * G + js) * kTileRows + r) * 2 + half;  // uint2 index
+      const uint2 *tb = bits2 + (size_t)t * G * (kTileRows * 2);
 #pragma unroll
-      for (int i = 0; i < P; ++i) o[i] = bits2[i * plane_stride * 2 + q];
+      for (int i = 0; i < P; ++i) {
+        const uint2 *pb = tb + (size_t)i * plane_stride * 2;
+        o[i] = pb[lq];
+      }
     }
   };
   // tile 0's sign words after the scales (the barrier below waits for those);
@@ -384,9 +410,7 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
     dst[1] = v[1];
     dst[2] = v[2];
     dst[3] = v[3];
-    float cs = (f[0] + f[1]) + (f[2] + f[3]);
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) cs += __shfl_xor(cs, off);
+    const float cs = sum32_lanes((f[0] + f[1]) + (f[2] + f[3]));
     if ((tid & 31) == 0) gsum[bj] = cs;
   }
 #pragma unroll
@@ -431,12 +455,18 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   }
 
   // ---- reduce the slot partials of each row of each tile, fixed order
+  const int xor32 = (lane ^ 32) << 2;
 #pragma unroll
   for (int k = 0; k < TMAX; ++k) {
-    acc[k] += __shfl_xor(acc[k], 16);
-    acc[k] += __shfl_xor(acc[k], 32);
-#pragma unroll
-    for (int m = kPartRows; m < kTileRows; m <<= 1) acc[k] += __shfl_xor(acc[k], m);  // plane parts
+    acc[k] = sum_rows4(acc[k], xor32);
+    // plane parts: lanes r, r + 16/RS, .. of a row hold one row's planes
+    // (rotations within the 16-lane row, DPP row_ror)
+    if constexpr (RS == 4)
+      acc[k] += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                              __builtin_bit_cast(int, acc[k]), 0x124, 0xF, 0xF, true));
+    if constexpr (RS >= 2)
+      acc[k] += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                              __builtin_bit_cast(int, acc[k]), 0x128, 0xF, 0xF, true));
     if (lane < 16) part[wave][k][lane] = acc[k];
   }
   __syncthreads();
@@ -523,23 +553,30 @@ __global__ __launch_bounds__(kRThreads) void gemv_stream_kernel(
   const int sa = min(tid / (kTileRows * 4), P);
   const int srow = (tid / 4) % kTileRows;
   const int sq = tid % 4;
-  const int s_m = min(tile * kTileRows + srow, M - 1);
-  const T *sbase = sa < P ? alpha + sa * MG + (size_t)s_m * G : zero + (size_t)s_m * G;
+  // scalar base of this wavefront's staging array (sa is the same for all 64
+  // lanes) plus a 32-bit row offset within the tile
+  const T *sbase = (sa < P ? alpha + (size_t)__builtin_amdgcn_readfirstlane(sa) * MG : zero) +
+                   (size_t)tile * kTileRows * G +
+                   (unsigned)(min(srow, M - 1 - tile * kTileRows) * G);
 
   auto fetch_bits = [&](int v, Slot &o) __attribute__((always_inline)) {
     const int w = min(v, nwin - 1);
     const int js = min(w * kG1Ksub + gw, G - 1);
-    const size_t q = (((size_t)tile * G + js) * kTileRows + r) * 2 + half;  // uint2 index
+    const unsigned lq = (unsigned)((js * kTileRows + r) * 2 + half);  // uint2 within the tile
+    const uint2 *tb = bits2 + (size_t)tile * G * (kTileRows * 2);
 #pragma unroll
-    for (int i = 0; i < P; ++i) o.bits[i] = bits2[i * plane_stride * 2 + q];
+    for (int i = 0; i < P; ++i) {
+      const uint2 *pb = tb + (size_t)i * plane_stride * 2;
+      o.bits[i] = pb[lq];
+    }
   };
   auto fetch_small = [&](int v, Slot &o) __attribute__((always_inline)) {
     const int w = min(v, nwin - 1);
     const int c = tid % kChunksPerGroup;
     const int jx = min(w * kG1Ksub + tid / kChunksPerGroup, G - 1);
-    o.x = Act<T>::load(x + (size_t)jx * kGroup + chunk_base(c), chunk_parity(c));
+    o.x = Act<T>::load(x + (unsigned)(jx * kGroup + chunk_base(c)), chunk_parity(c));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o.sc[e] = load_raw(sbase + min(w * kG1Ksub + 4 * sq + e, G - 1));
+    for (int e = 0; e < 4; ++e) o.sc[e] = load_raw(sbase + (unsigned)min(w * kG1Ksub + 4 * sq + e, G - 1));
   };
   auto fetch = [&](int v, Slot &o) __attribute__((always_inline)) {
     fetch_bits(v, o);
@@ -602,8 +639,7 @@ __global__ __launch_bounds__(kRThreads) void gemv_stream_kernel(
   }
 
   // ---- reduce the 32 slot partials of each row in a fixed order
-  acc += __shfl_xor(acc, 16);
-  acc += __shfl_xor(acc, 32);
+  acc = sum_rows4(acc, (lane ^ 32) << 2);
   if (lane < 16) part[wave][lane] = acc;
   __syncthreads();
   if constexpr (GU) {
@@ -663,8 +699,11 @@ __device__ __forceinline__ void stream_half(StreamShared<T, P> &sm, const uint4 
   const int sa = min(tid / (kTileRows * 4), P);
   const int srow = (tid / 4) % kTileRows;
   const int sq = tid % 4;
-  const int s_m = min(tile * kTileRows + srow, M - 1);
-  const T *sbase = sa < P ? alpha + sa * MG + (size_t)s_m * G : zero + (size_t)s_m * G;
+  // scalar base of this wavefront's staging array (sa is the same for all 64
+  // lanes) plus a 32-bit row offset within the tile
+  const T *sbase = (sa < P ? alpha + (size_t)__builtin_amdgcn_readfirstlane(sa) * MG : zero) +
+                   (size_t)tile * kTileRows * G +
+                   (unsigned)(min(srow, M - 1 - tile * kTileRows) * G);
 
   struct Slot {
     uint2 bits[NP];
@@ -674,19 +713,23 @@ __device__ __forceinline__ void stream_half(StreamShared<T, P> &sm, const uint4 
   auto fetch_bits = [&](int v, Slot &o) __attribute__((always_inline)) {
     const int w = min(v, nwin - 1);
     const int js = min(w * kG1Ksub + gw, G - 1);
-    const size_t q = (((size_t)tile * G + js) * kTileRows + r) * 2 + half;  // uint2 index
+    const unsigned lq = (unsigned)((js * kTileRows + r) * 2 + half);  // uint2 within the tile
+    const uint2 *tb = bits2 + (size_t)tile * G * (kTileRows * 2);
 #pragma unroll
-    for (int u = 0; u < NP; ++u) o.bits[u] = bits2[(I0 + u) * plane_stride * 2 + q];
+    for (int u = 0; u < NP; ++u) {
+      const uint2 *pb = tb + (size_t)(I0 + u) * plane_stride * 2;
+      o.bits[u] = pb[lq];
+    }
   };
   auto fetch_small = [&](int v, Slot &o) __attribute__((always_inline)) {
     if constexpr (!UPPER) {
       const int w = min(v, nwin - 1);
       const int c = tid % kChunksPerGroup;
       const int jx = min(w * kG1Ksub + tid / kChunksPerGroup, G - 1);
-      o.x = Act<T>::load(x + (size_t)jx * kGroup + chunk_base(c), chunk_parity(c));
+      o.x = Act<T>::load(x + (unsigned)(jx * kGroup + chunk_base(c)), chunk_parity(c));
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        o.sc[e] = load_raw(sbase + min(w * kG1Ksub + 4 * sq + e, G - 1));
+        o.sc[e] = load_raw(sbase + (unsigned)min(w * kG1Ksub + 4 * sq + e, G - 1));
     }
   };
   auto fetch = [&](int v, Slot &o) __attribute__((always_inline)) {
@@ -747,8 +790,7 @@ __device__ __forceinline__ void stream_half(StreamShared<T, P> &sm, const uint4 
       fetch(w + kStreamRing, ring[k]);
     }
   }
-  acc += __shfl_xor(acc, 16);
-  acc += __shfl_xor(acc, 32);
+  acc = sum_rows4(acc, (lane ^ 32) << 2);
   if (lane < 16) sm.part[(UPPER ? kRWaves : 0) + wave][lane] = acc;
 }
 
