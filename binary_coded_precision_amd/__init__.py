@@ -44,6 +44,7 @@ EXPORTS = (
     "bcq_unpack_planes",
     "bcq_gemv",
     "bcq_gemv_gate_up",
+    "bcq_gemm_gate_up",
     "bcq_gemm_skinny",
     "bcq_gemm_skinny_noalloc",
     "bcq_workspace_bytes",
@@ -99,6 +100,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
         "bcq_unpack_planes": (ctypes.c_int, [vp, i32, i32, i32, vp, vp]),
         "bcq_gemv": (ctypes.c_int, [st, i32, vp, ctypes.c_int, vp, ctypes.c_int, vp]),
         "bcq_gemv_gate_up": (ctypes.c_int, [st, i32, vp, ctypes.c_int, vp, ctypes.c_int, vp]),
+        "bcq_gemm_gate_up": (ctypes.c_int, [st, vp, vp, i32, i32, ctypes.c_int, vp, i32,
+                                            ctypes.c_int, vp]),
         "bcq_gemm_skinny": (ctypes.c_int, [st, i32, vp, i32, i32, ctypes.c_int, vp, i32,
                                            ctypes.c_int, vp, sz, vp]),
         "bcq_gemm_skinny_noalloc": (ctypes.c_int, [st, i32, vp, i32, i32, ctypes.c_int, vp, i32,
@@ -238,6 +241,21 @@ def bcq_gemv_gate_up(store: "Store", p: int, x, y, stream=None) -> None:
     _check("bcq_gemv_gate_up", load().bcq_gemv_gate_up(store.ref(), p, _ptr(x), _dtype_code(x),
                                                        _ptr(y), _dtype_code(y),
                                                        _stream(stream)))
+
+
+def bcq_gemm_gate_up(store: "Store", p_host: Sequence[int], X, Y, stream=None) -> None:
+    """``Y[r][j] = silu(gate_j . X[r]) * (up_j . X[r])`` at precision ``p_host[r]``
+    for a gate/up store (see :func:`bcq_gemv_gate_up`); ``Y`` is [b][>= M/2]."""
+    b = X.shape[0]
+    if len(p_host) != b:
+        raise ValueError("p_host has %d entries for %d requests" % (len(p_host), b))
+    _need_mat("X", X, b, store.K)
+    _need_mat("Y", Y, b, store.M // 2)
+    _check_store_tensors(store, p_host)
+    ps = (ctypes.c_int32 * b)(*[int(v) for v in p_host])
+    _check("bcq_gemm_gate_up",
+           load().bcq_gemm_gate_up(store.ref(), ps, _ptr(X), b, X.stride(0), _dtype_code(X),
+                                   _ptr(Y), Y.stride(0), _dtype_code(Y), _stream(stream)))
 
 
 def bcq_lowrank_correct(u_signs, v_signs, alpha, x, y, z=None, stream=None) -> None:

@@ -247,6 +247,55 @@ bcq_status bcq_gemv_gate_up(const bcq_store *store, int32_t p, const void *x, bc
                                              store->scale_dtype, stream));
 }
 
+bcq_status bcq_gemm_gate_up(const bcq_store *store, const int32_t *p_host, const void *X,
+                            int32_t b, int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,
+                            bcq_dtype y_dtype, hipStream_t stream) {
+  BCQ_TRY(check_store(store));
+  BCQ_TRY(check_dtypes(store, x_dtype, y_dtype));
+  if (store->M % bcq::kTileRows != 0) return BCQ_ERR_INVALID_ARG;
+  if (X == nullptr || Y == nullptr || p_host == nullptr) return BCQ_ERR_INVALID_ARG;
+  if (b < 1 || b > BCQ_MAX_BATCH || ldx < store->K || ldy < store->M / 2)
+    return BCQ_ERR_INVALID_ARG;
+  const size_t es = dtype_size(store->scale_dtype);
+  if (!aligned(X, 16) || ((size_t)ldx * es) % 16 != 0 || !aligned(Y, es)) return BCQ_ERR_ALIGNMENT;
+  for (int32_t r = 0; r < b; ++r) BCQ_TRY(check_precision(store, p_host[r]));
+  const char *Xc = static_cast<const char *>(X);
+  char *Yc = static_cast<char *>(Y);
+  int32_t pmax = 0;
+  bool shared = true;
+  for (int32_t r = 0; r < b; ++r) pmax = p_host[r] > pmax ? p_host[r] : pmax;
+  for (int32_t r = 0; r < b; ++r)
+    shared = shared && store->alpha[p_host[r]] == store->alpha[pmax] &&
+             store->zero[p_host[r]] == store->zero[pmax];
+  if (store->scale_dtype == BCQ_F16 && shared && b >= 2 && bcq::mfma_gate_up_ok(store->K, 16)) {
+    // launches of up to 16 requests on the matrix cores, each at the largest
+    // precision of its requests, every request summing its own planes
+    log_route("bcq_gemm_gate_up", store, b, "matrix cores, whole K, silu(gate)*up epilogue");
+    for (int32_t r0 = 0; r0 < b; r0 += 16) {
+      const int n = (b - r0) < 16 ? (b - r0) : 16;
+      int32_t pm = 0;
+      for (int q = 0; q < n; ++q) pm = p_host[r0 + q] > pm ? p_host[r0 + q] : pm;
+      hipError_t e = bcq::launch_gemm_gate_up(store->bits, store->M, store->K, pm,
+                                              store->alpha[pm], store->zero[pm],
+                                              Xc + (size_t)r0 * ldx * es, ldx, n,
+                                              Yc + (size_t)r0 * ldy * es, ldy, p_host + r0, stream);
+      if (e != hipSuccess) return BCQ_ERR_HIP;
+    }
+    return BCQ_OK;
+  }
+  // otherwise the batch-1 fused kernel, request by request, each with its own
+  // precision's tables
+  log_route("bcq_gemm_gate_up", store, b, "batch-1 fused kernel per request");
+  for (int32_t r = 0; r < b; ++r) {
+    const int32_t p = p_host[r];
+    hipError_t e = bcq::launch_gemv_gate_up(store->bits, store->M, store->K, p, store->alpha[p],
+                                            store->zero[p], Xc + (size_t)r * ldx * es,
+                                            Yc + (size_t)r * ldy * es, store->scale_dtype, stream);
+    if (e != hipSuccess) return BCQ_ERR_HIP;
+  }
+  return BCQ_OK;
+}
+
 bcq_status bcq_dequantize(const bcq_store *store, int32_t p, void *W, int32_t ldw,
                           bcq_dtype w_dtype, hipStream_t stream) {
   BCQ_TRY(check_store(store));

@@ -16,6 +16,10 @@ constexpr int kGroup = BCQ_GROUP;
 
 inline int row_tiles(int M) { return (M + kTileRows - 1) / kTileRows; }
 
+// The gated-MLP epilogue of a gate/up store: silu(g) * u with
+// silu(g) = g / (1 + exp(-g)), in fp32.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
+
 // Scale description used by the batched table kernel.  Each request of a
 // launch has its own precision and reads the scale/offset tables of that
 // precision (AnyBCQ per-request precision).  The host lists every distinct
@@ -86,6 +90,16 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
                             const void *zero, const void *x, int ldx, int b, void *y, int ldy,
                             void *ws, const int32_t *p_req, hipStream_t s);
 size_t mfma_workspace_bytes(int M, int K, int b);
+
+// Gate/up stores at batch b <= 16 with K <= 4096 (mfma_gate_up_ok), fp16:
+// the whole-K matrix-core kernel with the silu(gate) * up epilogue; request
+// q at precision p_req[q] (host, b values in 1..p; nullptr: all p), the tables
+// alpha / zero of precision p serving every request.  Y is [b][ldy], M / 2
+// outputs per request.
+bool mfma_gate_up_ok(int K, int n);
+hipError_t launch_gemm_gate_up(const uint32_t *bits, int M, int K, int p, const void *alpha,
+                               const void *zero, const void *x, int ldx, int b, void *y, int ldy,
+                               const int32_t *p_req, hipStream_t s);
 
 // True when a launch of n fp16 requests on (M, K) keeps K within one
 // workgroup (no workspace, no second kernel).

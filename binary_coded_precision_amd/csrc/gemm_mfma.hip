@@ -562,7 +562,11 @@ __device__ __forceinline__ floatx4 wk_sum(const floatx4 (&acc)[P + 1], const MfP
   return d;
 }
 
-template <int P, bool MIXED>
+// GU: a gate/up store (rows 0..7 of each 16-row tile are gate rows, 8..15 the
+// matching up rows, as bcq_gemv_gate_up lays them out); each tile's eight
+// outputs per request are silu(gate) * up, evaluated in fp32 on the summed
+// partial products and rounded once.
+template <int P, bool MIXED, bool GU = false>
 __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
     const u32x4 *__restrict__ bits, const half_t *__restrict__ alpha,
     const half_t *__restrict__ zero, const half_t *__restrict__ X, int ldx, int b,
@@ -634,7 +638,24 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
   // even) in wavefront order and store them: one pair of barriers per two tiles
   auto flush = [&](int k0, int n) __attribute__((always_inline)) {
     __syncthreads();
-    if (tid < 64 * 4 * n) {
+    if constexpr (GU) {
+      // gate row i (lane l < 32, element v: row 4 * (l >> 4) + v) meets up row
+      // i + 8 in lane l + 32, element v; output row t * 8 + i
+      if (tid < 32 * 4 * n) {
+        const int kk = tid >> 7;
+        const int l = (tid >> 2) & 31, v = tid & 3;
+        const int c = l & 15;
+        const int t = (int)blockIdx.x + (k0 + kk) * (int)gridDim.x;
+        const int jo = t * (kTileRows / 2) + 4 * (l >> 4) + v;
+        float gs = 0.f, us = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWkWaves; ++w) {
+          gs += red[kk][w][l][v];
+          us += red[kk][w][l + 32][v];
+        }
+        if (c < b && jo < M / 2) Y[(size_t)c * ldy + jo] = (half_t)silu_mul(gs, us);
+      }
+    } else if (tid < 64 * 4 * n) {
       const int kk = tid >> 8;
       const int l = (tid >> 2) & 63, v = tid & 3;
       const int c = l & 15;
@@ -777,6 +798,42 @@ size_t mfma_workspace_bytes(int M, int K, int b) {
     }
   }
   return need;
+}
+
+bool mfma_gate_up_ok(int K, int n) { return n <= 16 && K / kGroup <= kWkMaxGroups; }
+
+hipError_t launch_gemm_gate_up(const uint32_t *bits, int M, int K, int p, const void *alpha,
+                               const void *zero, const void *x, int ldx, int b, void *y, int ldy,
+                               const int32_t *p_req, hipStream_t s) {
+  const int G = K / kGroup;
+  const int MT = row_tiles(M);
+  const u32x4 *b4 = reinterpret_cast<const u32x4 *>(bits);
+  const half_t *a = static_cast<const half_t *>(alpha);
+  const half_t *z = static_cast<const half_t *>(zero);
+  const half_t *X = static_cast<const half_t *>(x);
+  half_t *Y = static_cast<half_t *>(y);
+  MfPrec prec;
+  bool mixed = false;
+  for (int q = 0; q < kMfMaxBatch; ++q) {
+    prec.p[q] = (uint8_t)(p_req != nullptr && q < b ? p_req[q] : p);
+    mixed = mixed || (q < b && prec.p[q] != p);
+  }
+  const dim3 grid(MT < kMfSlots ? MT : kMfSlots), block(64 * kWkWaves);
+#define BCQ_WKGU(PV)                                                                          \
+  if (mixed)                                                                                  \
+    hipLaunchKernelGGL((gemm_wk_kernel<PV, true, true>), grid, block, 0, s, b4, a, z, X, ldx, b, \
+                       Y, ldy, M, G, MT, prec);                                               \
+  else                                                                                        \
+    hipLaunchKernelGGL((gemm_wk_kernel<PV, false, true>), grid, block, 0, s, b4, a, z, X, ldx, \
+                       b, Y, ldy, M, G, MT, prec)
+  switch (p) {
+    case 1: BCQ_WKGU(1); break;
+    case 2: BCQ_WKGU(2); break;
+    case 3: BCQ_WKGU(3); break;
+    default: BCQ_WKGU(4); break;
+  }
+#undef BCQ_WKGU
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const void *alpha,

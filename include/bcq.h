@@ -168,6 +168,30 @@ bcq_status bcq_gemv_gate_up(const bcq_store *store, int32_t p, const void *x, bc
                             void *y, bcq_dtype y_dtype, hipStream_t stream);
 
 /*
+ * The gated-MLP epilogue of bcq_gemv_gate_up for a batch of requests, each at
+ * its own precision: Y[r][j] = silu(g_rj) * u_rj for j < M/2, where g_rj and
+ * u_rj are the BCQ products at precision p_host[r] of gate row j and up row j
+ * with X[r] (AnyBCQ paper notes, "Method / key designs" for the products and
+ * "overall framework" for per-request precision), silu(g) = g / (1 +
+ * exp(-g)) in fp32 on the fp32 sums, rounded once.  The store is laid out as
+ * for bcq_gemv_gate_up (M a multiple of 16; rows 0..7 of each 16-row tile the
+ * gate rows, 8..15 the matching up rows).
+ * Routes: fp16 batches of 2 and more whose precisions read one shared scale
+ * table (alpha[p], zero[p] aliasing those of the largest requested p) and
+ * K <= 4096 run on the matrix cores in launches of up to 16 requests (the
+ * whole-K kernel of bcq_gemm_skinny, each plane an exact fp16 operand, the
+ * epilogue on the summed partial products); all other calls run the batch-1
+ * fused kernel once per request.  No workspace.
+ * p_host: [b] in HOST memory, every entry in [1, planes] with its tables
+ *   present; X: [b][ldx] (ldx >= K, 16-byte aligned, ldx*size a multiple of
+ *   16 bytes); Y: [b][ldy], ldy >= M/2, element aligned.  1 <= b <=
+ *   BCQ_MAX_BATCH.  Dtypes, validation and stream behaviour as in bcq_gemv.
+ */
+bcq_status bcq_gemm_gate_up(const bcq_store *store, const int32_t *p_host, const void *X,
+                            int32_t b, int32_t ldx, bcq_dtype x_dtype, void *Y, int32_t ldy,
+                            bcq_dtype y_dtype, hipStream_t stream);
+
+/*
  * Y[r] = BCQ product at precision p for each of b activation rows X[r].
  * Defined by: the product of bcq_gemv (AnyBCQ paper notes, "Method / key
  * designs") applied to every row of a decode batch; one read of the first p

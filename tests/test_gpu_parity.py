@@ -847,6 +847,63 @@ def test_gate_up_mlp_shape_every_output():
         assert rel_l2(y.cpu().numpy(), ref) <= 2e-3, p
 
 
+@pytest.mark.parametrize("Mo,K,b,dt,mixed", [
+    (32, 1024, 4, np.float16, False),    # matrix cores, one tile per workgroup
+    (2048, 4096, 8, np.float16, True),   # matrix cores, per-request precision
+    (5000, 4096, 16, np.float16, True),  # several tiles per workgroup, a full request tile
+    (264, 2048, 20, np.float16, False),  # two launches (16 + 4)
+    (256, 6144, 4, np.float16, True),    # K past 4096: the batch-1 fused kernel per request
+    (64, 512, 3, np.float32, True),      # fp32: the batch-1 fused kernel per request
+])
+def test_gate_up_batched_per_request_precision(Mo, K, b, dt, mixed):
+    """bcq_gemm_gate_up: silu(gate . X[r]) * (up . X[r]) for each request at its
+    own precision, every output against the float64 oracle; padded output
+    rows untouched."""
+    w = bcq_synth.make(2 * Mo, K, 4, b=b, dtype=dt, seed=Mo + K + b, outlier_frac=0.01,
+                       p_choices=(1, 2, 3, 4) if mixed else (3,))
+    st = store_of(w)
+    ps = [int(p) for p in w.p_req] if mixed else [3] * b
+    tdt = torch.float16 if dt == np.float16 else torch.float32
+    Y = torch.full((b, Mo + 5), 5.0, dtype=tdt, device="cuda")
+    say("gate_up batched", Mo, K, b, np.dtype(dt).name, ps)
+    bcq.bcq_gemm_gate_up(st, ps, dev(w.x), Y[:, :Mo])
+    got = Y[:, :Mo].cpu().numpy()
+    gr, ur = oracle.gate_up_rows(np.arange(Mo))
+    for r, p in enumerate(ps):
+        yr = oracle_y_all(w, w.x[r:r + 1], [p])[0]
+        assert rel_l2(got[r], oracle.silu_mul(yr[gr], yr[ur])) <= TOL[np.dtype(dt)], (r, p)
+    assert (Y[:, Mo:].float() == 5.0).all()
+
+
+def test_gate_up_batched_independent_tables_and_mlp_shape():
+    """Per-precision tables that do not alias run request by request; the
+    MLP's 14336-output gate/up store at b = 4 and 8 (p = 3) on the matrix
+    cores, every output."""
+    w = bcq_synth.independent_tables(
+        bcq_synth.make(2 * 96, 1024, 4, b=4, dtype=np.float16, seed=41, p_choices=(1, 2, 3, 4)))
+    st = store_of(w, independent=True)
+    ps = [int(p) for p in w.p_req]
+    Y = torch.empty((4, 96), dtype=torch.float16, device="cuda")
+    say("gate_up batched independent", ps)
+    bcq.bcq_gemm_gate_up(st, ps, dev(w.x), Y)
+    gr, ur = oracle.gate_up_rows(np.arange(96))
+    for r, p in enumerate(ps):
+        yr = oracle_y(w, w.x[r:r + 1], [p])[0]
+        assert rel_l2(Y[r].cpu().numpy(), oracle.silu_mul(yr[gr], yr[ur])) <= 2e-3, r
+    Mo = 14336
+    w = bcq_synth.make(2 * Mo, 4096, 4, b=8, p=3, dtype=np.float16, seed=3)
+    st = store_of(w)
+    gr, ur = oracle.gate_up_rows(np.arange(Mo))
+    for b in (4, 8):
+        say("gate_up batched mlp", b)
+        Y = torch.empty((b, Mo), dtype=torch.float16, device="cuda")
+        bcq.bcq_gemm_gate_up(st, [3] * b, dev(w.x[:b]), Y)
+        got = Y.cpu().numpy()
+        ref = oracle_y_all(w, w.x[:b], [3] * b)
+        for r in range(b):
+            assert rel_l2(got[r], oracle.silu_mul(ref[r][gr], ref[r][ur])) <= 2e-3, (b, r)
+
+
 def test_qkv_concatenated_store():
     """q, k and v projections (4096, 1024 and 1024 rows of one 4096-column
     input) as one 6144-row store: one bcq_gemv call equals the three separate
