@@ -362,6 +362,28 @@ def secondary(args, bcq, torch, bcq_synth, flush):
         rows["gate_up_fused_28672x4096_b1"] = r
         del rot, ys
 
+    if want('gate_up_batched'):
+        # the same gate/up store at the MLP batches (4 and 8 requests, p = 3),
+        # fused epilogue (bcq_gemm_gate_up) against the plain batched product
+        # of all 28672 rows (bcq_gemm_skinny, both projections, no epilogue)
+        print("[bench] secondary gate/up batched", file=sys.stderr, flush=True)
+        Mo = 14336
+        r = {}
+        for b in (4, 8):
+            w = bcq_synth.make(2 * Mo, 4096, 4, b=b, seed=9, name="gate_up_28672x4096_b%d" % b)
+            rot = Rotation(w, ROTATE_BYTES, bcq, torch, with_x_rows=b)
+            Yg = [torch.empty((b, Mo), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+            Yp = [torch.empty((b, 2 * Mo), dtype=torch.float16, device="cuda") for _ in range(rot.n)]
+            dg = rotating_calls(torch, rot, lambda c: bcq.bcq_gemm_gate_up(
+                rot.stores[c], [3] * b, rot.x[c], Yg[c]), n, 10, flush)
+            dp = rotating_calls(torch, rot, lambda c: bcq.bcq_gemm_skinny(
+                rot.stores[c], 3, rot.x[c], Yp[c]), n, 10, flush)
+            nb = algorithmic_bytes(2 * Mo, 4096, 3, b) - b * Mo * 2
+            r["b%d" % b] = {"us": round(dg * 1e3, 3), "GBps": round(nb / (dg * 1e-3) / 1e9, 1),
+                            "product_without_epilogue_us": round(dp * 1e3, 3)}
+            del rot, Yg, Yp
+        rows["gate_up_batched_28672x4096_p3"] = r
+
     if want('qkv_concatenated'):
         # q, k and v (4096 + 1024 + 1024 rows over one 4096-wide input) as one
         # concatenated 6144-row store, next to the three separate products
@@ -634,9 +656,9 @@ def trace_summary(path: str, last: int) -> None:
     """Per-kernel duration statistics from a rocprofv3 kernel trace (see
     trace_dispatches): for each (kernel, grid) with at least 10 dispatches,
     count, mean, median, p10 and p90 in microseconds over all its dispatches,
-    and over the last `last` dispatches of its longest run of consecutive
-    dispatches (in a bench run, the timed replay of a cold per-precision
-    graph)."""
+    and over the last `last` dispatches of its last run of at least `last`
+    consecutive dispatches, else of its longest run (in a bench run, the timed
+    replay of a cold per-precision graph)."""
     seq = trace_dispatches(path)
 
     def stats(v):
@@ -647,24 +669,32 @@ def trace_summary(path: str, last: int) -> None:
                 "p90": round(float(np.percentile(v, 90)), 3)}
 
     groups = {}
-    runs = {}
+    runs = {}  # every run of consecutive dispatches of one (kernel, grid), in order
     prev, cur = None, []
     for _, name, grid, t in seq + [(None, None, None, None)]:
         k = (name, grid)
         if k != prev and prev is not None:
-            if len(cur) > len(runs.get(prev, [])):
-                runs[prev] = cur
+            runs.setdefault(prev, []).append(cur)
             cur = []
         if name is None:
             break
         groups.setdefault(k, []).append(t)
         cur.append(t)
         prev = k
+
+    def timed_run(k):
+        # the last run of at least `last` dispatches (in a bench run the timed
+        # replay comes after the warm-up calls and an untimed replay), else
+        # the longest
+        rs = runs.get(k, [])
+        full = [r for r in rs if len(r) >= last]
+        return full[-1] if full else max(rs, key=len, default=[])
+
     for k, v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         if len(v) < 10:
             continue
         out = {"kernel": k[0][:160], "grid": k[1], "all": stats(v)}
-        run = runs.get(k, [])
+        run = timed_run(k)
         if len(run) >= 10:
             out["longest_run_last"] = stats(run[-last:])
         print(json.dumps(out))
