@@ -36,6 +36,8 @@ BCQ_GROUP = 128
 BCQ_TILE_ROWS = 16
 BCQ_MAX_BATCH = 256
 BCQ_NOALLOC_SCRATCH_BYTES = 16 << 20
+BCQ_LOWRANK_MAX_RANK = 4096
+BCQ_LOWRANK_FUSED_MAX_RANK = 1024
 
 # Every symbol include/bcq.h declares.
 EXPORTS = (
@@ -50,6 +52,7 @@ EXPORTS = (
     "bcq_workspace_bytes",
     "bcq_gemv_mixed_p",
     "bcq_lowrank_correct",
+    "bcq_gemv_lowrank",
     "bcq_dequantize",
     "bcq_quantize",
     "bcq_status_string",
@@ -111,6 +114,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
                                             ctypes.c_int, vp, sz, vp]),
         "bcq_lowrank_correct": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp, ctypes.c_int,
                                                vp, vp]),
+        "bcq_gemv_lowrank": (ctypes.c_int, [st, i32, vp, ctypes.c_int, vp, vp, vp, i32, vp,
+                                            ctypes.c_int, vp, vp]),
         "bcq_dequantize": (ctypes.c_int, [st, i32, vp, i32, ctypes.c_int, vp]),
         "bcq_quantize": (ctypes.c_int, [vp, ctypes.c_int, i32, i32, i32, i32, i32, i32, vp, vp,
                                         vp, ctypes.c_int, vp]),
@@ -278,6 +283,30 @@ def bcq_lowrank_correct(u_signs, v_signs, alpha, x, y, z=None, stream=None) -> N
            load().bcq_lowrank_correct(_ptr(u_signs), _ptr(v_signs), _ptr(alpha), R, M, K,
                                       _ptr(x), _ptr(y), _dtype_code(y), _ptr(z),
                                       _stream(stream)))
+
+
+def bcq_gemv_lowrank(store: "Store", p: int, x, u_signs, v_signs, lr_alpha, y, z=None,
+                     stream=None) -> None:
+    """``y[M] = product at precision p of x + sum_r lr_alpha[r] * u[:, r] * (v[r] . x)``
+    (see ``include/bcq.h``): the product of :func:`bcq_gemv` with the correction
+    of :func:`bcq_lowrank_correct`, written once.  ``z`` is an R-float device
+    workspace (allocated through torch when None)."""
+    import torch
+
+    R, M, K = lr_alpha.numel(), store.M, store.K
+    if z is None:
+        z = torch.empty(R, dtype=torch.float32, device=y.device)
+    _need_vec("x", x, K)
+    _need_vec("y", y, M)
+    _need_vec("u_signs", u_signs, M * ((R + 31) // 32))
+    _need_vec("v_signs", v_signs, R * (K // 32))
+    _need_vec("lr_alpha", lr_alpha, R)
+    _need_vec("z", z, R)
+    _check_store_tensors(store, [p])
+    _check("bcq_gemv_lowrank",
+           load().bcq_gemv_lowrank(store.ref(), p, _ptr(x), _dtype_code(x), _ptr(u_signs),
+                                   _ptr(v_signs), _ptr(lr_alpha), R, _ptr(y), _dtype_code(y),
+                                   _ptr(z), _stream(stream)))
 
 
 def bcq_dequantize(store: "Store", p: int, W, stream=None) -> None:

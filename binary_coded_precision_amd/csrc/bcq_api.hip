@@ -324,6 +324,36 @@ bcq_status bcq_lowrank_correct(const uint32_t *u_signs, const uint32_t *v_signs,
   return hip_status(bcq::launch_lowrank(u_signs, v_signs, alpha, R, M, K, x, y, dtype, z, stream));
 }
 
+bcq_status bcq_gemv_lowrank(const bcq_store *store, int32_t p, const void *x, bcq_dtype x_dtype,
+                            const uint32_t *u_signs, const uint32_t *v_signs,
+                            const void *lr_alpha, int32_t R, void *y, bcq_dtype y_dtype, float *z,
+                            hipStream_t stream) {
+  BCQ_TRY(check_store(store));
+  BCQ_TRY(check_precision(store, p));
+  BCQ_TRY(check_dtypes(store, x_dtype, y_dtype));
+  if (R < 1 || R > BCQ_LOWRANK_MAX_RANK) return BCQ_ERR_INVALID_ARG;
+  if (x == nullptr || y == nullptr || u_signs == nullptr || v_signs == nullptr ||
+      lr_alpha == nullptr || z == nullptr)
+    return BCQ_ERR_INVALID_ARG;
+  const bcq_dtype dt = store->scale_dtype;
+  if (!aligned(x, 16) || !aligned(y, dtype_size(y_dtype)) || !aligned(u_signs, 4) ||
+      !aligned(v_signs, 4) || !aligned(z, 4) || !aligned(lr_alpha, dtype_size(dt)))
+    return BCQ_ERR_ALIGNMENT;
+  const bool fused = bcq::gemv_lowrank_fused_ok(store->K, R);
+  log_route("bcq_gemv_lowrank", store, 1,
+            fused ? "batch-1 tables, correction in the writeback" : "batch-1 tables, then correction");
+  if (bcq::launch_lowrank_z(v_signs, lr_alpha, R, store->K, x, z, dt, stream) != hipSuccess)
+    return BCQ_ERR_HIP;
+  if (fused)
+    return hip_status(bcq::launch_gemv_lowrank(store->bits, store->M, store->K, p,
+                                               store->alpha[p], store->zero[p], x, y, u_signs, z,
+                                               R, dt, stream));
+  if (bcq::launch_gemv_lut(store->bits, store->M, store->K, p, store->alpha[p], store->zero[p], x,
+                           y, dt, stream) != hipSuccess)
+    return BCQ_ERR_HIP;
+  return hip_status(bcq::launch_lowrank_expand(u_signs, R, store->M, z, y, dt, stream));
+}
+
 size_t bcq_workspace_bytes(const bcq_store *store, int32_t b) {
   if (check_store(store) != BCQ_OK || b < 1 || b > BCQ_MAX_BATCH) return 0;
   if (!on_matrix_cores(store, b)) return 0;

@@ -62,6 +62,18 @@ hipError_t launch_dequant(const uint32_t *bits, int M, int K, int p, const void 
 constexpr int kLrMaxRank = BCQ_LOWRANK_MAX_RANK;
 hipError_t launch_lowrank(const uint32_t *u, const uint32_t *v, const void *alpha, int R, int M,
                           int K, const void *x, void *y, bcq_dtype dt, float *z, hipStream_t s);
+// Its two steps: z_r = alpha_r (v_r . x) into z (fp32), then y += U z.
+hipError_t launch_lowrank_z(const uint32_t *v, const void *alpha, int R, int K, const void *x,
+                            float *z, bcq_dtype dt, hipStream_t s);
+hipError_t launch_lowrank_expand(const uint32_t *u, int R, int M, const float *z, void *y,
+                                 bcq_dtype dt, hipStream_t s);
+// Batch-1 product with the correction U z (z from launch_lowrank_z) added
+// before the output is rounded, one launch; only where
+// gemv_lowrank_fused_ok(K, R) (K <= 4096, R <= 1024).
+bool gemv_lowrank_fused_ok(int K, int R);
+hipError_t launch_gemv_lowrank(const uint32_t *bits, int M, int K, int p, const void *alpha,
+                               const void *zero, const void *x, void *y, const uint32_t *u,
+                               const float *z, int R, bcq_dtype dt, hipStream_t s);
 
 // Progressive-precision quantizer (bcq_quantize): W [M][ldw] of w_dt (fp16 or
 // fp32) -> canonical signs [P][M][K/32] and the scale / offset tables of

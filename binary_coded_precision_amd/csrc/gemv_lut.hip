@@ -235,6 +235,18 @@ constexpr int kRHalfPad = 64;                        // bytes between the two ha
 constexpr int kRGroupStride = kChunksPerGroup * kG1ChunkStride + kRHalfPad + 64;  // 2688
 constexpr int kRWindowBytes = kG1Ksub * kRGroupStride;                           // 43008
 
+// Binary low-rank correction fused into the writeback (bcq_gemv_lowrank, the
+// BiLoCo summary's inference step): z_r = alpha_r (v_r . x) comes from a launch
+// before the product; the product kernel turns z into 16-entry tables of sign
+// combinations over 4 consecutive ranks (the primitive of the activation
+// tables) and lane (r, slot ls) adds the 8 lookups of its row's u word ls to
+// its partial, so the correction rides the product's own reduction and the
+// output is rounded once.  Up to kLrMaxWords u words (1024 ranks) per row: one
+// word per (row, slot) lane.  The 8 tables of word w sit at float w * 144, so
+// the four words a wavefront reads start in different quarters of the banks.
+constexpr int kLrMaxWords = 32;
+constexpr int kLrWordStride = 8 * kEntries + 16;  // floats: 8 tables + 64 B pad
+
 __device__ __forceinline__ int r_chunk_offset(int c) {  // chunk c (0..31) within its group
   return c * kG1ChunkStride + (c >= 16 ? kRHalfPad : 0);
 }
@@ -286,10 +298,11 @@ __device__ __forceinline__ float r_half_sum(const uint2 bw, uint32_t base) {
 // 8w..8w+7 look up window w.  At K = 4096 that is four wavefronts per SIMD,
 // enough to hide the LDS latency of the lookups, and every lane builds one
 // chunk's table.
-template <typename T, int NW, int P, int TMAX, int RS = 1, bool GU = false>
+template <typename T, int NW, int P, int TMAX, int RS = 1, bool GU = false, bool LR = false>
 __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
     const uint4 *__restrict__ bits, const T *__restrict__ alpha, const T *__restrict__ zero,
-    const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT) {
+    const T *__restrict__ x, T *__restrict__ y, int M, int G, int MT,
+    const uint32_t *__restrict__ lr_u, const float *__restrict__ lr_z, int R) {
   constexpr int kMaxG = NW * kG1Ksub;
   constexpr int kWaves = kRWaves * NW;
   constexpr int kPos = kTileRows * kMaxG;        // staging positions of one tile
@@ -304,6 +317,10 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   // odd number of words so the 16 rows x 2 groups one wavefront reads hit
   // distinct banks
   __shared__ uint32_t scl[TMAX][P + 1][kTileRows][kMaxG + 1];
+  // low-rank correction tables (LR): u word w of a row at float w * kLrWordStride
+  __shared__ __attribute__((aligned(16))) float lrt[LR ? kLrMaxWords * kLrWordStride : 1];
+  static_assert(!LR || !GU, "the correction applies to plain products");
+  static_assert(kLrMaxWords <= kRWaves * 4, "one u word per (row, slot) lane");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -358,6 +375,26 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
                         M - 1);
     const T *src = a < P ? alpha + a * MG : zero;
     sv[u] = load_raw(src + (size_t)row * G + sgc);
+  }
+
+  // ---- low-rank correction (LR): lane (r, slot ls) takes u word ls of its
+  // row in every tile, and thread tid < 8 * nwu builds the table of ranks
+  // 4 tid .. 4 tid + 3 from z (written by the launch before this one).
+  const int nwu = LR ? (R + 31) / 32 : 0;
+  const int ls = wave * 4 + (lane >> 4);
+  uint32_t uw[TMAX];
+  float zf[4];
+  if constexpr (LR) {
+    const int wl = min(ls, nwu - 1);
+#pragma unroll
+    for (int k = 0; k < TMAX; ++k) {
+      const int t = RS > 1 ? (int)blockIdx.x / RS
+                           : (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x;
+      const int m = min(t * kTileRows + (RS > 1 ? prow : r), M - 1);
+      uw[k] = lr_u[(size_t)m * nwu + wl];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) zf[q] = 4 * tid + q < R ? lr_z[4 * tid + q] : 0.f;
   }
 
   // ---- sign words of this lane's half group, one uint2 per plane.  Past my
@@ -418,6 +455,18 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
     const int n = u * kParts + spart;
     if (n < kPairs) scl[n / (P + 1)][n % (P + 1)][srow][sg] = sv[u];
   }
+  if constexpr (LR) {
+    if (tid < 8 * nwu) {
+      float4 v[4];
+      chunk_entries(zf, v);
+      float4 *dst =
+          reinterpret_cast<float4 *>(lrt + (tid >> 3) * kLrWordStride + (tid & 7) * kEntries);
+      dst[0] = v[0];
+      dst[1] = v[1];
+      dst[2] = v[2];
+      dst[3] = v[3];
+    }
+  }
   __syncthreads();
   if (TMAX > 1) fetch(1, tiles[1]);
 
@@ -452,6 +501,21 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
     acc[k] = 0.f;
     if (k < nt) acc[k] = consume(k, tiles[k % 2]);
     if (k + 2 < TMAX) fetch(k + 2, tiles[k % 2]);  // refill the slot just read
+  }
+
+  // ---- low-rank correction: sum_r u_mr z_r of this lane's 32 ranks (8
+  // table reads) joins the row's slot partials; one lane per (row, slot)
+  if constexpr (LR) {
+    if (ls < nwu && (RS == 1 || ph == 0)) {
+      const float *zt = lrt + ls * kLrWordStride;
+#pragma unroll
+      for (int k = 0; k < TMAX; ++k) {
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s += zt[q * kEntries + ((uw[k] >> (4 * q)) & 15u)];
+        acc[k] += s;
+      }
+    }
   }
 
   // ---- reduce the slot partials of each row of each tile, fixed order
@@ -844,25 +908,26 @@ int compute_units() {
   return n;
 }
 
-template <typename T, int NW, int TMAX, int RS = 1, bool GU = false>
+template <typename T, int NW, int TMAX, int RS = 1, bool GU = false, bool LR = false>
 void gemv_res_launch(dim3 grid, hipStream_t s, const uint4 *b4, const T *a, const T *z,
-                     const T *xx, T *yy, int M, int G, int MT, int p) {
+                     const T *xx, T *yy, int M, int G, int MT, int p, const uint32_t *lu,
+                     const float *lz, int R) {
   switch (p) {
     case 1:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 1, TMAX, RS, GU>), grid, dim3(kRThreads * NW), 0, s,
-                         b4, a, z, xx, yy, M, G, MT);
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 1, TMAX, RS, GU, LR>), grid, dim3(kRThreads * NW),
+                         0, s, b4, a, z, xx, yy, M, G, MT, lu, lz, R);
       break;
     case 2:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 2, TMAX, RS, GU>), grid, dim3(kRThreads * NW), 0, s,
-                         b4, a, z, xx, yy, M, G, MT);
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 2, TMAX, RS, GU, LR>), grid, dim3(kRThreads * NW),
+                         0, s, b4, a, z, xx, yy, M, G, MT, lu, lz, R);
       break;
     case 3:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 3, TMAX, RS, GU>), grid, dim3(kRThreads * NW), 0, s,
-                         b4, a, z, xx, yy, M, G, MT);
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 3, TMAX, RS, GU, LR>), grid, dim3(kRThreads * NW),
+                         0, s, b4, a, z, xx, yy, M, G, MT, lu, lz, R);
       break;
     default:
-      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 4, TMAX, RS, GU>), grid, dim3(kRThreads * NW), 0, s,
-                         b4, a, z, xx, yy, M, G, MT);
+      hipLaunchKernelGGL((gemv_res_kernel<T, NW, 4, TMAX, RS, GU, LR>), grid, dim3(kRThreads * NW),
+                         0, s, b4, a, z, xx, yy, M, G, MT, lu, lz, R);
       break;
   }
 }
@@ -871,22 +936,45 @@ void gemv_res_launch(dim3 grid, hipStream_t s, const uint4 *b4, const T *a, cons
 // units or fewer holding a tile, each tile's rows are split over 4 (2)
 // workgroups.  More tiles than compute units: tiles dealt round-robin, up to 4
 // per workgroup.
-template <typename T, int NW, bool GU>
+template <typename T, int NW, bool GU, bool LR = false>
 void gemv_res_tiles(hipStream_t s, const uint4 *b4, const T *a, const T *z, const T *xx, T *yy,
-                    int M, int G, int MT, int p) {
+                    int M, int G, int MT, int p, const uint32_t *lu = nullptr,
+                    const float *lz = nullptr, int R = 0) {
   const int cus = compute_units();
   const int tmax = (MT + cus - 1) / cus;
   if (!GU && 4 * MT <= cus)
-    gemv_res_launch<T, NW, 1, 4>(dim3(MT * 4), s, b4, a, z, xx, yy, M, G, MT, p);
+    gemv_res_launch<T, NW, 1, 4, false, LR>(dim3(MT * 4), s, b4, a, z, xx, yy, M, G, MT, p, lu,
+                                            lz, R);
   else if (!GU && 2 * MT <= cus)
-    gemv_res_launch<T, NW, 1, 2>(dim3(MT * 2), s, b4, a, z, xx, yy, M, G, MT, p);
+    gemv_res_launch<T, NW, 1, 2, false, LR>(dim3(MT * 2), s, b4, a, z, xx, yy, M, G, MT, p, lu,
+                                            lz, R);
   else if (tmax <= 1)
-    gemv_res_launch<T, NW, 1, 1, GU>(dim3(MT), s, b4, a, z, xx, yy, M, G, MT, p);
+    gemv_res_launch<T, NW, 1, 1, GU, LR>(dim3(MT), s, b4, a, z, xx, yy, M, G, MT, p, lu, lz, R);
   else if (tmax <= 2)
-    gemv_res_launch<T, NW, 2, 1, GU>(dim3((MT + 1) / 2), s, b4, a, z, xx, yy, M, G, MT, p);
+    gemv_res_launch<T, NW, 2, 1, GU, LR>(dim3((MT + 1) / 2), s, b4, a, z, xx, yy, M, G, MT, p, lu,
+                                         lz, R);
   else
-    gemv_res_launch<T, NW, 4, 1, GU>(dim3((MT + 3) / 4 > cus ? (MT + 3) / 4 : cus), s, b4, a, z,
-                                     xx, yy, M, G, MT, p);
+    gemv_res_launch<T, NW, 4, 1, GU, LR>(dim3((MT + 3) / 4 > cus ? (MT + 3) / 4 : cus), s, b4, a,
+                                         z, xx, yy, M, G, MT, p, lu, lz, R);
+}
+
+// Product plus fused low-rank correction, resident tables only (K <= 4096).
+template <typename T>
+hipError_t gemv_lowrank_dispatch(const uint32_t *bits, int M, int K, int p, const void *alpha,
+                                 const void *zero, const void *x, void *y, const uint32_t *u,
+                                 const float *z, int R, hipStream_t s) {
+  const int G = K / kGroup;
+  const int MT = row_tiles(M);
+  const uint4 *b4 = reinterpret_cast<const uint4 *>(bits);
+  const T *a = static_cast<const T *>(alpha);
+  const T *zz = static_cast<const T *>(zero);
+  const T *xx = static_cast<const T *>(x);
+  T *yy = static_cast<T *>(y);
+  if (G <= kG1Ksub)
+    gemv_res_tiles<T, 1, false, true>(s, b4, a, zz, xx, yy, M, G, MT, p, u, z, R);
+  else
+    gemv_res_tiles<T, 2, false, true>(s, b4, a, zz, xx, yy, M, G, MT, p, u, z, R);
+  return hipGetLastError();
 }
 
 template <typename T, bool GU>
@@ -1340,6 +1428,19 @@ hipError_t launch_gemv_lut(const uint32_t *bits, int M, int K, int p, const void
                            hipStream_t s) {
   if (dt == BCQ_F16) return gemv_dispatch<half_t, false>(bits, M, K, p, alpha, zero, x, y, s);
   return gemv_dispatch<float, false>(bits, M, K, p, alpha, zero, x, y, s);
+}
+
+bool gemv_lowrank_fused_ok(int K, int R) {
+  return K <= 2 * kG1Ksub * kGroup && R >= 1 && R <= 32 * kLrMaxWords;
+}
+
+hipError_t launch_gemv_lowrank(const uint32_t *bits, int M, int K, int p, const void *alpha,
+                               const void *zero, const void *x, void *y, const uint32_t *u,
+                               const float *z, int R, bcq_dtype dt, hipStream_t s) {
+  if (!gemv_lowrank_fused_ok(K, R)) return hipErrorInvalidValue;
+  if (dt == BCQ_F16)
+    return gemv_lowrank_dispatch<half_t>(bits, M, K, p, alpha, zero, x, y, u, z, R, s);
+  return gemv_lowrank_dispatch<float>(bits, M, K, p, alpha, zero, x, y, u, z, R, s);
 }
 
 hipError_t launch_gemv_gate_up(const uint32_t *bits, int M, int K, int p, const void *alpha,

@@ -119,25 +119,41 @@ __global__ __launch_bounds__(kLrExpandThreads) void lowrank_expand_kernel(
 }
 
 template <typename T>
-hipError_t lowrank_launch(const uint32_t *u, const uint32_t *v, const void *alpha, int R, int M,
-                          int K, const void *x, void *y, float *z, hipStream_t s) {
+hipError_t lowrank_z_launch(const uint32_t *v, const void *alpha, int R, int K, const void *x,
+                            float *z, hipStream_t s) {
   hipLaunchKernelGGL(lowrank_z_kernel<T>, dim3(R), dim3(kLrThreads), 0, s, v, K,
                      static_cast<const T *>(x), static_cast<const T *>(alpha), z);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t lowrank_expand_launch(const uint32_t *u, int R, int M, const float *z, void *y,
+                                 hipStream_t s) {
   const size_t lds = (size_t)((R + 3) / 4) * 16 * sizeof(float);  // <= 64 KB
   hipLaunchKernelGGL(lowrank_expand_kernel<T>, dim3((M + kLrRowsPerBlock - 1) / kLrRowsPerBlock),
-                     dim3(kLrExpandThreads), lds, s, u, R, M, static_cast<const float *>(z),
-                     static_cast<T *>(y));
+                     dim3(kLrExpandThreads), lds, s, u, R, M, z, static_cast<T *>(y));
   return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_lowrank_z(const uint32_t *v, const void *alpha, int R, int K, const void *x,
+                            float *z, bcq_dtype dt, hipStream_t s) {
+  if (dt == BCQ_F16) return lowrank_z_launch<_Float16>(v, alpha, R, K, x, z, s);
+  return lowrank_z_launch<float>(v, alpha, R, K, x, z, s);
+}
+
+hipError_t launch_lowrank_expand(const uint32_t *u, int R, int M, const float *z, void *y,
+                                 bcq_dtype dt, hipStream_t s) {
+  if (dt == BCQ_F16) return lowrank_expand_launch<_Float16>(u, R, M, z, y, s);
+  return lowrank_expand_launch<float>(u, R, M, z, y, s);
+}
+
 hipError_t launch_lowrank(const uint32_t *u, const uint32_t *v, const void *alpha, int R, int M,
                           int K, const void *x, void *y, bcq_dtype dt, float *z, hipStream_t s) {
-  if (dt == BCQ_F16) return lowrank_launch<_Float16>(u, v, alpha, R, M, K, x, y, z, s);
-  return lowrank_launch<float>(u, v, alpha, R, M, K, x, y, z, s);
+  hipError_t e = launch_lowrank_z(v, alpha, R, K, x, z, dt, s);
+  if (e != hipSuccess) return e;
+  return launch_lowrank_expand(u, R, M, z, y, dt, s);
 }
 
 }  // namespace bcq

@@ -51,8 +51,11 @@ extern "C" {
 #define BCQ_TILE_ROWS 16
 /* Largest batch accepted by bcq_gemm_skinny / bcq_gemv_mixed_p in one call. */
 #define BCQ_MAX_BATCH 256
-/* Largest rank accepted by bcq_lowrank_correct. */
+/* Largest rank accepted by bcq_lowrank_correct and bcq_gemv_lowrank. */
 #define BCQ_LOWRANK_MAX_RANK 4096
+/* bcq_gemv_lowrank adds the correction inside the product's own launch (one
+ * rounding of y) for K <= 4096 and R up to this rank. */
+#define BCQ_LOWRANK_FUSED_MAX_RANK 1024
 /* Device scratch held by the library for bcq_gemm_skinny_noalloc, per GPU. */
 #define BCQ_NOALLOC_SCRATCH_BYTES (16u << 20)
 
@@ -323,6 +326,31 @@ bcq_status bcq_dequantize(const bcq_store *store, int32_t p, void *W, int32_t ld
 bcq_status bcq_lowrank_correct(const uint32_t *u_signs, const uint32_t *v_signs,
                                const void *alpha, int32_t R, int32_t M, int32_t K, const void *x,
                                void *y, bcq_dtype dtype, float *z, hipStream_t stream);
+
+/*
+ * Batch-1 product with a binary low-rank correction, written (not added):
+ *     y[m] = (W_hat_p x)[m] + sum_{r<R} lr_alpha[r] * u[m][r] * (v[r] . x)
+ * with W_hat_p the store's reconstruction at precision p (as bcq_gemv) and
+ * u, v, lr_alpha the terms of bcq_lowrank_correct.  Defined by: AnyBCQ paper
+ * notes, "Method / key designs" (the product) and the BiLoCo summary, "core
+ * idea" and its fused-operator section (the correction, computed as
+ * z = lr_alpha * (V x) first and expanded by u into the product's output
+ * before it is written back).
+ * Two launches on `stream`: z_r = lr_alpha[r] (v_r . x) into z, then the
+ * product.  When K <= 4096 and R <= BCQ_LOWRANK_FUSED_MAX_RANK the product's
+ * kernel adds sum_r u[m][r] z_r to its fp32 row sums and rounds y once;
+ * otherwise the product is written and a third launch adds the correction to
+ * it (y rounded twice).
+ * store, p, x, x_dtype, y, y_dtype: as in bcq_gemv.
+ * u_signs [M][ceil(R/32)], v_signs [R][K/32], z (R floats, clobbered): as in
+ * bcq_lowrank_correct; lr_alpha [R] in the store's scale dtype, element
+ * aligned.  1 <= R <= BCQ_LOWRANK_MAX_RANK.  Validation and stream behaviour
+ * as in bcq_gemv: a rejected call enqueues nothing.
+ */
+bcq_status bcq_gemv_lowrank(const bcq_store *store, int32_t p, const void *x, bcq_dtype x_dtype,
+                            const uint32_t *u_signs, const uint32_t *v_signs,
+                            const void *lr_alpha, int32_t R, void *y, bcq_dtype y_dtype, float *z,
+                            hipStream_t stream);
 
 /*
  * Offline quantizer: a weight matrix W [M][K] becomes P shared sign planes and

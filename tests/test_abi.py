@@ -83,6 +83,12 @@ def lowrank(u=FAKE, v=FAKE, a=FAKE, R=16, M=64, K=256, x=FAKE, y=FAKE, dt=bcq.BC
     return bcq.load().bcq_lowrank_correct(u, v, a, R, M, K, x, y, dt, z, None)
 
 
+def gemv_lr(st, p=2, x=FAKE, u=FAKE, v=FAKE, a=FAKE, R=16, y=FAKE, z=FAKE, xdt=bcq.BCQ_F16,
+            ydt=bcq.BCQ_F16):
+    ref = None if st is None else ctypes.byref(st)
+    return bcq.load().bcq_gemv_lowrank(ref, p, x, xdt, u, v, a, R, y, ydt, z, None)
+
+
 def skinny(st, p=2, X=FAKE, b=4, ldx=None, Y=FAKE, ldy=None, dt=bcq.BCQ_F16, ws=None, wsb=0):
     ldx = st.K if ldx is None else ldx
     ldy = st.M if ldy is None else ldy
@@ -147,6 +153,25 @@ E_ARG, E_UNS, E_ALN = bcq.BCQ_ERR_INVALID_ARG, bcq.BCQ_ERR_UNSUPPORTED, bcq.BCQ_
     (lambda: lowrank(z=FAKE + 2), E_ALN),
     (lambda: lowrank(y=FAKE + 1), E_ALN),
     (lambda: lowrank(x=FAKE + 8), E_ALN),
+    (lambda: gemv_lr(None), E_ARG),
+    (lambda: gemv_lr(make_store(), p=5), E_ARG),
+    (lambda: gemv_lr(make_store(K=192)), E_ARG),
+    (lambda: gemv_lr(make_store(), R=0), E_ARG),
+    (lambda: gemv_lr(make_store(), R=4097), E_ARG),
+    (lambda: gemv_lr(make_store(), u=0), E_ARG),
+    (lambda: gemv_lr(make_store(), v=0), E_ARG),
+    (lambda: gemv_lr(make_store(), a=0), E_ARG),
+    (lambda: gemv_lr(make_store(), z=0), E_ARG),
+    (lambda: gemv_lr(make_store(), y=0), E_ARG),
+    (lambda: gemv_lr(make_store(), xdt=bcq.BCQ_F32), E_UNS),
+    (lambda: gemv_lr(make_store(), x=FAKE + 8), E_ALN),
+    (lambda: gemv_lr(make_store(), y=FAKE + 1), E_ALN),
+    (lambda: gemv_lr(make_store(), u=FAKE + 2), E_ALN),
+    (lambda: gemv_lr(make_store(), v=FAKE + 2), E_ALN),
+    (lambda: gemv_lr(make_store(), z=FAKE + 2), E_ALN),
+    (lambda: gemv_lr(make_store(), a=FAKE + 1), E_ALN),
+    (lambda: gemv_lr(make_store(dtype=bcq.BCQ_F32), a=FAKE + 2, xdt=bcq.BCQ_F32,
+                     ydt=bcq.BCQ_F32), E_ALN),
     (lambda: skinny(make_store(), b=0), E_ARG),
     (lambda: skinny(make_store(), b=257), E_ARG),
     (lambda: skinny(make_store(), ldx=255), E_ARG),

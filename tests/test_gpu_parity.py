@@ -950,6 +950,106 @@ def test_lowrank_correction(M, K, R, dt):
     assert rel_l2(y.cpu().numpy(), ref) <= TOL[np.dtype(dt)]
 
 
+LOWRANK_CASES = [
+    # the correction in the product's writeback: one tile per workgroup (two
+    # windows), four and two tiles per workgroup, row halves at the largest
+    # fused rank, row quarters with a ragged tile and a rank not a multiple of
+    # 4, one window with a rank not a multiple of 32, the smallest case
+    (4096, 4096, 4, 3, 128, np.float16), (4096, 4096, 4, 4, 512, np.float16),
+    (14336, 4096, 4, 4, 256, np.float16), (8192, 4096, 3, 2, 64, np.float16),
+    (2000, 4096, 2, 2, 1024, np.float16), (37, 384, 3, 3, 5, np.float32),
+    (1000, 2048, 4, 4, 37, np.float16), (1, 128, 1, 1, 1, np.float32),
+    # past the fused limits (rank above 1024, K above 4096): product, then the
+    # correction added by its own launch
+    (4096, 4096, 3, 3, 1025, np.float16), (300, 8320, 3, 3, 64, np.float32),
+    (1024, 14336, 4, 4, 4096, np.float16),
+]
+
+
+def lowrank_case(M, K, P, p, R, dt):
+    w = bcq_synth.make(M, K, P, dtype=dt, seed=M + 3 * K + R)
+    lr = bcq_synth.lowrank(M, K, R, dtype=dt, seed=M + K + 5 * R)
+    base = oracle_y_all(w, w.x[:1], [p])[0]
+    ref = oracle.lowrank_correct(lr.u, lr.v, lr.alpha, w.x[0], base)
+    return w, lr, base, ref
+
+
+def lowrank_ok(y, base, ref, dt):
+    got = y.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert rel_l2(got, ref) <= TOL[np.dtype(dt)]
+    # the correction is a real part of the result at these scales
+    assert rel_l2(base, ref) > 50 * TOL[np.dtype(dt)]
+
+
+@pytest.mark.parametrize("M,K,P,p,R,dt", LOWRANK_CASES)
+def test_gemv_with_lowrank_correction(M, K, P, p, R, dt):
+    """bcq_gemv_lowrank: the product at precision p plus the binary low-rank
+    correction, every output against the float64 oracle (oracle.gemv's
+    product, then oracle.lowrank_correct on it)."""
+    w, lr, base, ref = lowrank_case(M, K, P, p, R, dt)
+    say("gemv_lowrank", M, K, P, p, R, np.dtype(dt).name)
+    st = store_of(w)
+    tdt = torch.float16 if dt == np.float16 else torch.float32
+    y = torch.full((M,), float("nan"), dtype=tdt, device="cuda")
+    bcq.bcq_gemv_lowrank(st, p, dev(w.x[0]), dev(lr.u.view(np.int32)), dev(lr.v.view(np.int32)),
+                         dev(lr.alpha), y)
+    lowrank_ok(y, base, ref, dt)
+
+
+def test_gemv_lowrank_workspace_reused_across_calls_and_ranks():
+    """One z workspace through calls in a row at different precisions, ranks
+    and inputs: each call must use only its own z."""
+    M, K, P = 4096, 4096, 4
+    z = torch.full((1024,), float("nan"), dtype=torch.float32, device="cuda")
+    cases = [(3, 128, 11), (4, 1024, 12), (2, 16, 13), (3, 128, 14), (4, 512, 15)]
+    w = bcq_synth.make(M, K, P, b=len(cases), seed=77)
+    st = store_of(w)
+    for i, (p, R, seed) in enumerate(cases):
+        lr = bcq_synth.lowrank(M, K, R, seed=seed)
+        say("gemv_lowrank reuse", p, R)
+        y = torch.full((M,), float("nan"), dtype=torch.float16, device="cuda")
+        bcq.bcq_gemv_lowrank(st, p, dev(w.x[i]), dev(lr.u.view(np.int32)),
+                             dev(lr.v.view(np.int32)), dev(lr.alpha), y, z)
+        base = oracle_y_all(w, w.x[i:i + 1], [p])[0]
+        ref = oracle.lowrank_correct(lr.u, lr.v, lr.alpha, w.x[i], base)
+        assert rel_l2(y.cpu().numpy(), ref) <= 2e-3, (p, R)
+
+
+def test_gemv_lowrank_graph_replays():
+    """bcq_gemv_lowrank captured once in a HIP graph and replayed with new
+    activations copied in between (eager work between replays): every replay
+    against the oracle."""
+    M, K, P, p, R = 4096, 4096, 4, 3, 128
+    w = bcq_synth.make(M, K, P, b=3, seed=78)
+    lr = bcq_synth.lowrank(M, K, R, seed=79)
+    st = store_of(w)
+    u, v, a = dev(lr.u.view(np.int32)), dev(lr.v.view(np.int32)), dev(lr.alpha)
+    x = dev(w.x[0])
+    y = torch.empty(M, dtype=torch.float16, device="cuda")
+    z = torch.empty(R, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bcq.bcq_gemv_lowrank(st, p, x, u, v, a, y, z)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bcq.bcq_gemv_lowrank(st, p, x, u, v, a, y, z)
+    torch.cuda.synchronize()
+    for i in (1, 2, 0, 1):
+        say("gemv_lowrank graph replay", i)
+        x.copy_(dev(w.x[i]))
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        base = oracle_y_all(w, w.x[i:i + 1], [p])[0]
+        ref = oracle.lowrank_correct(lr.u, lr.v, lr.alpha, w.x[i], base)
+        assert rel_l2(y.cpu().numpy(), ref) <= 2e-3, i
+
+
 # ---------------------------------------------------------------- dense reconstruction export
 
 @pytest.mark.parametrize("M,K,P,dt,pad", [
