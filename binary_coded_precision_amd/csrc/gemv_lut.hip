@@ -31,6 +31,8 @@
 //    sums per entry, see the section below.
 //  * Every reduction over lanes and wavefronts runs in a fixed order, so
 //    results are deterministic.
+#include <stdlib.h>
+
 #include <atomic>
 
 #include "bcq_internal.h"
@@ -890,6 +892,217 @@ __global__ __launch_bounds__(2 * kRThreads) void gemv_stream2_kernel(
   }
 }
 
+// ------------------------------------------------ batch 1, fp16 tables for K up to 14336
+//
+// For fp16 stores with 4096 < K <= 14336 the tables of all of K fit in LDS
+// when each entry is held in fp16 (32 bytes per chunk; 126 KB of tables at
+// K = 14336), so one workgroup per 16-row tile builds them once, behind one
+// barrier, instead of streaming windows through two buffers with a barrier
+// each.  An entry is the fp32 sum of its four signed activations rounded
+// once to fp16 (relative error at most 2^-11 of the entry); lookups are
+// summed in fp32.
+//
+// 1024 lanes: lane (r, s) takes row r of the tile and half-group slots
+// s, s + 64, s + 128, ... (s = wave * 4 + lane / 16); every thread builds
+// chunks tid, tid + 1024, ... of K.  In LDS a group's 32 tables take 1152
+// bytes (the second half of the group 64 bytes after the first), so the four
+// slots of a wavefront, two groups x two halves, start in different quarters
+// of the banks and each reads its own eight.
+constexpr int kHThreads = 1024;
+constexpr int kHWaves = kHThreads / 64;
+constexpr int kHMaxG = 112;  // groups resident: K <= 14336
+constexpr int kHChunkBytes = 2 * kEntries;
+constexpr int kHHalfPad = 64;
+constexpr int kHGroupStride = kChunksPerGroup * kHChunkBytes + kHHalfPad + 64;  // 1152
+constexpr int kHMaxChunkRounds = (kHMaxG * kChunksPerGroup + kHThreads - 1) / kHThreads;  // 4
+constexpr int kHScaleWords = kHMaxG / 2 + 1;  // staged scale row, 32-bit words (odd)
+
+__device__ __forceinline__ int h_chunk_offset(int c) {
+  return c * kHChunkBytes + (c >= 16 ? kHHalfPad : 0);
+}
+
+typedef __attribute__((address_space(3))) const _Float16 lds_half;
+template <int B>
+__device__ __forceinline__ _Float16 lds_h(uint32_t base, uint32_t v, int off) {
+  return ((lds_half *)(size_t)add_byte<B>(base, v))[off];
+}
+
+// Sum over the 16 chunks of one half group of T_c[nibble] with fp16 tables:
+// byte b of ev (od) is twice nibble 2b (2b + 1) of a packed word, the entry's
+// byte offset in its chunk's table.  Each entry joins an fp32 sum through a
+// mixed-precision multiply-add (fp16 entry times 1, v_fma_mix_f32), so a
+// lookup costs one address add and one add, as with fp32 tables.
+__device__ __forceinline__ float h_half_sum(const uint2 bw, uint32_t base) {
+  constexpr int S = kHChunkBytes / 2;  // chunk stride in halves
+  // 1.0 through an empty asm, so that entry * 1 + sum is not folded into a
+  // conversion and an add
+  float one = 1.f;
+  asm("" : "+s"(one));
+  const uint32_t wd[2] = {bw.x, bw.y};
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t ev = (wd[q] << 1) & 0x1E1E1E1Eu;
+    const uint32_t od = (wd[q] >> 3) & 0x1E1E1E1Eu;
+    const int c = q * 8;
+    s[0] = fmaf((float)lds_h<0>(base, ev, (c + 0) * S), one, s[0]);
+    s[1] = fmaf((float)lds_h<0>(base, od, (c + 1) * S), one, s[1]);
+    s[2] = fmaf((float)lds_h<1>(base, ev, (c + 2) * S), one, s[2]);
+    s[3] = fmaf((float)lds_h<1>(base, od, (c + 3) * S), one, s[3]);
+    s[0] = fmaf((float)lds_h<2>(base, ev, (c + 4) * S), one, s[0]);
+    s[1] = fmaf((float)lds_h<2>(base, od, (c + 5) * S), one, s[1]);
+    s[2] = fmaf((float)lds_h<3>(base, ev, (c + 6) * S), one, s[2]);
+    s[3] = fmaf((float)lds_h<3>(base, od, (c + 7) * S), one, s[3]);
+  }
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
+template <int P, bool GU = false>
+__global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
+    const uint4 *__restrict__ bits, const half_t *__restrict__ alpha,
+    const half_t *__restrict__ zero, const half_t *__restrict__ x, half_t *__restrict__ y, int M,
+    int G, int MT) {
+  __shared__ __attribute__((aligned(16))) char lut[kHMaxG * kHGroupStride];
+  __shared__ float gsum[kHMaxG];
+  __shared__ float part[kHWaves][kTileRows];
+  // staged scales and offsets as fp16 bits: [array][row][group], rows at an
+  // odd number of words so the 16 rows a wavefront reads hit distinct banks
+  __shared__ uint32_t scl[(P + 1) * kTileRows * kHScaleWords];
+  constexpr int kRounds = kHMaxChunkRounds;
+  // staging: 128 threads per (array, row) run of G <= 112 values, eight runs
+  // at a time
+  constexpr int kRuns = (P + 1) * kTileRows;
+  constexpr int kScalePerThread = (kRuns + kHThreads / 128 - 1) / (kHThreads / 128);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int s = wave * 4 + (lane >> 4);  // half-group slot 0..63
+  const int tile = blockIdx.x;
+  const int H = 2 * G;                   // half groups of K
+  const int NC = kChunksPerGroup * G;    // chunks of K
+  const size_t plane_stride = (size_t)MT * G * kTileRows;  // in uint4
+  const size_t MG = (size_t)M * G;
+  const uint2 *bits2 = reinterpret_cast<const uint2 *>(bits);
+
+  // ---- activations of the chunks this thread builds (a past-the-end chunk
+  // re-reads the last one and builds nothing)
+  typename Act<half_t>::raw xr[kRounds];
+#pragma unroll
+  for (int t = 0; t < kRounds; ++t) {
+    const int c = min(tid + kHThreads * t, NC - 1);
+    xr[t] = Act<half_t>::load(x + (unsigned)((c / kChunksPerGroup) * kGroup +
+                                             chunk_base(c % kChunksPerGroup)),
+                              0);
+  }
+
+  // ---- scales and offsets of the tile: thread tid stages group tid % 128 of
+  // runs tid / 128 + 8u (run = array * 16 + row; planes, then offsets), so
+  // consecutive threads read consecutive groups of a row (coalesced); a
+  // group or run past the end re-reads a valid value and stages nothing
+  const int sg = tid % 128;
+  const int sgc = min(sg, G - 1);
+  unsigned short sv[kScalePerThread];
+#pragma unroll
+  for (int u = 0; u < kScalePerThread; ++u) {
+    const int run = min(tid / 128 + 8 * u, kRuns - 1);
+    const int a = run / kTileRows;
+    const int row = min(tile * kTileRows + run % kTileRows, M - 1);
+    const half_t *src = (a < P ? alpha + (size_t)a * MG : zero) + (size_t)row * G + sgc;
+    sv[u] = *reinterpret_cast<const unsigned short *>(src);
+  }
+
+  // ---- sign words of this lane's half groups, one uint2 per plane (a slot
+  // past the last half group re-reads the last one and adds nothing)
+  constexpr int kSlotsMax = (2 * kHMaxG + 63) / 64;  // 4
+  uint2 w[kSlotsMax][P];
+#pragma unroll
+  for (int t = 0; t < kSlotsMax; ++t) {
+    const int h = min(s + 64 * t, H - 1);
+    const unsigned q = (unsigned)((((size_t)tile * G + (h >> 1)) * kTileRows + r) * 2 + (h & 1));
+#pragma unroll
+    for (int i = 0; i < P; ++i) w[t][i] = bits2[(size_t)i * plane_stride * 2 + q];
+  }
+
+  // ---- build the tables and group sums.  Every round computes its chunk
+  // (a past-the-end one its clamped copy) and only the stores are guarded:
+  // an activation load used only under the guard is sunk below the sign
+  // words by the compiler, and its wait then covers all of them.
+#pragma unroll
+  for (int t = 0; t < kRounds; ++t) {
+    const int c = tid + kHThreads * t;
+    const int cg = c % kChunksPerGroup;
+    float f[4];
+    Act<half_t>::cvt(xr[t], chunk_parity(cg), f);
+    float4 v[4];
+    chunk_entries(f, v);
+    uint32_t hv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hv[2 * e] = (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].x) |
+                  ((uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].y) << 16);
+      hv[2 * e + 1] = (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].z) |
+                      ((uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].w) << 16);
+    }
+    const float cs = sum32_lanes((f[0] + f[1]) + (f[2] + f[3]));
+    if (c < NC) {  // whole aligned 32-lane blocks (NC is a multiple of 32)
+      uint4 *dst = reinterpret_cast<uint4 *>(lut + (c / kChunksPerGroup) * kHGroupStride +
+                                             h_chunk_offset(cg));
+      dst[0] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+      dst[1] = make_uint4(hv[4], hv[5], hv[6], hv[7]);
+      if ((tid & 31) == 0) gsum[c / kChunksPerGroup] = cs;
+    }
+  }
+  unsigned short *scl16 = reinterpret_cast<unsigned short *>(scl);
+#pragma unroll
+  for (int u = 0; u < kScalePerThread; ++u) {
+    const int run = tid / 128 + 8 * u;
+    if (run < kRuns && sg < G) scl16[run * kHScaleWords * 2 + sg] = sv[u];
+  }
+  __syncthreads();
+
+  // ---- lookups
+  auto scale = [&](int a, int j) -> float {
+    return (float)__builtin_bit_cast(half_t, scl16[((a * kTileRows + r) * kHScaleWords) * 2 + j]);
+  };
+  float acc = 0.f;
+#pragma unroll
+  for (int t = 0; t < kSlotsMax; ++t) {
+    const int h = s + 64 * t;
+    if (h < H) {
+      const int j = h >> 1, half = h & 1;
+      const uint32_t base = lds_addr(lut + j * kHGroupStride + h_chunk_offset(16 * half));
+#pragma unroll
+      for (int i = 0; i < P; ++i) acc = fmaf(scale(i, j), h_half_sum(w[t][i], base), acc);
+      if (half == 0) acc = fmaf(scale(P, j), gsum[j], acc);
+    }
+  }
+
+  // ---- reduce the 64 slot partials of each row in a fixed order
+  acc = sum_rows4(acc, (lane ^ 32) << 2);
+  if (lane < 16) part[wave][lane] = acc;
+  __syncthreads();
+  if constexpr (GU) {
+    if (tid < kGuRows) {
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int v = 0; v < kHWaves; ++v) {
+        g += part[v][tid];
+        u += part[v][tid + kGuRows];
+      }
+      const int jo = tile * kGuRows + tid;
+      if (jo < M / 2) y[jo] = (half_t)gate_up_out(g, u);
+    }
+  } else if (tid < kTileRows) {
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kHWaves; ++v) sum += part[v][tid];
+    const int mm = tile * kTileRows + tid;
+    if (mm < M) y[mm] = (half_t)sum;
+  }
+}
+
 // Compute units of the current device, cached per device (atomics: calls may
 // come from several host threads).  Only the grid size depends on it.
 int compute_units() {
@@ -977,6 +1190,19 @@ hipError_t gemv_lowrank_dispatch(const uint32_t *bits, int M, int K, int p, cons
   return hipGetLastError();
 }
 
+// Batch 1, fp16, 4096 < K <= 14336: resident fp16 tables (gemv_h16_kernel)
+// or streamed fp32 windows (gemv_stream*_kernel).  Measured same-run over
+// eight shapes, the resident tables won from K = 8192 at p <= 3 and lost at
+// p = 4 (lookups VALU-bound, nothing left to overlap them with) and below
+// K = 8192 (few windows, the stream's overlap wins).  BCQ_H16=1 / 0 forces
+// one or the other (A/B runs and tests).
+bool gemv_h16_route(int G, int p) {
+  const char *e = getenv("BCQ_H16");
+  if (e != nullptr && e[0] == '0') return false;
+  if (e != nullptr && e[0] == '1') return true;
+  return G >= 64 && p <= 3;
+}
+
 template <typename T, bool GU>
 hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *alpha,
                          const void *zero, const void *x, void *y, hipStream_t s) {
@@ -995,6 +1221,31 @@ hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *
   if (nwin <= 2) {
     gemv_res_tiles<T, 2, GU>(s, b4, a, z, xx, yy, M, G, MT, p);
     return hipGetLastError();
+  }
+  if constexpr (sizeof(T) == 2) {
+    // fp16 with K <= 14336: tables of all of K resident as fp16 where that
+    // measured faster (gemv_h16_route)
+    if (G <= kHMaxG && gemv_h16_route(G, p)) {
+      switch (p) {
+        case 1:
+          hipLaunchKernelGGL((gemv_h16_kernel<1, GU>), dim3(MT), dim3(kHThreads), 0, s, b4, a, z,
+                             xx, yy, M, G, MT);
+          break;
+        case 2:
+          hipLaunchKernelGGL((gemv_h16_kernel<2, GU>), dim3(MT), dim3(kHThreads), 0, s, b4, a, z,
+                             xx, yy, M, G, MT);
+          break;
+        case 3:
+          hipLaunchKernelGGL((gemv_h16_kernel<3, GU>), dim3(MT), dim3(kHThreads), 0, s, b4, a, z,
+                             xx, yy, M, G, MT);
+          break;
+        default:
+          hipLaunchKernelGGL((gemv_h16_kernel<4, GU>), dim3(MT), dim3(kHThreads), 0, s, b4, a, z,
+                             xx, yy, M, G, MT);
+          break;
+      }
+      return hipGetLastError();
+    }
   }
   // larger K: one tile per workgroup, tables streamed window by window
   dim3 grid(MT), block(kRThreads), block2(2 * kRThreads);

@@ -801,6 +801,74 @@ def test_wide_random_sweep_with_padding_and_offsets():
             assert (Yb[:, M:].float() == 3.0).all(), (case, "mixed")
 
 
+# ---------------------------------------------------------------- fp16 tables for K past 4096
+
+class h16_route:
+    """BCQ_H16 for the calls inside the block: "1" resident fp16 tables,
+    "0" streamed fp32 windows (fp16 stores, 4096 < K <= 14336)."""
+
+    def __init__(self, value):
+        self.value = value
+
+    def __enter__(self):
+        import os
+        self.old = os.environ.get("BCQ_H16")
+        os.environ["BCQ_H16"] = self.value
+
+    def __exit__(self, *exc):
+        import os
+        if self.old is None:
+            os.environ.pop("BCQ_H16", None)
+        else:
+            os.environ["BCQ_H16"] = self.old
+
+
+@pytest.mark.parametrize("M,K,P", [
+    (4096, 14336, 4),   # the MLP down shape: 112 groups, one tile per workgroup
+    (37, 8320, 3),      # 65 groups (odd), ragged rows, three workgroups
+    (1000, 4224, 4),    # 33 groups, just past the resident fp32 tables
+    (300, 12416, 2),    # 97 groups
+])
+@pytest.mark.parametrize("route", ["1", "0"])
+def test_fp16_tables_and_streamed_windows(M, K, P, route):
+    """Both batch-1 routes for fp16 K past 4096, forced, every output at every
+    precision: relative L2 within the fp16 bar, and every output within the
+    a-priori bound of its arithmetic. The resident route rounds each table
+    entry (a sum of four signed activations) once to fp16, which adds at
+    most 2^-11 of the output's term magnitude sum |w_k x_k| on top of fp32
+    accumulation and the output's own rounding."""
+    w = bcq_synth.make(M, K, P, seed=M + K + P, outlier_frac=0.01)
+    st = store_of(w)
+    rows = np.arange(M) if M <= 1000 else sample_rows(M, 512, seed=K)
+    for p in range(1, P + 1):
+        say("fp16 K>4096", M, K, P, p, "route", route)
+        y = torch.empty(M, dtype=torch.float16, device="cuda")
+        with h16_route(route):
+            bcq.bcq_gemv(st, p, dev(w.x[0]), y)
+        got = y.cpu().numpy().astype(np.float64)
+        ref = oracle_y_all(w, w.x[:1], [p])[0]
+        assert rel_l2(got, ref) <= 2e-3, (M, K, p, route)
+        mag = magnitudes(w, w.x[:1], [p], rows)[0]
+        c = (K / 4 + 16) * 2.0 ** -24 + (2.0 ** -11 if route == "1" else 0.0)
+        bound = 1.01 * (c * mag + 2.0 ** -11 * np.abs(ref[rows])) + 1e-30
+        assert np.all(np.abs(got[rows] - ref[rows]) <= bound), (M, K, p, route)
+
+
+@pytest.mark.parametrize("Mo,K,P", [(1000, 14336, 4), (40, 8320, 3)])
+def test_gate_up_fp16_tables(Mo, K, P):
+    """The gated-MLP epilogue on the resident fp16-table route (forced, every
+    precision), every output against the oracle."""
+    w = bcq_synth.make(2 * Mo, K, P, seed=Mo + K, outlier_frac=0.01)
+    st = store_of(w)
+    for p in range(1, P + 1):
+        say("gate_up fp16 tables", Mo, K, P, p)
+        y = torch.empty(Mo, dtype=torch.float16, device="cuda")
+        with h16_route("1"):
+            bcq.bcq_gemv_gate_up(st, p, dev(w.x[0]), y)
+        ref = oracle.gemv_gate_up(w.signs, w.alpha, w.zero, w.x[0], p)
+        assert rel_l2(y.cpu().numpy(), ref) <= 2e-3, (Mo, K, p)
+
+
 # ---------------------------------------------------------------- gated-MLP epilogue
 
 @pytest.mark.parametrize("Mo,K,P,dt", [
