@@ -692,13 +692,16 @@ def trace_dispatches(path: str):
     return seq
 
 
-def trace_summary(path: str, last: int) -> None:
+def trace_summary(path: str, last: int, run_index: int = 2) -> None:
     """Per-kernel duration statistics from a rocprofv3 kernel trace (see
     trace_dispatches): for each (kernel, grid) with at least 10 dispatches,
     count, mean, median, p10 and p90 in microseconds over all its dispatches,
-    and over the last `last` dispatches of its last run of at least `last`
-    consecutive dispatches, else of its longest run (in a bench run, the timed
-    replay of a cold per-precision graph)."""
+    and over the last `last` dispatches of its `run_index`-th run (counting
+    from 1) of at least `last` consecutive dispatches, else of its last such
+    run, else of its longest run.  In a bench run a kernel's first timing
+    makes two such runs, the eager pass with the untimed replay, then (after
+    the cache flush) the timed replay: run 2 is that timed replay, and later
+    rows may reuse the same kernel."""
     seq = trace_dispatches(path)
 
     def stats(v):
@@ -723,11 +726,10 @@ def trace_summary(path: str, last: int) -> None:
         prev = k
 
     def timed_run(k):
-        # the last run of at least `last` dispatches (in a bench run the timed
-        # replay comes after the warm-up calls and an untimed replay), else
-        # the longest
         rs = runs.get(k, [])
         full = [r for r in rs if len(r) >= last]
+        if len(full) >= run_index >= 1:
+            return full[run_index - 1]
         return full[-1] if full else max(rs, key=len, default=[])
 
     for k, v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
@@ -764,12 +766,16 @@ def main():
                     help="with --counter-run: precisions (default 2,3,4 at batch 1, else 4)")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="only summarise a rocprofv3 kernel-trace CSV (no GPU needed)")
+    ap.add_argument("--trace-run", type=int, default=2,
+                    help="with --trace-summary: which run (from 1) of at least --trace-last "
+                         "consecutive dispatches to take (default 2: a kernel's first timed "
+                         "replay in a bench run)")
     ap.add_argument("--trace-last", type=int, default=58,
                     help="with --trace-summary: dispatches taken from the end of each "
                          "kernel's longest run")
     args = ap.parse_args()
     if args.trace_summary:
-        trace_summary(args.trace_summary, args.trace_last)
+        trace_summary(args.trace_summary, args.trace_last, args.trace_run)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the BCQ product runs on a single MI355X "

@@ -105,3 +105,27 @@ def test_trace_summary_statistics(tmp_path, capsys):
     b = next(r for r in rows if r["kernel"] == "B")
     assert b["all"]["n"] == 12 and b["all"]["median"] == 7.0
     assert "longest_run_last" not in b  # its longest run is one dispatch
+
+
+def test_trace_summary_takes_the_requested_run(tmp_path, capsys):
+    """The n-th run of at least `last` dispatches: in a bench run, the eager
+    pass with the untimed replay, then the timed replay, then a later row that
+    reuses the kernel."""
+    import json
+
+    path = tmp_path / "kernel_trace.csv"
+    lines = ["Dispatch_Id,Kernel_Name,Grid_Size,Start_Timestamp,End_Timestamp"]
+    d = 0
+    for dur, n in ((9000, 20), (5000, 10), (7000, 10)):  # runs of A, split by B
+        for _ in range(n):
+            d += 1
+            lines.append("%d,A,256,%d,%d" % (d, 1000 * d, 1000 * d + dur))
+        d += 1
+        lines.append("%d,B,256,%d,%d" % (d, 1000 * d, 1000 * d + 1000))
+    path.write_text("\n".join(lines) + "\n")
+    for run, want in ((1, 9.0), (2, 5.0), (3, 7.0), (4, 7.0)):
+        bench.trace_summary(str(path), 10, run)
+        rows = [json.loads(l) for l in capsys.readouterr().out.splitlines()]
+        a = next(r for r in rows if r["kernel"] == "A")
+        assert a["longest_run_last"]["median"] == want, run
+
