@@ -898,7 +898,8 @@ __global__ __launch_bounds__(2 * kRThreads) void gemv_stream2_kernel(
 // when each entry is held in fp16 (32 bytes per chunk; 126 KB of tables at
 // K = 14336), so one workgroup per 16-row tile builds them once, behind one
 // barrier, instead of streaming windows through two buffers with a barrier
-// each.  An entry is the fp32 sum of its four signed activations rounded
+// each.  Dispatched where that measured faster: K >= 8192 at p <= 3
+// (gemv_h16_route).  An entry is the fp32 sum of its four signed activations rounded
 // once to fp16 (relative error at most 2^-11 of the entry); lookups are
 // summed in fp32.
 //

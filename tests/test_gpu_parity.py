@@ -828,6 +828,7 @@ class h16_route:
     (37, 8320, 3),      # 65 groups (odd), ragged rows, three workgroups
     (1000, 4224, 4),    # 33 groups, just past the resident fp32 tables
     (300, 12416, 2),    # 97 groups
+    (5000, 8192, 3),    # more tiles than compute units: workgroups in two rounds
 ])
 @pytest.mark.parametrize("route", ["1", "0"])
 def test_fp16_tables_and_streamed_windows(M, K, P, route):
