@@ -1032,6 +1032,9 @@ LOWRANK_CASES = [
     # correction added by its own launch
     (4096, 4096, 3, 3, 1025, np.float16), (300, 8320, 3, 3, 64, np.float32),
     (1024, 14336, 4, 4, 4096, np.float16),
+    # fp32 with two windows of tables (fused); K = 8192 at p = 3, whose product
+    # runs on the resident fp16 tables before the correction's own launch
+    (600, 4096, 4, 4, 200, np.float32), (2048, 8192, 4, 3, 64, np.float16),
 ]
 
 
