@@ -616,8 +616,8 @@ def test_fp32_large_batch_uses_exact_tables():
 # ---------------------------------------------------------------- graphs and streams
 
 def test_graph_replays_match_eager():
-    """Every product kernel captured in one HIP graph (batch 1 whole-K and
-    streamed, whole-K and split matrix cores with their finalize, tables for
+    """Every product kernel captured in one HIP graph (batch 1 whole-K,
+    resident fp16 tables and streamed, whole-K and split matrix cores with their finalize, tables for
     fp16 batch 2, per-request precision), replayed three times with new
     activations written eagerly between replays; each replay must equal the
     eager calls on the same inputs bit for bit (the kernels are deterministic)."""
@@ -635,10 +635,15 @@ def test_graph_replays_match_eager():
         ws = bcq.new_workspace(st, b)
         cases.append((w, st, X, Yg, Ym, ws))
 
+    Y4 = [torch.empty(c[0].M, dtype=torch.float16, device="cuda") for c in cases]
+
     def body():
-        for w, st, X, Yg, Ym, ws in cases:
+        for (w, st, X, Yg, Ym, ws), y4 in zip(cases, Y4):
             if w.b == 1:
+                # p = 3 and p = 4: at K = 8320 the resident fp16 tables and
+                # the streamed windows
                 bcq.bcq_gemv(st, 3, X[0], Yg[0])
+                bcq.bcq_gemv(st, 4, X[0], y4)
             else:
                 bcq.bcq_gemm_skinny(st, 4, X, Yg, workspace=ws)
             bcq.bcq_gemv_mixed_p(st, w.p_req, X, Ym, workspace=ws)
@@ -652,12 +657,15 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = [(Yg.clone(), Ym.clone()) for _, _, _, Yg, Ym, _ in cases]
+        got = [(Yg.clone(), Ym.clone(), y4.clone())
+               for (_, _, _, Yg, Ym, _), y4 in zip(cases, Y4)]
         body()  # the same calls, eagerly, on the same inputs
         torch.cuda.synchronize()
-        for (w, st, X, Yg, Ym, ws), (gg, gm) in zip(cases, got):
+        for (w, st, X, Yg, Ym, ws), (gg, gm, g4), y4 in zip(cases, got, Y4):
             assert torch.equal(gg, Yg), (rep, w.M, w.K, w.b)
             assert torch.equal(gm, Ym), (rep, w.M, w.K, w.b, "mixed")
+            if w.b == 1:
+                assert torch.equal(g4, y4), (rep, w.M, w.K, "p=4")
 
 
 def test_calls_on_two_streams_are_independent():
