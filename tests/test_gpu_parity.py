@@ -280,7 +280,8 @@ def test_deterministic():
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
-@pytest.mark.parametrize("M,K", [(14336, 4096), (4096, 14336), (1024, 4096)])
+@pytest.mark.parametrize("M,K", [(14336, 4096), (4096, 14336), (1024, 4096),
+                                 (20003, 4096)])  # eight tiles per workgroup, ragged
 def test_full_size_shapes_every_row(M, K):
     """The batch-1 target shapes at p = 2, 3, 4: every output row."""
     w = bcq_synth.make(M, K, 4, dtype=np.float16, seed=M + 3 * K)
