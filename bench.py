@@ -319,8 +319,8 @@ def secondary(args, bcq, torch, bcq_synth, flush):
 
     if want('gemv_'):
         # MLP shapes at batch 1, p = 2/3/4: 14336x4096 (gate/up projection, the
-        # large-shape target row) and 4096x14336 (down projection, whose K exceeds
-        # what one workgroup keeps resident, so its tables stream through LDS)
+        # large-shape target row) and 4096x14336 (down projection, whose K is past
+        # the whole-K fp32 tables: its tables are held resident in fp16)
         for M, K, seed in ((14336, 4096, 3), (4096, 14336, 6)):
             if not want("gemv_%dx%d_b1" % (M, K)):
                 continue

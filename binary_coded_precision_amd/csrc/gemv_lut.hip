@@ -900,12 +900,12 @@ __global__ __launch_bounds__(2 * kRThreads) void gemv_stream2_kernel(
 //
 // For fp16 stores with 4096 < K <= 14336 the tables of all of K fit in LDS
 // when each entry is held in fp16 (32 bytes per chunk; 126 KB of tables at
-// K = 14336), so one workgroup per 16-row tile builds them once, behind one
-// barrier, instead of streaming windows through two buffers with a barrier
-// each.  Dispatched where that measured faster: K >= 8192 at p <= 3
-// (gemv_h16_route).  An entry is the fp32 sum of its four signed activations rounded
-// once to fp16 (relative error at most 2^-11 of the entry); lookups are
-// summed in fp32.
+// K = 14336), so a workgroup builds them once, behind one barrier, instead of
+// streaming windows through two buffers with a barrier each, and with more
+// row tiles than compute units walks several tiles with them (gemv_h16_route
+// has the measurements).  An entry is the fp32 sum of its four signed
+// activations rounded once to fp16 (relative error at most 2^-11 of the
+// entry); lookups are summed in fp32.
 //
 // 1024 lanes: lane (r, s) takes row r of the tile and half-group slots
 // s, s + 64, s + 128, ... (s = wave * 4 + lane / 16); every thread builds
@@ -962,34 +962,48 @@ __device__ __forceinline__ float h_half_sum(const uint2 bw, uint32_t base) {
   return (s[0] + s[1]) + (s[2] + s[3]);
 }
 
-template <int P, bool GU = false>
+// NG: groups of K the tables hold (64: K <= 8192, 112: K <= 14336).
+// NB = 1: one tile per workgroup (grid = row tiles).  NB = 2: the workgroup
+// walks tiles blockIdx.x + k * gridDim.x with the tables built once; the next
+// tile's scales are staged into the other of two buffers during the current
+// tile's lookups, and its sign words are requested one tile ahead, so each
+// tile costs one barrier.
+template <int P, bool GU, int NG, int NB>
 __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
     const uint4 *__restrict__ bits, const half_t *__restrict__ alpha,
     const half_t *__restrict__ zero, const half_t *__restrict__ x, half_t *__restrict__ y, int M,
     int G, int MT) {
-  __shared__ __attribute__((aligned(16))) char lut[kHMaxG * kHGroupStride];
-  __shared__ float gsum[kHMaxG];
-  __shared__ float part[kHWaves][kTileRows];
-  // staged scales and offsets as fp16 bits: [array][row][group], rows at an
-  // odd number of words so the 16 rows a wavefront reads hit distinct banks
-  __shared__ uint32_t scl[(P + 1) * kTileRows * kHScaleWords];
-  constexpr int kRounds = kHMaxChunkRounds;
-  // staging: 128 threads per (array, row) run of G <= 112 values, eight runs
-  // at a time
+  static_assert(NG <= kHMaxG && (NB == 1 || NB == 2), "resident groups, scale buffers");
+  constexpr int kRounds = (NG * kChunksPerGroup + kHThreads - 1) / kHThreads;
+  constexpr int kSW = NG / 2 + 1;  // staged scale row in 32-bit words (odd)
+  // staging: kSG threads per (array, row) run of G <= NG values
+  constexpr int kSG = NG <= 64 ? 64 : 128;
   constexpr int kRuns = (P + 1) * kTileRows;
-  constexpr int kScalePerThread = (kRuns + kHThreads / 128 - 1) / (kHThreads / 128);
+  constexpr int kRunsAtOnce = kHThreads / kSG;
+  constexpr int kScalePerThread = (kRuns + kRunsAtOnce - 1) / kRunsAtOnce;
+  constexpr int kSlots = (2 * NG + 63) / 64;  // half-group slots per lane
+  __shared__ __attribute__((aligned(16))) char lut[NG * kHGroupStride];
+  __shared__ float gsum[NG];
+  __shared__ float part[NB][kHWaves][kTileRows];
+  // staged scales and offsets as fp16 bits: [buffer][array][row][group], rows
+  // at an odd number of words so the 16 rows a wavefront reads hit distinct
+  // banks
+  __shared__ uint32_t scl[NB][kRuns * kSW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r = lane & 15;
   const int s = wave * 4 + (lane >> 4);  // half-group slot 0..63
-  const int tile = blockIdx.x;
   const int H = 2 * G;                   // half groups of K
   const int NC = kChunksPerGroup * G;    // chunks of K
+  const int nt = NB == 1 ? 1 : (MT - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const size_t plane_stride = (size_t)MT * G * kTileRows;  // in uint4
   const size_t MG = (size_t)M * G;
   const uint2 *bits2 = reinterpret_cast<const uint2 *>(bits);
+  // tile k of this workgroup; past its last tile a load re-reads the last
+  // one (lines already fetched), so the load phase stays branch-free
+  auto tile_of = [&](int k) { return (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x; };
 
   // ---- activations of the chunks this thread builds (a past-the-end chunk
   // re-reads the last one and builds nothing)
@@ -1002,33 +1016,53 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
                               0);
   }
 
-  // ---- scales and offsets of the tile: thread tid stages group tid % 128 of
-  // runs tid / 128 + 8u (run = array * 16 + row; planes, then offsets), so
-  // consecutive threads read consecutive groups of a row (coalesced); a
-  // group or run past the end re-reads a valid value and stages nothing
-  const int sg = tid % 128;
+  // ---- scales and offsets of a tile: thread tid stages group tid % kSG of
+  // runs tid / kSG + kRunsAtOnce * u (run = array * 16 + row; planes, then
+  // offsets), so consecutive threads read consecutive groups of a row
+  // (coalesced); a group or run past the end re-reads a valid value and
+  // stages nothing
+  const int sg = tid % kSG;
   const int sgc = min(sg, G - 1);
   unsigned short sv[kScalePerThread];
+  auto sload = [&](int k) {
+    const int tl = tile_of(k);
 #pragma unroll
-  for (int u = 0; u < kScalePerThread; ++u) {
-    const int run = min(tid / 128 + 8 * u, kRuns - 1);
-    const int a = run / kTileRows;
-    const int row = min(tile * kTileRows + run % kTileRows, M - 1);
-    const half_t *src = (a < P ? alpha + (size_t)a * MG : zero) + (size_t)row * G + sgc;
-    sv[u] = *reinterpret_cast<const unsigned short *>(src);
-  }
+    for (int u = 0; u < kScalePerThread; ++u) {
+      const int run = min(tid / kSG + kRunsAtOnce * u, kRuns - 1);
+      const int a = run / kTileRows;
+      const int row = min(tl * kTileRows + run % kTileRows, M - 1);
+      const half_t *src = (a < P ? alpha + (size_t)a * MG : zero) + (size_t)row * G + sgc;
+      sv[u] = *reinterpret_cast<const unsigned short *>(src);
+    }
+  };
+  auto sstore = [&](int b) {
+    unsigned short *s16 = reinterpret_cast<unsigned short *>(scl[b]);
+#pragma unroll
+    for (int u = 0; u < kScalePerThread; ++u) {
+      const int run = tid / kSG + kRunsAtOnce * u;
+      if (run < kRuns && sg < G) s16[run * kSW * 2 + sg] = sv[u];
+    }
+  };
 
-  // ---- sign words of this lane's half groups, one uint2 per plane (a slot
-  // past the last half group re-reads the last one and adds nothing)
-  constexpr int kSlotsMax = (2 * kHMaxG + 63) / 64;  // 4
-  uint2 w[kSlotsMax][P];
-#pragma unroll
-  for (int t = 0; t < kSlotsMax; ++t) {
+  // ---- sign words of this lane's half groups in a tile, one uint2 per
+  // plane (a slot past the last half group re-reads the last one and adds
+  // nothing)
+  uint2 wa[kSlots][P], wb[kSlots][P];
+  auto wfetch = [&](int k, int t, uint2 (&w)[kSlots][P]) {
     const int h = min(s + 64 * t, H - 1);
-    const unsigned q = (unsigned)((((size_t)tile * G + (h >> 1)) * kTileRows + r) * 2 + (h & 1));
+    const unsigned q =
+        (unsigned)((((size_t)tile_of(k) * G + (h >> 1)) * kTileRows + r) * 2 + (h & 1));
 #pragma unroll
     for (int i = 0; i < P; ++i) w[t][i] = bits2[(size_t)i * plane_stride * 2 + q];
-  }
+  };
+
+  // ---- first tile: scales, then only the first slot's sign words before the
+  // table barrier.  The barrier waits for the activations; sign words
+  // requested ahead of it queue in front of other workgroups' activation and
+  // scale loads and hold every barrier back (4096x14336, p = 4: 14.7 us with
+  // all slots requested first, 12.3 with one).
+  sload(0);
+  wfetch(0, 0, wa);
 
   // ---- build the tables and group sums.  Every round computes its chunk
   // (a past-the-end one its clamped copy) and only the stores are guarded:
@@ -1059,52 +1093,80 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
       if ((tid & 31) == 0) gsum[c / kChunksPerGroup] = cs;
     }
   }
-  unsigned short *scl16 = reinterpret_cast<unsigned short *>(scl);
-#pragma unroll
-  for (int u = 0; u < kScalePerThread; ++u) {
-    const int run = tid / 128 + 8 * u;
-    if (run < kRuns && sg < G) scl16[run * kHScaleWords * 2 + sg] = sv[u];
-  }
+  sstore(0);
   __syncthreads();
+#pragma unroll
+  for (int t = 1; t < kSlots; ++t) wfetch(0, t, wa);
 
-  // ---- lookups
-  auto scale = [&](int a, int j) -> float {
-    return (float)__builtin_bit_cast(half_t, scl16[((a * kTileRows + r) * kHScaleWords) * 2 + j]);
-  };
-  float acc = 0.f;
+  // ---- lookups of one tile from scale buffer b; returns this lane's partial
+  auto lookups = [&](int b, const uint2 (&w)[kSlots][P]) -> float {
+    const unsigned short *s16 = reinterpret_cast<const unsigned short *>(scl[b]);
+    auto scale = [&](int a, int j) -> float {
+      return (float)__builtin_bit_cast(half_t, s16[((a * kTileRows + r) * kSW) * 2 + j]);
+    };
+    float acc = 0.f;
 #pragma unroll
-  for (int t = 0; t < kSlotsMax; ++t) {
-    const int h = s + 64 * t;
-    if (h < H) {
-      const int j = h >> 1, half = h & 1;
-      const uint32_t base = lds_addr(lut + j * kHGroupStride + h_chunk_offset(16 * half));
+    for (int t = 0; t < kSlots; ++t) {
+      const int h = s + 64 * t;
+      if (h < H) {
+        const int j = h >> 1, half = h & 1;
+        const uint32_t base = lds_addr(lut + j * kHGroupStride + h_chunk_offset(16 * half));
 #pragma unroll
-      for (int i = 0; i < P; ++i) acc = fmaf(scale(i, j), h_half_sum(w[t][i], base), acc);
-      if (half == 0) acc = fmaf(scale(P, j), gsum[j], acc);
-    }
-  }
-
-  // ---- reduce the 64 slot partials of each row in a fixed order
-  acc = sum_rows4(acc, (lane ^ 32) << 2);
-  if (lane < 16) part[wave][lane] = acc;
-  __syncthreads();
-  if constexpr (GU) {
-    if (tid < kGuRows) {
-      float g = 0.f, u = 0.f;
-#pragma unroll
-      for (int v = 0; v < kHWaves; ++v) {
-        g += part[v][tid];
-        u += part[v][tid + kGuRows];
+        for (int i = 0; i < P; ++i) acc = fmaf(scale(i, j), h_half_sum(w[t][i], base), acc);
+        if (half == 0) acc = fmaf(scale(P, j), gsum[j], acc);
       }
-      const int jo = tile * kGuRows + tid;
-      if (jo < M / 2) y[jo] = (half_t)gate_up_out(g, u);
     }
-  } else if (tid < kTileRows) {
-    float sum = 0.f;
+    // the 64 slot partials of each row, reduced in a fixed order
+    return sum_rows4(acc, (lane ^ 32) << 2);
+  };
+  // ---- the 16 wavefront partials of each row of tile k, in a fixed order
+  auto finish = [&](int k, int b) {
+    const int tl = tile_of(k);
+    if constexpr (GU) {
+      if (tid < kGuRows) {
+        float g = 0.f, u = 0.f;
 #pragma unroll
-    for (int v = 0; v < kHWaves; ++v) sum += part[v][tid];
-    const int mm = tile * kTileRows + tid;
-    if (mm < M) y[mm] = (half_t)sum;
+        for (int v = 0; v < kHWaves; ++v) {
+          g += part[b][v][tid];
+          u += part[b][v][tid + kGuRows];
+        }
+        const int jo = tl * kGuRows + tid;
+        if (jo < M / 2) y[jo] = (half_t)gate_up_out(g, u);
+      }
+    } else if (tid < kTileRows) {
+      float sum = 0.f;
+#pragma unroll
+      for (int v = 0; v < kHWaves; ++v) sum += part[b][v][tid];
+      const int mm = tl * kTileRows + tid;
+      if (mm < M) y[mm] = (half_t)sum;
+    }
+  };
+
+  if constexpr (NB == 1) {
+    const float acc = lookups(0, wa);
+    if (lane < 16) part[0][wave][lane] = acc;
+    __syncthreads();
+    finish(0, 0);
+  } else {
+    // tile k: request tile k + 1's scales and sign words, look up tile k,
+    // stage tile k + 1's scales into the other buffer (its last readers, tile
+    // k - 1's lookups, finished before the previous barrier), then one
+    // barrier before tile k's rows are summed
+    auto step = [&](int k, const uint2 (&wc)[kSlots][P], uint2 (&wn)[kSlots][P]) {
+      const int b = k & 1;
+      sload(k + 1);
+#pragma unroll
+      for (int t = 0; t < kSlots; ++t) wfetch(k + 1, t, wn);
+      const float acc = lookups(b, wc);
+      if (lane < 16) part[b][wave][lane] = acc;
+      sstore(b ^ 1);
+      __syncthreads();
+      finish(k, b);
+    };
+    for (int k = 0; k < nt; k += 2) {
+      step(k, wa, wb);
+      if (k + 1 < nt) step(k + 1, wb, wa);
+    }
   }
 }
 
@@ -1201,17 +1263,55 @@ hipError_t gemv_lowrank_dispatch(const uint32_t *bits, int M, int K, int p, cons
   return hipGetLastError();
 }
 
+template <int P, bool GU, int NG>
+void gemv_h16_tiles(hipStream_t s, const uint4 *b4, const half_t *a, const half_t *z,
+                    const half_t *xx, half_t *yy, int M, int G, int MT) {
+  // more row tiles than compute units: one workgroup per unit walks several
+  // tiles with the tables built once (two scale buffers; at K > 8192, p = 4
+  // they do not fit beside the tables, and every tile takes a workgroup)
+  const int cus = compute_units();
+  if constexpr (NG == 64 || P <= 3) {
+    if (MT > cus) {
+      hipLaunchKernelGGL((gemv_h16_kernel<P, GU, NG, 2>), dim3(cus), dim3(kHThreads), 0, s, b4, a,
+                         z, xx, yy, M, G, MT);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((gemv_h16_kernel<P, GU, NG, 1>), dim3(MT), dim3(kHThreads), 0, s, b4, a, z,
+                     xx, yy, M, G, MT);
+}
+
+template <bool GU>
+void gemv_h16_launch(hipStream_t s, const uint4 *b4, const half_t *a, const half_t *z,
+                     const half_t *xx, half_t *yy, int M, int G, int MT, int p) {
+  if (G <= 64) {
+    switch (p) {
+      case 1: gemv_h16_tiles<1, GU, 64>(s, b4, a, z, xx, yy, M, G, MT); break;
+      case 2: gemv_h16_tiles<2, GU, 64>(s, b4, a, z, xx, yy, M, G, MT); break;
+      case 3: gemv_h16_tiles<3, GU, 64>(s, b4, a, z, xx, yy, M, G, MT); break;
+      default: gemv_h16_tiles<4, GU, 64>(s, b4, a, z, xx, yy, M, G, MT); break;
+    }
+  } else {
+    switch (p) {
+      case 1: gemv_h16_tiles<1, GU, kHMaxG>(s, b4, a, z, xx, yy, M, G, MT); break;
+      case 2: gemv_h16_tiles<2, GU, kHMaxG>(s, b4, a, z, xx, yy, M, G, MT); break;
+      case 3: gemv_h16_tiles<3, GU, kHMaxG>(s, b4, a, z, xx, yy, M, G, MT); break;
+      default: gemv_h16_tiles<4, GU, kHMaxG>(s, b4, a, z, xx, yy, M, G, MT); break;
+    }
+  }
+}
+
 // Batch 1, fp16, 4096 < K <= 14336: resident fp16 tables (gemv_h16_kernel)
-// or streamed fp32 windows (gemv_stream*_kernel).  Measured same-run over
-// eight shapes, the resident tables won from K = 8192 at p <= 3 and lost at
-// p = 4 (lookups VALU-bound, nothing left to overlap them with) and below
-// K = 8192 (few windows, the stream's overlap wins).  BCQ_H16=1 / 0 forces
-// one or the other (A/B runs and tests).
+// or streamed fp32 windows (gemv_stream*_kernel).  Measured same-run at
+// p = 2..4 over 16 shapes from 256x12288 to 28672x8192 (K = 4224 to 14336),
+// the resident tables won everywhere: by 4-30% with few row tiles and by up
+// to 2x with many (28672x5120, p = 2: 16.9 against 33.6 us).  BCQ_H16=0
+// forces the stream (A/B runs and tests); BCQ_H16=1 the resident tables.
 bool gemv_h16_route(int G, int p) {
+  (void)G;
+  (void)p;
   const char *e = getenv("BCQ_H16");
-  if (e != nullptr && e[0] == '0') return false;
-  if (e != nullptr && e[0] == '1') return true;
-  return G >= 64 && p <= 3;
+  return !(e != nullptr && e[0] == '0');
 }
 
 template <typename T, bool GU>
@@ -1237,24 +1337,7 @@ hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *
     // fp16 with K <= 14336: tables of all of K resident as fp16 where that
     // measured faster (gemv_h16_route)
     if (G <= kHMaxG && gemv_h16_route(G, p)) {
-      switch (p) {
-        case 1:
-          hipLaunchKernelGGL((gemv_h16_kernel<1, GU>), dim3(MT), dim3(kHThreads), 0, s, b4, a, z,
-                             xx, yy, M, G, MT);
-          break;
-        case 2:
-          hipLaunchKernelGGL((gemv_h16_kernel<2, GU>), dim3(MT), dim3(kHThreads), 0, s, b4, a, z,
-                             xx, yy, M, G, MT);
-          break;
-        case 3:
-          hipLaunchKernelGGL((gemv_h16_kernel<3, GU>), dim3(MT), dim3(kHThreads), 0, s, b4, a, z,
-                             xx, yy, M, G, MT);
-          break;
-        default:
-          hipLaunchKernelGGL((gemv_h16_kernel<4, GU>), dim3(MT), dim3(kHThreads), 0, s, b4, a, z,
-                             xx, yy, M, G, MT);
-          break;
-      }
+      gemv_h16_launch<GU>(s, b4, a, z, xx, yy, M, G, MT, p);
       return hipGetLastError();
     }
   }

@@ -618,15 +618,16 @@ def test_fp32_large_batch_uses_exact_tables():
 
 def test_graph_replays_match_eager():
     """Every product kernel captured in one HIP graph (batch 1 whole-K,
-    resident fp16 tables and streamed, whole-K and split matrix cores with their finalize, tables for
+    resident fp16 tables (one and several tiles per workgroup) and streamed,
+    whole-K and split matrix cores with their finalize, tables for
     fp16 batch 2, per-request precision), replayed three times with new
     activations written eagerly between replays; each replay must equal the
     eager calls on the same inputs bit for bit (the kernels are deterministic)."""
     import bench
 
     cases = []
-    for M, K, b in [(3200, 2304, 1), (64, 8320, 1), (3200, 2304, 8), (3200, 2304, 32),
-                    (256, 8320, 2)]:
+    for M, K, b in [(3200, 2304, 1), (64, 8320, 1), (5000, 8192, 1), (3200, 2304, 8),
+                    (3200, 2304, 32), (256, 8320, 2)]:
         w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=M + K + b,
                            p_choices=(2, 3, 4))
         st = store_of(w)
@@ -641,10 +642,12 @@ def test_graph_replays_match_eager():
     def body():
         for (w, st, X, Yg, Ym, ws), y4 in zip(cases, Y4):
             if w.b == 1:
-                # p = 3 and p = 4: at K = 8320 the resident fp16 tables and
-                # the streamed windows
+                # p = 3 and p = 4: past K = 4096 the resident fp16 tables
+                # (5000 rows: workgroups walking two tiles) and the
+                # streamed windows
                 bcq.bcq_gemv(st, 3, X[0], Yg[0])
-                bcq.bcq_gemv(st, 4, X[0], y4)
+                with h16_route("0"):
+                    bcq.bcq_gemv(st, 4, X[0], y4)
             else:
                 bcq.bcq_gemm_skinny(st, 4, X, Yg, workspace=ws)
             bcq.bcq_gemv_mixed_p(st, w.p_req, X, Ym, workspace=ws)
@@ -837,7 +840,10 @@ class h16_route:
     (37, 8320, 3),      # 65 groups (odd), ragged rows, three workgroups
     (1000, 4224, 4),    # 33 groups, just past the resident fp32 tables
     (300, 12416, 2),    # 97 groups
-    (5000, 8192, 3),    # more tiles than compute units: workgroups in two rounds
+    (5000, 8192, 3),    # more tiles than compute units: workgroups take one or two tiles
+    (12003, 8192, 4),   # 751 tiles: two or three per workgroup, ragged rows
+    (9001, 10240, 3),   # 80 groups, 563 tiles over the workgroups, ragged rows
+    (6000, 12416, 4),   # 97 groups at p = 4: one tile per workgroup, 375 workgroups
 ])
 @pytest.mark.parametrize("route", ["1", "0"])
 def test_fp16_tables_and_streamed_windows(M, K, P, route):
@@ -864,7 +870,12 @@ def test_fp16_tables_and_streamed_windows(M, K, P, route):
         assert np.all(np.abs(got[rows] - ref[rows]) <= bound), (M, K, p, route)
 
 
-@pytest.mark.parametrize("Mo,K,P", [(1000, 14336, 4), (40, 8320, 3)])
+@pytest.mark.parametrize("Mo,K,P", [
+    (1000, 14336, 4),   # one tile per workgroup
+    (40, 8320, 3),
+    (3000, 8192, 2),    # 375 tiles: workgroups walk one or two
+    (2504, 10240, 3),   # 313 tiles at 80 groups
+])
 def test_gate_up_fp16_tables(Mo, K, P):
     """The gated-MLP epilogue on the resident fp16-table route (forced, every
     precision), every output against the oracle."""
