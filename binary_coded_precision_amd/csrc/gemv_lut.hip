@@ -968,12 +968,19 @@ __device__ __forceinline__ float h_half_sum(const uint2 bw, uint32_t base) {
 // tile's scales are staged into the other of two buffers during the current
 // tile's lookups, and its sign words are requested one tile ahead, so each
 // tile costs one barrier.
-template <int P, bool GU, int NG, int NB>
+// RS > 1 (few row tiles, one per workgroup): RS workgroups share tile
+// blockIdx.x / RS, each taking 16 / RS of its rows; lane (r, s) takes row
+// r % (16 / RS) of that part and planes PC * (r / (16 / RS)) .. + PC - 1, as
+// in gemv_res_kernel, so the lookups of a tile spread over RS compute units.
+template <int P, bool GU, int NG, int NB, int RS = 1>
 __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
     const uint4 *__restrict__ bits, const half_t *__restrict__ alpha,
     const half_t *__restrict__ zero, const half_t *__restrict__ x, half_t *__restrict__ y, int M,
     int G, int MT) {
   static_assert(NG <= kHMaxG && (NB == 1 || NB == 2), "resident groups, scale buffers");
+  static_assert(RS == 1 || (NB == 1 && !GU), "row parts: one tile per workgroup, plain products");
+  constexpr int kPartRows = kTileRows / RS;
+  constexpr int PC = (P + RS - 1) / RS;  // planes per lane
   constexpr int kRounds = (NG * kChunksPerGroup + kHThreads - 1) / kHThreads;
   constexpr int kSW = NG / 2 + 1;  // staged scale row in 32-bit words (odd)
   // staging: kSG threads per (array, row) run of G <= NG values
@@ -995,6 +1002,9 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   const int wave = tid >> 6;
   const int r = lane & 15;
   const int s = wave * 4 + (lane >> 4);  // half-group slot 0..63
+  const int rl = r % kPartRows;          // row within the part
+  const int ph = r / kPartRows;          // plane part of this lane
+  const int prow = RS > 1 ? ((int)blockIdx.x % RS) * kPartRows + rl : r;  // row within the tile
   const int H = 2 * G;                   // half groups of K
   const int NC = kChunksPerGroup * G;    // chunks of K
   const int nt = NB == 1 ? 1 : (MT - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
@@ -1003,7 +1013,9 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   const uint2 *bits2 = reinterpret_cast<const uint2 *>(bits);
   // tile k of this workgroup; past its last tile a load re-reads the last
   // one (lines already fetched), so the load phase stays branch-free
-  auto tile_of = [&](int k) { return (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x; };
+  auto tile_of = [&](int k) {
+    return RS > 1 ? (int)blockIdx.x / RS : (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x;
+  };
 
   // ---- activations of the chunks this thread builds (a past-the-end chunk
   // re-reads the last one and builds nothing)
@@ -1045,15 +1057,18 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   };
 
   // ---- sign words of this lane's half groups in a tile, one uint2 per
-  // plane (a slot past the last half group re-reads the last one and adds
-  // nothing)
-  uint2 wa[kSlots][P], wb[kSlots][P];
-  auto wfetch = [&](int k, int t, uint2 (&w)[kSlots][P]) {
+  // plane it looks up (a slot past the last half group re-reads the last one
+  // and adds nothing; so does a plane past P)
+  uint2 wa[kSlots][PC], wb[kSlots][PC];
+  auto wfetch = [&](int k, int t, uint2 (&w)[kSlots][PC]) {
     const int h = min(s + 64 * t, H - 1);
     const unsigned q =
-        (unsigned)((((size_t)tile_of(k) * G + (h >> 1)) * kTileRows + r) * 2 + (h & 1));
+        (unsigned)((((size_t)tile_of(k) * G + (h >> 1)) * kTileRows + prow) * 2 + (h & 1));
 #pragma unroll
-    for (int i = 0; i < P; ++i) w[t][i] = bits2[(size_t)i * plane_stride * 2 + q];
+    for (int u = 0; u < PC; ++u) {
+      const int i = RS > 1 ? min(ph * PC + u, P - 1) : u;
+      w[t][u] = bits2[(size_t)i * plane_stride * 2 + q];
+    }
   };
 
   // ---- first tile: scales, then only the first slot's sign words before the
@@ -1099,10 +1114,10 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   for (int t = 1; t < kSlots; ++t) wfetch(0, t, wa);
 
   // ---- lookups of one tile from scale buffer b; returns this lane's partial
-  auto lookups = [&](int b, const uint2 (&w)[kSlots][P]) -> float {
+  auto lookups = [&](int b, const uint2 (&w)[kSlots][PC]) -> float {
     const unsigned short *s16 = reinterpret_cast<const unsigned short *>(scl[b]);
     auto scale = [&](int a, int j) -> float {
-      return (float)__builtin_bit_cast(half_t, s16[((a * kTileRows + r) * kSW) * 2 + j]);
+      return (float)__builtin_bit_cast(half_t, s16[((a * kTileRows + prow) * kSW) * 2 + j]);
     };
     float acc = 0.f;
 #pragma unroll
@@ -1112,12 +1127,25 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
         const int j = h >> 1, half = h & 1;
         const uint32_t base = lds_addr(lut + j * kHGroupStride + h_chunk_offset(16 * half));
 #pragma unroll
-        for (int i = 0; i < P; ++i) acc = fmaf(scale(i, j), h_half_sum(w[t][i], base), acc);
-        if (half == 0) acc = fmaf(scale(P, j), gsum[j], acc);
+        for (int u = 0; u < PC; ++u) {
+          // a plane index past P (P not a multiple of RS) looks up with scale 0
+          const int i = RS > 1 ? ph * PC + u : u;
+          const float sc = i < P ? scale(min(i, P - 1), j) : 0.f;
+          acc = fmaf(sc, h_half_sum(w[t][u], base), acc);
+        }
+        if (half == 0 && (RS == 1 || ph == 0)) acc = fmaf(scale(P, j), gsum[j], acc);
       }
     }
-    // the 64 slot partials of each row, reduced in a fixed order
-    return sum_rows4(acc, (lane ^ 32) << 2);
+    // the 64 slot partials of each row, reduced in a fixed order; then the
+    // plane parts, lanes r, r + 16/RS, .. of the 16-lane row (DPP row_ror)
+    acc = sum_rows4(acc, (lane ^ 32) << 2);
+    if constexpr (RS == 4)
+      acc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, acc), 0x124,
+                                                                0xF, 0xF, true));
+    if constexpr (RS >= 2)
+      acc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, acc), 0x128,
+                                                                0xF, 0xF, true));
+    return acc;
   };
   // ---- the 16 wavefront partials of each row of tile k, in a fixed order
   auto finish = [&](int k, int b) {
@@ -1133,11 +1161,11 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
         const int jo = tl * kGuRows + tid;
         if (jo < M / 2) y[jo] = (half_t)gate_up_out(g, u);
       }
-    } else if (tid < kTileRows) {
+    } else if (tid < kPartRows) {
       float sum = 0.f;
 #pragma unroll
       for (int v = 0; v < kHWaves; ++v) sum += part[b][v][tid];
-      const int mm = tl * kTileRows + tid;
+      const int mm = tl * kTileRows + (RS > 1 ? ((int)blockIdx.x % RS) * kPartRows : 0) + tid;
       if (mm < M) y[mm] = (half_t)sum;
     }
   };
@@ -1152,7 +1180,7 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
     // stage tile k + 1's scales into the other buffer (its last readers, tile
     // k - 1's lookups, finished before the previous barrier), then one
     // barrier before tile k's rows are summed
-    auto step = [&](int k, const uint2 (&wc)[kSlots][P], uint2 (&wn)[kSlots][P]) {
+    auto step = [&](int k, const uint2 (&wc)[kSlots][PC], uint2 (&wn)[kSlots][PC]) {
       const int b = k & 1;
       sload(k + 1);
 #pragma unroll
@@ -1268,8 +1296,22 @@ void gemv_h16_tiles(hipStream_t s, const uint4 *b4, const half_t *a, const half_
                     const half_t *xx, half_t *yy, int M, int G, int MT) {
   // more row tiles than compute units: one workgroup per unit walks several
   // tiles with the tables built once (two scale buffers; at K > 8192, p = 4
-  // they do not fit beside the tables, and every tile takes a workgroup)
+  // they do not fit beside the tables, and every tile takes a workgroup).
+  // At most a quarter (a half) of the units holding a tile: each tile's rows
+  // split over 4 (2) workgroups.
   const int cus = compute_units();
+  if constexpr (!GU) {
+    if (4 * MT <= cus) {
+      hipLaunchKernelGGL((gemv_h16_kernel<P, GU, NG, 1, 4>), dim3(4 * MT), dim3(kHThreads), 0, s, b4,
+                         a, z, xx, yy, M, G, MT);
+      return;
+    }
+    if (2 * MT <= cus) {
+      hipLaunchKernelGGL((gemv_h16_kernel<P, GU, NG, 1, 2>), dim3(2 * MT), dim3(kHThreads), 0, s, b4,
+                         a, z, xx, yy, M, G, MT);
+      return;
+    }
+  }
   if constexpr (NG == 64 || P <= 3) {
     if (MT > cus) {
       hipLaunchKernelGGL((gemv_h16_kernel<P, GU, NG, 2>), dim3(cus), dim3(kHThreads), 0, s, b4, a,

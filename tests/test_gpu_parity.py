@@ -837,13 +837,15 @@ class h16_route:
 
 @pytest.mark.parametrize("M,K,P", [
     (4096, 14336, 4),   # the MLP down shape: 112 groups, one tile per workgroup
-    (37, 8320, 3),      # 65 groups (odd), ragged rows, three workgroups
+    (37, 8320, 3),      # 65 groups (odd), ragged rows, three tiles split four ways
     (1000, 4224, 4),    # 33 groups, just past the resident fp32 tables
     (300, 12416, 2),    # 97 groups
     (5000, 8192, 3),    # more tiles than compute units: workgroups take one or two tiles
     (12003, 8192, 4),   # 751 tiles: two or three per workgroup, ragged rows
     (9001, 10240, 3),   # 80 groups, 563 tiles over the workgroups, ragged rows
     (6000, 12416, 4),   # 97 groups at p = 4: one tile per workgroup, 375 workgroups
+    (1500, 6144, 3),    # 94 tiles: rows split over two workgroups, ragged rows
+    (1024, 8192, 4),    # 64 tiles: rows split over four workgroups
 ])
 @pytest.mark.parametrize("route", ["1", "0"])
 def test_fp16_tables_and_streamed_windows(M, K, P, route):
