@@ -972,13 +972,18 @@ __device__ __forceinline__ float h_half_sum(const uint2 bw, uint32_t base) {
 // blockIdx.x / RS, each taking 16 / RS of its rows; lane (r, s) takes row
 // r % (16 / RS) of that part and planes PC * (r / (16 / RS)) .. + PC - 1, as
 // in gemv_res_kernel, so the lookups of a tile spread over RS compute units.
-template <int P, bool GU, int NG, int NB, int RS = 1>
+// MP (NG < G <= 2 NG, one tile per workgroup): K is walked in two passes with
+// the tables of one pass resident; the second pass's activations, scales and
+// sign words are requested during the first pass's lookups, and two barriers
+// free the tables and publish the new ones.
+template <int P, bool GU, int NG, int NB, int RS = 1, bool MP = false>
 __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
     const uint4 *__restrict__ bits, const half_t *__restrict__ alpha,
     const half_t *__restrict__ zero, const half_t *__restrict__ x, half_t *__restrict__ y, int M,
     int G, int MT) {
   static_assert(NG <= kHMaxG && (NB == 1 || NB == 2), "resident groups, scale buffers");
   static_assert(RS == 1 || (NB == 1 && !GU), "row parts: one tile per workgroup, plain products");
+  static_assert(!MP || NB == 1, "passes over K: one tile per workgroup");
   constexpr int kPartRows = kTileRows / RS;
   constexpr int PC = (P + RS - 1) / RS;  // planes per lane
   constexpr int kRounds = (NG * kChunksPerGroup + kHThreads - 1) / kHThreads;
@@ -1005,8 +1010,7 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   const int rl = r % kPartRows;          // row within the part
   const int ph = r / kPartRows;          // plane part of this lane
   const int prow = RS > 1 ? ((int)blockIdx.x % RS) * kPartRows + rl : r;  // row within the tile
-  const int H = 2 * G;                   // half groups of K
-  const int NC = kChunksPerGroup * G;    // chunks of K
+  const int G0 = MP ? NG : G;  // groups of the first pass (G <= NG without MP)
   const int nt = NB == 1 ? 1 : (MT - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const size_t plane_stride = (size_t)MT * G * kTileRows;  // in uint4
   const size_t MG = (size_t)M * G;
@@ -1017,16 +1021,21 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
     return RS > 1 ? (int)blockIdx.x / RS : (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x;
   };
 
-  // ---- activations of the chunks this thread builds (a past-the-end chunk
-  // re-reads the last one and builds nothing)
+  // ---- activations of the chunks this thread builds in the pass of Gp
+  // groups from group g0 (a past-the-end chunk re-reads the last one and
+  // builds nothing)
   typename Act<half_t>::raw xr[kRounds];
+  auto xload = [&](int g0, int Gp) {
+    const int NCp = kChunksPerGroup * Gp;
 #pragma unroll
-  for (int t = 0; t < kRounds; ++t) {
-    const int c = min(tid + kHThreads * t, NC - 1);
-    xr[t] = Act<half_t>::load(x + (unsigned)((c / kChunksPerGroup) * kGroup +
-                                             chunk_base(c % kChunksPerGroup)),
-                              0);
-  }
+    for (int t = 0; t < kRounds; ++t) {
+      const int c = min(tid + kHThreads * t, NCp - 1);
+      xr[t] = Act<half_t>::load(x + (unsigned)((g0 + c / kChunksPerGroup) * kGroup +
+                                               chunk_base(c % kChunksPerGroup)),
+                                0);
+    }
+  };
+  xload(0, G0);
 
   // ---- scales and offsets of a tile: thread tid stages group tid % kSG of
   // runs tid / kSG + kRunsAtOnce * u (run = array * 16 + row; planes, then
@@ -1034,10 +1043,10 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   // (coalesced); a group or run past the end re-reads a valid value and
   // stages nothing
   const int sg = tid % kSG;
-  const int sgc = min(sg, G - 1);
   unsigned short sv[kScalePerThread];
-  auto sload = [&](int k) {
+  auto sload = [&](int k, int g0, int Gp) {
     const int tl = tile_of(k);
+    const int sgc = g0 + min(sg, Gp - 1);
 #pragma unroll
     for (int u = 0; u < kScalePerThread; ++u) {
       const int run = min(tid / kSG + kRunsAtOnce * u, kRuns - 1);
@@ -1047,12 +1056,12 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
       sv[u] = *reinterpret_cast<const unsigned short *>(src);
     }
   };
-  auto sstore = [&](int b) {
+  auto sstore = [&](int b, int Gp) {
     unsigned short *s16 = reinterpret_cast<unsigned short *>(scl[b]);
 #pragma unroll
     for (int u = 0; u < kScalePerThread; ++u) {
       const int run = tid / kSG + kRunsAtOnce * u;
-      if (run < kRuns && sg < G) s16[run * kSW * 2 + sg] = sv[u];
+      if (run < kRuns && sg < Gp) s16[run * kSW * 2 + sg] = sv[u];
     }
   };
 
@@ -1060,10 +1069,10 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   // plane it looks up (a slot past the last half group re-reads the last one
   // and adds nothing; so does a plane past P)
   uint2 wa[kSlots][PC], wb[kSlots][PC];
-  auto wfetch = [&](int k, int t, uint2 (&w)[kSlots][PC]) {
-    const int h = min(s + 64 * t, H - 1);
+  auto wfetch = [&](int k, int t, uint2 (&w)[kSlots][PC], int g0, int Gp) {
+    const int h = min(s + 64 * t, 2 * Gp - 1);
     const unsigned q =
-        (unsigned)((((size_t)tile_of(k) * G + (h >> 1)) * kTileRows + prow) * 2 + (h & 1));
+        (unsigned)((((size_t)tile_of(k) * G + g0 + (h >> 1)) * kTileRows + prow) * 2 + (h & 1));
 #pragma unroll
     for (int u = 0; u < PC; ++u) {
       const int i = RS > 1 ? min(ph * PC + u, P - 1) : u;
@@ -1076,54 +1085,57 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   // requested ahead of it queue in front of other workgroups' activation and
   // scale loads and hold every barrier back (4096x14336, p = 4: 14.7 us with
   // all slots requested first, 12.3 with one).
-  sload(0);
-  wfetch(0, 0, wa);
+  sload(0, 0, G0);
+  wfetch(0, 0, wa, 0, G0);
 
-  // ---- build the tables and group sums.  Every round computes its chunk
-  // (a past-the-end one its clamped copy) and only the stores are guarded:
-  // an activation load used only under the guard is sunk below the sign
-  // words by the compiler, and its wait then covers all of them.
+  // ---- build the tables and group sums of a pass of Gp groups.  Every round
+  // computes its chunk (a past-the-end one its clamped copy) and only the
+  // stores are guarded: an activation load used only under the guard is sunk
+  // below the sign words by the compiler, and its wait then covers all of them.
+  auto build = [&](int Gp) {
+    const int NCp = kChunksPerGroup * Gp;
 #pragma unroll
-  for (int t = 0; t < kRounds; ++t) {
-    const int c = tid + kHThreads * t;
-    const int cg = c % kChunksPerGroup;
-    float f[4];
-    Act<half_t>::cvt(xr[t], chunk_parity(cg), f);
-    float4 v[4];
-    chunk_entries(f, v);
-    uint32_t hv[8];
+    for (int t = 0; t < kRounds; ++t) {
+      const int c = tid + kHThreads * t;
+      const int cg = c % kChunksPerGroup;
+      float f[4];
+      Act<half_t>::cvt(xr[t], chunk_parity(cg), f);
+      float4 v[4];
+      chunk_entries(f, v);
+      uint32_t hv[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      hv[2 * e] = (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].x) |
-                  ((uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].y) << 16);
-      hv[2 * e + 1] = (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].z) |
-                      ((uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].w) << 16);
+      for (int e = 0; e < 4; ++e) {
+        hv[2 * e] = (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].x) |
+                    ((uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].y) << 16);
+        hv[2 * e + 1] = (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].z) |
+                        ((uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].w) << 16);
+      }
+      const float cs = sum32_lanes((f[0] + f[1]) + (f[2] + f[3]));
+      if (c < NCp) {  // whole aligned 32-lane blocks (NCp is a multiple of 32)
+        uint4 *dst = reinterpret_cast<uint4 *>(lut + (c / kChunksPerGroup) * kHGroupStride +
+                                               h_chunk_offset(cg));
+        dst[0] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+        dst[1] = make_uint4(hv[4], hv[5], hv[6], hv[7]);
+        if ((tid & 31) == 0) gsum[c / kChunksPerGroup] = cs;
+      }
     }
-    const float cs = sum32_lanes((f[0] + f[1]) + (f[2] + f[3]));
-    if (c < NC) {  // whole aligned 32-lane blocks (NC is a multiple of 32)
-      uint4 *dst = reinterpret_cast<uint4 *>(lut + (c / kChunksPerGroup) * kHGroupStride +
-                                             h_chunk_offset(cg));
-      dst[0] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-      dst[1] = make_uint4(hv[4], hv[5], hv[6], hv[7]);
-      if ((tid & 31) == 0) gsum[c / kChunksPerGroup] = cs;
-    }
-  }
-  sstore(0);
+  };
+  build(G0);
+  sstore(0, G0);
   __syncthreads();
 #pragma unroll
-  for (int t = 1; t < kSlots; ++t) wfetch(0, t, wa);
+  for (int t = 1; t < kSlots; ++t) wfetch(0, t, wa, 0, G0);
 
-  // ---- lookups of one tile from scale buffer b; returns this lane's partial
-  auto lookups = [&](int b, const uint2 (&w)[kSlots][PC]) -> float {
+  // ---- lookups of slot t in a pass of Gp groups of one tile, scales from
+  // buffer b, added to this lane's partial acc
+  auto lookup_slot = [&](int b, const uint2 (&w)[kSlots][PC], int Gp, int t, float acc) -> float {
     const unsigned short *s16 = reinterpret_cast<const unsigned short *>(scl[b]);
     auto scale = [&](int a, int j) -> float {
       return (float)__builtin_bit_cast(half_t, s16[((a * kTileRows + prow) * kSW) * 2 + j]);
     };
-    float acc = 0.f;
-#pragma unroll
-    for (int t = 0; t < kSlots; ++t) {
+    {
       const int h = s + 64 * t;
-      if (h < H) {
+      if (h < 2 * Gp) {
         const int j = h >> 1, half = h & 1;
         const uint32_t base = lds_addr(lut + j * kHGroupStride + h_chunk_offset(16 * half));
 #pragma unroll
@@ -1136,8 +1148,17 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
         if (half == 0 && (RS == 1 || ph == 0)) acc = fmaf(scale(P, j), gsum[j], acc);
       }
     }
-    // the 64 slot partials of each row, reduced in a fixed order; then the
-    // plane parts, lanes r, r + 16/RS, .. of the 16-lane row (DPP row_ror)
+    return acc;
+  };
+  auto lookups = [&](int b, const uint2 (&w)[kSlots][PC], int Gp) -> float {
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < kSlots; ++t) acc = lookup_slot(b, w, Gp, t, acc);
+    return acc;
+  };
+  // the 64 slot partials of each row, reduced in a fixed order; then the
+  // plane parts, lanes r, r + 16/RS, .. of the 16-lane row (DPP row_ror)
+  auto reduce_rows = [&](float acc) -> float {
     acc = sum_rows4(acc, (lane ^ 32) << 2);
     if constexpr (RS == 4)
       acc += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, acc), 0x124,
@@ -1171,7 +1192,32 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   };
 
   if constexpr (NB == 1) {
-    const float acc = lookups(0, wa);
+    float acc;
+    if constexpr (MP) {
+      // two passes (NG < G <= 2 NG), straight-line: the second pass's
+      // activations and scales are requested as the first starts, and each
+      // slot's sign words for it as soon as the slot has been looked up (one
+      // register set).  (As a loop over passes the compiler's waits for these
+      // loop-carried loads degraded to full drains.)
+      const int G1 = G - NG;
+      xload(NG, G1);
+      sload(0, NG, G1);
+      acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < kSlots; ++t) {
+        acc = lookup_slot(0, wa, NG, t, acc);
+        wfetch(0, t, wa, NG, G1);
+      }
+      __syncthreads();  // every lookup of the first pass done: tables and scales free
+      sstore(0, G1);    // first, so its registers are free during the build
+      build(G1);
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < kSlots; ++t) acc = lookup_slot(0, wa, G1, t, acc);
+    } else {
+      acc = lookups(0, wa, G0);
+    }
+    acc = reduce_rows(acc);
     if (lane < 16) part[0][wave][lane] = acc;
     __syncthreads();
     finish(0, 0);
@@ -1182,12 +1228,12 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
     // barrier before tile k's rows are summed
     auto step = [&](int k, const uint2 (&wc)[kSlots][PC], uint2 (&wn)[kSlots][PC]) {
       const int b = k & 1;
-      sload(k + 1);
+      sload(k + 1, 0, G);
 #pragma unroll
-      for (int t = 0; t < kSlots; ++t) wfetch(k + 1, t, wn);
-      const float acc = lookups(b, wc);
+      for (int t = 0; t < kSlots; ++t) wfetch(k + 1, t, wn, 0, G);
+      const float acc = reduce_rows(lookups(b, wc, G));
       if (lane < 16) part[b][wave][lane] = acc;
-      sstore(b ^ 1);
+      sstore(b ^ 1, G);
       __syncthreads();
       finish(k, b);
     };
@@ -1323,9 +1369,40 @@ void gemv_h16_tiles(hipStream_t s, const uint4 *b4, const half_t *a, const half_
                      xx, yy, M, G, MT);
 }
 
+// K past 112 groups, up to 224: one tile per workgroup (rows split when few
+// tiles), K walked in two passes of at most 112 groups.
+template <int P, bool GU>
+void gemv_h16_passes(hipStream_t s, const uint4 *b4, const half_t *a, const half_t *z,
+                     const half_t *xx, half_t *yy, int M, int G, int MT) {
+  const int cus = compute_units();
+  if constexpr (!GU) {
+    if (4 * MT <= cus) {
+      hipLaunchKernelGGL((gemv_h16_kernel<P, GU, kHMaxG, 1, 4, true>), dim3(4 * MT), dim3(kHThreads),
+                         0, s, b4, a, z, xx, yy, M, G, MT);
+      return;
+    }
+    if (2 * MT <= cus) {
+      hipLaunchKernelGGL((gemv_h16_kernel<P, GU, kHMaxG, 1, 2, true>), dim3(2 * MT), dim3(kHThreads),
+                         0, s, b4, a, z, xx, yy, M, G, MT);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((gemv_h16_kernel<P, GU, kHMaxG, 1, 1, true>), dim3(MT), dim3(kHThreads), 0, s,
+                     b4, a, z, xx, yy, M, G, MT);
+}
+
 template <bool GU>
 void gemv_h16_launch(hipStream_t s, const uint4 *b4, const half_t *a, const half_t *z,
                      const half_t *xx, half_t *yy, int M, int G, int MT, int p) {
+  if (G > kHMaxG) {  // the caller routes at most 2 * kHMaxG groups here
+    switch (p) {
+      case 1: gemv_h16_passes<1, GU>(s, b4, a, z, xx, yy, M, G, MT); break;
+      case 2: gemv_h16_passes<2, GU>(s, b4, a, z, xx, yy, M, G, MT); break;
+      case 3: gemv_h16_passes<3, GU>(s, b4, a, z, xx, yy, M, G, MT); break;
+      default: gemv_h16_passes<4, GU>(s, b4, a, z, xx, yy, M, G, MT); break;
+    }
+    return;
+  }
   if (G <= 64) {
     switch (p) {
       case 1: gemv_h16_tiles<1, GU, 64>(s, b4, a, z, xx, yy, M, G, MT); break;
@@ -1343,12 +1420,15 @@ void gemv_h16_launch(hipStream_t s, const uint4 *b4, const half_t *a, const half
   }
 }
 
-// Batch 1, fp16, 4096 < K <= 14336: resident fp16 tables (gemv_h16_kernel)
-// or streamed fp32 windows (gemv_stream*_kernel).  Measured same-run at
-// p = 2..4 over 16 shapes from 256x12288 to 28672x8192 (K = 4224 to 14336),
-// the resident tables won everywhere: by 4-30% with few row tiles and by up
-// to 2x with many (28672x5120, p = 2: 16.9 against 33.6 us).  BCQ_H16=0
-// forces the stream (A/B runs and tests); BCQ_H16=1 the resident tables.
+// Batch 1, fp16, 4096 < K <= 28672: resident fp16 tables (gemv_h16_kernel,
+// in two passes past K = 14336) or streamed fp32 windows (gemv_stream*_kernel).
+// Measured same-run at p = 2..4 over 16 shapes from 256x12288 to 28672x8192
+// (K = 4224 to 14336), the resident tables won everywhere: by 4-30% with few
+// row tiles and by up to 2x with many (28672x5120, p = 2: 16.9 against 33.6
+// us); in two passes over six shapes with K = 16384 to 28672, by 3-44%
+// (4096x28672: 14.9 / 18.6 / 22.0 against 20.1 / 23.4 / 23.9 us at
+// p = 2 / 3 / 4).  BCQ_H16=0 forces the stream (A/B runs and tests); BCQ_H16=1
+// the resident tables.
 bool gemv_h16_route(int G, int p) {
   (void)G;
   (void)p;
@@ -1376,9 +1456,9 @@ hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *
     return hipGetLastError();
   }
   if constexpr (sizeof(T) == 2) {
-    // fp16 with K <= 14336: tables of all of K resident as fp16 where that
-    // measured faster (gemv_h16_route)
-    if (G <= kHMaxG && gemv_h16_route(G, p)) {
+    // fp16: tables resident as fp16, of all of K up to K = 14336 and in two
+    // passes up to K = 28672 (gemv_h16_route)
+    if (G <= 2 * kHMaxG && gemv_h16_route(G, p)) {
       gemv_h16_launch<GU>(s, b4, a, z, xx, yy, M, G, MT, p);
       return hipGetLastError();
     }

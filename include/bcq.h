@@ -33,7 +33,7 @@
  *    Two fp16 routes also round an intermediate once to fp16, each adding at
  *    most 2^-11 of an output's term magnitude sum_k |w_k x_k| to its error:
  *    the summed decode of the matrix cores (see bcq_gemm_skinny), and the
- *    batch-1 tables for 4096 < K <= 14336, whose entries (sums of four
+ *    batch-1 tables for 4096 < K <= 28672, whose entries (sums of four
  *    signed activations, formed in fp32) are held in fp16.
  *  - Shapes: K must be a positive multiple of 128 (group_size must be 128),
  *    M >= 1, 1 <= p <= planes <= 4.

@@ -846,10 +846,15 @@ class h16_route:
     (6000, 12416, 4),   # 97 groups at p = 4: one tile per workgroup, 375 workgroups
     (1500, 6144, 3),    # 94 tiles: rows split over two workgroups, ragged rows
     (1024, 8192, 4),    # 64 tiles: rows split over four workgroups
+    (300, 16384, 4),    # 128 groups: two passes over K (the second of 16 groups), rows split
+    (2000, 28672, 3),   # 224 groups: two full passes, rows split over two workgroups
+    (5003, 20480, 4),   # 160 groups: two passes, one tile per workgroup, ragged rows
+    (64, 43008, 2),     # 336 groups: past two passes, streamed on either route
 ])
 @pytest.mark.parametrize("route", ["1", "0"])
 def test_fp16_tables_and_streamed_windows(M, K, P, route):
-    """Both batch-1 routes for fp16 K past 4096, forced, every output at every
+    """Both batch-1 routes for fp16 K past 4096 (the resident tables in passes
+    of 112 groups past K = 14336), forced, every output at every
     precision: relative L2 within the fp16 bar, and every output within the
     a-priori bound of its arithmetic. The resident route rounds each table
     entry (a sum of four signed activations) once to fp16, which adds at
@@ -877,6 +882,7 @@ def test_fp16_tables_and_streamed_windows(M, K, P, route):
     (40, 8320, 3),
     (3000, 8192, 2),    # 375 tiles: workgroups walk one or two
     (2504, 10240, 3),   # 313 tiles at 80 groups
+    (1000, 16384, 3),   # 128 groups: two passes over K
 ])
 def test_gate_up_fp16_tables(Mo, K, P):
     """The gated-MLP epilogue on the resident fp16-table route (forced, every
