@@ -568,7 +568,9 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
 
 // ------------------------------------------------ batch 1, K past the resident tables
 //
-// For K > 4096 the tables of all of K do not fit in LDS, so a workgroup (one
+// For fp32 stores with K > 4096 (and fp16 ones past K = 28672, or with the
+// resident fp16 tables switched off) the fp32 tables of all of K do not fit in
+// LDS, so a workgroup (one
 // 16-row tile, 512 lanes, the lane mapping of gemv_res_kernel) streams K in
 // windows of 16 groups with two table buffers and one barrier per window:
 // after the barrier it builds window w+1's tables (one chunk per lane) and
@@ -896,14 +898,15 @@ __global__ __launch_bounds__(2 * kRThreads) void gemv_stream2_kernel(
   }
 }
 
-// ------------------------------------------------ batch 1, fp16 tables for K up to 14336
+// ------------------------------------------------ batch 1, fp16 tables for K up to 28672
 //
 // For fp16 stores with 4096 < K <= 14336 the tables of all of K fit in LDS
 // when each entry is held in fp16 (32 bytes per chunk; 126 KB of tables at
 // K = 14336), so a workgroup builds them once, behind one barrier, instead of
 // streaming windows through two buffers with a barrier each, and with more
 // row tiles than compute units walks several tiles with them (gemv_h16_route
-// has the measurements).  An entry is the fp32 sum of its four signed
+// has the measurements); up to K = 28672 it takes K in two passes of at most
+// 14336 columns.  An entry is the fp32 sum of its four signed
 // activations rounded once to fp16 (relative error at most 2^-11 of the
 // entry); lookups are summed in fp32.
 //
