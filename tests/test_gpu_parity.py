@@ -898,6 +898,38 @@ def test_gate_up_fp16_tables(Mo, K, P):
         assert rel_l2(y.cpu().numpy(), ref) <= 2e-3, (Mo, K, p)
 
 
+def test_random_shapes_fp16_resident_tables():
+    """24 seeded random fp16 batch-1 problems across the boundaries of the
+    resident fp16-table kernel (64 and 112 groups, one and two passes over K,
+    tile rows split over 2 or 4 workgroups, one and several tiles per
+    workgroup), on the default route: every sampled output within the a-priori
+    bound of its arithmetic (fp32 sums, fp16 table entries), and the sampled
+    rows' relative L2 within the fp16 bar."""
+    rng = np.random.default_rng(20261204)
+    for case in range(24):
+        M = int(rng.choice([1, 15, 17, 300, 1500, 2050, 4100, 8195]))
+        G = int(rng.choice([33, 63, 64, 65, 100, 112, 113, 150, 224]))
+        K = 128 * G
+        if M * K > 120_000_000:  # keep the inputs to a second or so
+            M = 4100
+        P = int(rng.integers(1, 5))
+        p = int(rng.integers(1, P + 1))
+        w = bcq_synth.make(M, K, P, seed=case + 2000, outlier_frac=0.01)
+        st = store_of(w)
+        rows = sample_rows(M, 64, seed=case)
+        say("random fp16 resident", case, M, K, P, p)
+        y = torch.empty(M, dtype=torch.float16, device="cuda")
+        bcq.bcq_gemv(st, p, dev(w.x[0]), y)
+        got = y.cpu().numpy().astype(np.float64)[rows]
+        ref = np.asarray(oracle_y(w, w.x[:1], [p], rows))[0]
+        mag = magnitudes(w, w.x[:1], [p], rows)[0]
+        c = (K / 4 + 16) * 2.0 ** -24 + 2.0 ** -11
+        bound = 1.01 * (c * mag + 2.0 ** -11 * np.abs(ref)) + 1e-30
+        assert np.all(np.abs(got - ref) <= bound), (case, M, K, P, p)
+        if len(rows) >= 16:
+            assert rel_l2(got, ref) <= 2e-3, (case, M, K, P, p)
+
+
 # ---------------------------------------------------------------- gated-MLP epilogue
 
 @pytest.mark.parametrize("Mo,K,P,dt", [
