@@ -922,8 +922,6 @@ constexpr int kHMaxG = 112;  // groups resident: K <= 14336
 constexpr int kHChunkBytes = 2 * kEntries;
 constexpr int kHHalfPad = 64;
 constexpr int kHGroupStride = kChunksPerGroup * kHChunkBytes + kHHalfPad + 64;  // 1152
-constexpr int kHMaxChunkRounds = (kHMaxG * kChunksPerGroup + kHThreads - 1) / kHThreads;  // 4
-constexpr int kHScaleWords = kHMaxG / 2 + 1;  // staged scale row, 32-bit words (odd)
 
 __device__ __forceinline__ int h_chunk_offset(int c) {
   return c * kHChunkBytes + (c >= 16 ? kHHalfPad : 0);
