@@ -412,19 +412,20 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   uint2 tiles[2][P];
   const int js = min(win * kG1Ksub + gw, G - 1);
   const unsigned lq = (unsigned)((js * kTileRows + (RS > 1 ? prow : r)) * 2 + half);
-  auto fetch = [&](int k, uint2 (&o)[P]) {
+  // planes [u0, u1) of tile k (of the lane's PC planes with RS > 1)
+  auto fetch = [&](int k, uint2 (&o)[P], int u0 = 0, int u1 = P) {
     if constexpr (RS > 1) {
       const uint2 *tb = bits2 + (size_t)((int)blockIdx.x / RS) * G * (kTileRows * 2);
 #pragma unroll
       for (int u = 0; u < PC; ++u)
-        o[u] = tb[(size_t)min(ph * PC + u, P - 1) * plane_stride * 2 + lq];
+        if (u >= u0 && u < u1) o[u] = tb[(size_t)min(ph * PC + u, P - 1) * plane_stride * 2 + lq];
     } else {
       const int t = (int)blockIdx.x + min(k, nt - 1) * (int)gridDim.x;
       const uint2 *tb = bits2 + (size_t)t * G * (kTileRows * 2);
 #pragma unroll
       for (int i = 0; i < P; ++i) {
         const uint2 *pb = tb + (size_t)i * plane_stride * 2;
-        o[i] = pb[lq];
+        if (i >= u0 && i < u1) o[i] = pb[lq];
       }
     }
   };
@@ -437,9 +438,15 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   // and without it their small loads queue behind the early ones' bulk
   // (measured 4096x4096: 5.60 -> 5.31 us at p = 4; 8192x4096: 7.72 -> 7.35;
   // 14336x4096 within noise).  No sleep at all and requesting the sign words
-  // only after the table barrier were both slower.
+  // only after the table barrier were both slower.  With one tile and at
+  // least three planes, only the first half of the planes goes before the
+  // barrier and the rest right after it (4096x4096: p = 3 4.72 -> 4.54 us,
+  // p = 4 5.52 -> 5.28; at p = 2 and with several tiles per workgroup the
+  // split was 2-11% slower).
+  constexpr bool kSplitFirst = TMAX == 1 && RS == 1 && P >= 3;
+  constexpr int kFirstPlanes = kSplitFirst ? (P + 1) / 2 : PC;
   __builtin_amdgcn_s_sleep(12);
-  fetch(0, tiles[0]);
+  fetch(0, tiles[0], 0, kFirstPlanes);
 
   // ---- build the tables and group sums
   {
@@ -474,6 +481,7 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
     }
   }
   __syncthreads();
+  if (kSplitFirst) fetch(0, tiles[0], kFirstPlanes, PC);
   if (TMAX > 1) fetch(1, tiles[1]);
 
   const int j = win * kG1Ksub + gw;
