@@ -1093,9 +1093,18 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   // table barrier.  The barrier waits for the activations; sign words
   // requested ahead of it queue in front of other workgroups' activation and
   // scale loads and hold every barrier back (4096x14336, p = 4: 14.7 us with
-  // all slots requested first, 12.3 with one).
+  // all slots requested first, 12.3 with one).  Where a lane's slot carries
+  // fewer planes (rows split four ways) two slots go first; with the
+  // 64-group tables and one tile per workgroup a short sleep precedes them,
+  // as in gemv_res_kernel (same-process A/B, six repeats: 1024x14336 p = 4
+  // 7.75 -> 7.02 us, 4096x8192 8.14 -> 7.74, 4096x6144 6.89 -> 6.58; both
+  // were within 1% or slower elsewhere).
+  constexpr int kBefore = RS == 4 ? 2 : 1;
   sload(0, 0, G0);
-  wfetch(0, 0, wa, 0, G0);
+  if constexpr (NG == 64 && NB == 1 && RS == 1) __builtin_amdgcn_s_sleep(12);
+#pragma unroll
+  for (int t = 0; t < kSlots; ++t)
+    if (t < kBefore) wfetch(0, t, wa, 0, G0);
 
   // ---- build the tables and group sums of a pass of Gp groups.  Every round
   // computes its chunk (a past-the-end one its clamped copy) and only the
@@ -1133,7 +1142,7 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   sstore(0, G0);
   __syncthreads();
 #pragma unroll
-  for (int t = 1; t < kSlots; ++t) wfetch(0, t, wa, 0, G0);
+  for (int t = kBefore; t < kSlots; ++t) wfetch(0, t, wa, 0, G0);
 
   // ---- lookups of slot t in a pass of Gp groups of one tile, scales from
   // buffer b, added to this lane's partial acc
