@@ -618,7 +618,8 @@ def test_fp32_large_batch_uses_exact_tables():
 
 def test_graph_replays_match_eager():
     """Every product kernel captured in one HIP graph (batch 1 whole-K,
-    resident fp16 tables (one and several tiles per workgroup) and streamed,
+    resident fp16 tables (one and several tiles per workgroup, two passes)
+    and streamed,
     whole-K and split matrix cores with their finalize, tables for
     fp16 batch 2, per-request precision), replayed three times with new
     activations written eagerly between replays; each replay must equal the
@@ -626,8 +627,8 @@ def test_graph_replays_match_eager():
     import bench
 
     cases = []
-    for M, K, b in [(3200, 2304, 1), (64, 8320, 1), (5000, 8192, 1), (3200, 2304, 8),
-                    (3200, 2304, 32), (256, 8320, 2)]:
+    for M, K, b in [(3200, 2304, 1), (64, 8320, 1), (5000, 8192, 1), (300, 16384, 1),
+                    (3200, 2304, 8), (3200, 2304, 32), (256, 8320, 2)]:
         w = bcq_synth.make(M, K, 4, b=b, dtype=np.float16, seed=M + K + b,
                            p_choices=(2, 3, 4))
         st = store_of(w)
@@ -643,8 +644,8 @@ def test_graph_replays_match_eager():
         for (w, st, X, Yg, Ym, ws), y4 in zip(cases, Y4):
             if w.b == 1:
                 # p = 3 and p = 4: past K = 4096 the resident fp16 tables
-                # (5000 rows: workgroups walking two tiles) and the
-                # streamed windows
+                # (5000 rows: workgroups walking two tiles; K = 16384: two
+                # passes) and the streamed windows
                 bcq.bcq_gemv(st, 3, X[0], Yg[0])
                 with h16_route("0"):
                     bcq.bcq_gemv(st, 4, X[0], y4)
