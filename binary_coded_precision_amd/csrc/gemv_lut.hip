@@ -1093,13 +1093,15 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   // table barrier.  The barrier waits for the activations; sign words
   // requested ahead of it queue in front of other workgroups' activation and
   // scale loads and hold every barrier back (4096x14336, p = 4: 14.7 us with
-  // all slots requested first, 12.3 with one).  Where a lane's slot carries
-  // fewer planes (rows split four ways) two slots go first; with the
-  // 64-group tables and one tile per workgroup a short sleep precedes them,
-  // as in gemv_res_kernel (same-process A/B, six repeats: 1024x14336 p = 4
-  // 7.75 -> 7.02 us, 4096x8192 8.14 -> 7.74, 4096x6144 6.89 -> 6.58; both
-  // were within 1% or slower elsewhere).
-  constexpr int kBefore = RS == 4 ? 2 : 1;
+  // all slots requested first, 12.3 with one).  Two slots go first where a
+  // slot carries few sign words (at most two planes per lane with the
+  // 112-group tables, rows split four ways) and when a workgroup walks
+  // several tiles; with the 64-group tables and one tile per workgroup a
+  // short sleep precedes the first slot's words, as in gemv_res_kernel
+  // (same-process A/B, six repeats: 1024x14336 p = 4 7.75 -> 7.02 us,
+  // 4096x14336 p = 2 9.01 -> 8.59, 14336x8192 p = 3 18.62 -> 18.30,
+  // 4096x8192 p = 4 8.14 -> 7.74; within 1% or slower elsewhere).
+  constexpr int kBefore = (RS == 4 || NB == 2 || (NG == 112 && PC <= 2)) ? 2 : 1;
   sload(0, 0, G0);
   if constexpr (NG == 64 && NB == 1 && RS == 1) __builtin_amdgcn_s_sleep(12);
 #pragma unroll
