@@ -1122,13 +1122,13 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
       Act<half_t>::cvt(xr[t], chunk_parity(cg), f);
       float4 v[4];
       chunk_entries(f, v);
+      // entries rounded to fp16 in pairs (one packed conversion each)
+      typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
       uint32_t hv[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        hv[2 * e] = (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].x) |
-                    ((uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].y) << 16);
-        hv[2 * e + 1] = (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].z) |
-                        ((uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v[e].w) << 16);
+        hv[2 * e] = __builtin_bit_cast(uint32_t, h2_t{(_Float16)v[e].x, (_Float16)v[e].y});
+        hv[2 * e + 1] = __builtin_bit_cast(uint32_t, h2_t{(_Float16)v[e].z, (_Float16)v[e].w});
       }
       const float cs = sum32_lanes((f[0] + f[1]) + (f[2] + f[3]));
       if (c < NCp) {  // whole aligned 32-lane blocks (NCp is a multiple of 32)
