@@ -574,6 +574,140 @@ __global__ __launch_bounds__(kRThreads * NW) void gemv_res_kernel(
   }
 }
 
+// ------------------------------------------------ batch 1, direct add/subtract
+//
+// The pages name two ways to form B_i x ("AnyBCQ paper notes", direct
+// bit-plane kernel): adding and subtracting the activations under each sign
+// bit, or looking up sums of sign combinations (the tables above).  This is
+// the direct form, for fp16 stores with K <= 4096, in the lane mapping of
+// gemv_res_kernel (lane (r, hs): row r, 64 columns of half-group hs; one
+// 16-row tile per workgroup) with no tables: each lane loads its 64
+// activations as 32 fp16 pairs, turns each plane's sign bits into +-|alpha|
+// fp16 pairs (the sign of alpha folded into the bits; one 64-bit shift serves
+// the same pair of both 32-column words, as in the matrix-core decode) and
+// adds alpha * (x_2t, x_2t+1) per pair with one v_dot2_f32_f16 (fp16
+// products are exact in fp32; the sum is fp32).  The offset term is the same
+// instruction with (z, z) pairs.  So a weight bit costs 1.25 vector
+// instructions, against about 0.6 for a table lookup, but nothing waits for
+// tables: the barrier only publishes the staged scales, which are requested
+// first.  Selected with BCQ_B1_DIRECT=1 (measured against the tables).
+template <int P>
+__global__ __launch_bounds__(kRThreads * 2) void gemv_direct_kernel(
+    const uint4 *__restrict__ bits, const half_t *__restrict__ alpha,
+    const half_t *__restrict__ zero, const half_t *__restrict__ x, half_t *__restrict__ y, int M,
+    int G, int MT) {
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  constexpr int NW = 2;
+  constexpr int kMaxG = NW * kG1Ksub;  // 32 groups: K <= 4096
+  constexpr int kThreads = kRThreads * NW;
+  constexpr int kWaves = kThreads / 64;
+  constexpr int kPos = kTileRows * kMaxG;  // staging positions of one array
+  constexpr int kParts = kThreads / kPos;  // thread sets sharing the arrays
+  constexpr int kPerThread = (P + 1 + kParts - 1) / kParts;
+  // staged scales and offsets as fp16 bits, [array][row][group], rows padded
+  // to an odd number of words
+  __shared__ unsigned short scl[P + 1][kTileRows][kMaxG + 2];
+  __shared__ float part[kWaves][kTileRows];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int win = wave / kRWaves;
+  const int r = lane & 15;
+  const int hs = (wave % kRWaves) * 4 + (lane >> 4);  // half-group slot 0..31 of window win
+  const int j = win * kG1Ksub + (hs >> 1);             // group of this lane
+  const int half = hs & 1;
+  const int jc = min(j, G - 1);  // a group past G reads the last one and adds nothing
+  const int tile = blockIdx.x;
+  const size_t plane_stride = (size_t)MT * G * kTileRows;  // in uint4
+  const size_t MG = (size_t)M * G;
+  const uint2 *bits2 = reinterpret_cast<const uint2 *>(bits);
+
+  // ---- scales and offsets first (the barrier waits for them only): thread
+  // (row, group) = ((tid % kPos) / kMaxG, tid % kMaxG) of part tid / kPos
+  // loads arrays spart, spart + kParts, ...; consecutive threads read
+  // consecutive groups of a row
+  const int spart = tid / kPos;
+  const int srow = (tid % kPos) / kMaxG;
+  const int sg = tid % kMaxG;
+  const int srowc = min(tile * kTileRows + srow, M - 1);
+  uint32_t sv[kPerThread];
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int a = min(u * kParts + spart, P);
+    sv[u] = load_raw((a < P ? alpha + (size_t)a * MG : zero) + (size_t)srowc * G + min(sg, G - 1));
+  }
+
+  // ---- this lane's 64 activations (32 fp16 pairs), then its sign words
+  // (kept as 32 plain words: component indexing into an array of vector
+  // registers read the wrong component)
+  uint32_t xw[32];
+  const half_t *xl = x + (unsigned)(jc * kGroup + half * 64);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const act_u32x4 v = *reinterpret_cast<const act_u32x4 *>(xl + 8 * u);
+    xw[4 * u] = v.x;
+    xw[4 * u + 1] = v.y;
+    xw[4 * u + 2] = v.z;
+    xw[4 * u + 3] = v.w;
+  }
+  uint2 w[P];
+  const unsigned lq = (unsigned)(((tile * G + jc) * kTileRows + r) * 2 + half);
+#pragma unroll
+  for (int i = 0; i < P; ++i) w[i] = bits2[(size_t)i * plane_stride * 2 + lq];
+
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int a = u * kParts + spart;
+    if (a <= P && sg < G) scl[a][srow][sg] = (unsigned short)sv[u];
+  }
+  __syncthreads();
+
+  float acc = 0.f;
+  if (j < G) {
+    auto xp = [&](int q) -> h2_t { return __builtin_bit_cast(h2_t, xw[q]); };
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const uint32_t a16 = scl[i][r][j];
+      const uint32_t neg = (uint32_t)((int32_t)(a16 << 16) >> 31);
+      const uint32_t mag = (a16 & 0x7FFFu) * 0x10001u;
+      // a set bit (+1) gives +|alpha| when alpha >= 0: invert the word, so
+      // that the sign bit placed in the fp16 sign position is clear
+      const uint64_t wd = (uint64_t)(~(w[i].y ^ neg)) << 32 | (uint32_t)(~(w[i].x ^ neg));
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        int sh = 15 - t;
+        asm("" : "+s"(sh));  // one 64-bit shift for both words (see the decode in gemm_mfma.hip)
+        const uint64_t m = wd << sh;
+        const uint32_t lo = ((uint32_t)m & 0x80008000u) | mag;
+        const uint32_t hi = ((uint32_t)(m >> 32) & 0x80008000u) | mag;
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, lo), xp(t), acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, hi), xp(16 + t), acc, false);
+      }
+    }
+    const uint32_t z2 = (uint32_t)scl[P][r][j] * 0x10001u;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, z2), xp(q), acc, false);
+  }
+
+  // ---- the 64 slot partials of each row, then the wavefronts, fixed order
+  acc = sum_rows4(acc, (lane ^ 32) << 2);
+  if (lane < 16) part[wave][lane] = acc;
+  __syncthreads();
+  if (tid < kTileRows) {
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) sum += part[v][tid];
+    const int mm = tile * kTileRows + tid;
+    if (mm < M) y[mm] = (half_t)sum;
+  }
+}
+
+bool gemv_direct_route() {
+  const char *e = getenv("BCQ_B1_DIRECT");
+  return e != nullptr && e[0] == '1';
+}
+
 // ------------------------------------------------ batch 1, K past the resident tables
 //
 // For fp32 stores with K > 4096 (and fp16 ones past K = 28672, or with the
@@ -1470,6 +1604,29 @@ hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *
   if (nwin <= 1) {
     gemv_res_tiles<T, 1, GU>(s, b4, a, z, xx, yy, M, G, MT, p);
     return hipGetLastError();
+  }
+  if constexpr (sizeof(T) == 2 && !GU) {
+    if (nwin <= 2 && gemv_direct_route()) {  // direct add/subtract, measured against the tables
+      switch (p) {
+        case 1:
+          hipLaunchKernelGGL(gemv_direct_kernel<1>, dim3(MT), dim3(2 * kRThreads), 0, s, b4, a, z, xx,
+                             yy, M, G, MT);
+          break;
+        case 2:
+          hipLaunchKernelGGL(gemv_direct_kernel<2>, dim3(MT), dim3(2 * kRThreads), 0, s, b4, a, z, xx,
+                             yy, M, G, MT);
+          break;
+        case 3:
+          hipLaunchKernelGGL(gemv_direct_kernel<3>, dim3(MT), dim3(2 * kRThreads), 0, s, b4, a, z, xx,
+                             yy, M, G, MT);
+          break;
+        default:
+          hipLaunchKernelGGL(gemv_direct_kernel<4>, dim3(MT), dim3(2 * kRThreads), 0, s, b4, a, z, xx,
+                             yy, M, G, MT);
+          break;
+      }
+      return hipGetLastError();
+    }
   }
   if (nwin <= 2) {
     gemv_res_tiles<T, 2, GU>(s, b4, a, z, xx, yy, M, G, MT, p);

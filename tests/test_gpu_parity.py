@@ -899,6 +899,50 @@ def test_gate_up_fp16_tables(Mo, K, P):
         assert rel_l2(y.cpu().numpy(), ref) <= 2e-3, (Mo, K, p)
 
 
+class b1_direct:
+    """Sets BCQ_B1_DIRECT (the batch-1 direct add/subtract kernel) for a block."""
+
+    def __enter__(self):
+        import os
+        self.old = os.environ.get("BCQ_B1_DIRECT")
+        os.environ["BCQ_B1_DIRECT"] = "1"
+
+    def __exit__(self, *exc):
+        import os
+        if self.old is None:
+            os.environ.pop("BCQ_B1_DIRECT", None)
+        else:
+            os.environ["BCQ_B1_DIRECT"] = self.old
+
+
+@pytest.mark.parametrize("M,K,P", [
+    (4096, 4096, 4),   # the q_proj workload
+    (37, 4096, 3),     # ragged rows
+    (300, 2048, 4),    # one window of groups (16), the other window's lanes idle
+    (1000, 384, 2),    # three groups
+    (16, 4224, 1),     # 33 groups: past the direct kernel, tables
+])
+def test_batch1_direct_add_subtract(M, K, P):
+    """The batch-1 direct add/subtract kernel (fp16, K <= 4096; forced), every
+    output at every precision against the oracle: relative L2 within the fp16
+    bar and every output within the a-priori bound of fp32 accumulation."""
+    w = bcq_synth.make(M, K, P, seed=M + K + 7 * P, outlier_frac=0.01)
+    st = store_of(w)
+    rows = np.arange(M) if M <= 1000 else sample_rows(M, 512, seed=K)
+    for p in range(1, P + 1):
+        say("direct", M, K, P, p)
+        y = torch.empty(M, dtype=torch.float16, device="cuda")
+        with b1_direct():
+            bcq.bcq_gemv(st, p, dev(w.x[0]), y)
+        got = y.cpu().numpy().astype(np.float64)
+        ref = oracle_y_all(w, w.x[:1], [p])[0]
+        assert rel_l2(got, ref) <= 2e-3, (M, K, p)
+        mag = magnitudes(w, w.x[:1], [p], rows)[0]
+        c = (K / 4 + 16) * 2.0 ** -24
+        bound = 1.01 * (c * mag + 2.0 ** -11 * np.abs(ref[rows])) + 1e-30
+        assert np.all(np.abs(got[rows] - ref[rows]) <= bound), (M, K, p)
+
+
 def test_random_shapes_fp16_resident_tables():
     """24 seeded random fp16 batch-1 problems across the boundaries of the
     resident fp16-table kernel (64 and 112 groups, one and two passes over K,
