@@ -18,12 +18,15 @@
 //  * Scales fuse at the group boundary: acc += alpha_i * P_i after the 32
 //    lookups of a group, and acc += z * S_j with S_j the group's activation sum
 //    (asymmetric BCQ offset, AnyBCQ paper notes, "Training strategy").
-//  * Batch 1 (gemv_res_kernel, gemv_stream_kernel): a 512-lane workgroup owns
-//    16-row tiles; lane (r, hs) takes row r and half-group slot hs of a
-//    16-group window of tables (64 columns, two packed words per plane).
-//    K <= 4096 keeps the tables of all of K resident while the workgroup walks
-//    several tiles; larger K streams windows of tables through two buffers
-//    (with two or more planes, 1024 lanes split the planes of each window).
+//  * Batch 1 (gemv_res_kernel, gemv_h16_kernel, gemv_stream_kernel): a
+//    workgroup owns 16-row tiles; lane (r, hs) takes row r and half-group slot
+//    hs of a 16-group window of tables (64 columns, two packed words per
+//    plane).  K <= 4096 keeps the fp32 tables of all of K resident while the
+//    workgroup walks several tiles; fp16 stores up to K = 28672 keep fp16
+//    tables resident (in two passes past K = 14336); other K stream windows of
+//    tables through two buffers (with two or more planes, 1024 lanes split the
+//    planes of each window).  gemv_direct_kernel is the table-free form, kept
+//    behind a switch for comparison.
 //  * LDS banks.  Table c sits at 80-byte stride (16 entries + 16 B pad) so that
 //    the 16-byte writes of 16 consecutive chunks cover distinct banks, and the
 //    four slots of a wavefront read disjoint quarters of the 64 banks.
