@@ -1108,7 +1108,8 @@ __device__ __forceinline__ float h_half_sum(const uint2 bw, uint32_t base) {
   return (s[0] + s[1]) + (s[2] + s[3]);
 }
 
-// NG: groups of K the tables hold (64: K <= 8192, 112: K <= 14336).
+// NG: groups of K the tables hold (32: K <= 4096, 64: K <= 8192, 112: K <=
+// 14336).
 // NB = 1: one tile per workgroup (grid = row tiles).  NB = 2: the workgroup
 // walks tiles blockIdx.x + k * gridDim.x with the tables built once; the next
 // tile's scales are staged into the other of two buffers during the current
@@ -1212,17 +1213,18 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   };
 
   // ---- sign words of this lane's half groups in a tile, one uint2 per
-  // plane it looks up (a slot past the last half group re-reads the last one
-  // and adds nothing; so does a plane past P)
+  // plane it looks up, planes [u0, u1) of slot t (a slot past the last half
+  // group re-reads the last one and adds nothing; so does a plane past P)
   uint2 wa[kSlots][PC], wb[kSlots][PC];
-  auto wfetch = [&](int k, int t, uint2 (&w)[kSlots][PC], int g0, int Gp) {
+  auto wfetch = [&](int k, int t, uint2 (&w)[kSlots][PC], int g0, int Gp, int u0 = 0,
+                    int u1 = P) {
     const int h = min(s + 64 * t, 2 * Gp - 1);
     const unsigned q =
         (unsigned)((((size_t)tile_of(k) * G + g0 + (h >> 1)) * kTileRows + prow) * 2 + (h & 1));
 #pragma unroll
     for (int u = 0; u < PC; ++u) {
       const int i = RS > 1 ? min(ph * PC + u, P - 1) : u;
-      w[t][u] = bits2[(size_t)i * plane_stride * 2 + q];
+      if (u >= u0 && u < u1) w[t][u] = bits2[(size_t)i * plane_stride * 2 + q];
     }
   };
 
@@ -1238,12 +1240,17 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   // (same-process A/B, six repeats: 1024x14336 p = 4 7.75 -> 7.02 us,
   // 4096x14336 p = 2 9.01 -> 8.59, 14336x8192 p = 3 18.62 -> 18.30,
   // 4096x8192 p = 4 8.14 -> 7.74; within 1% or slower elsewhere).
+  // With one slot per lane (32 groups) and at least three planes, only the
+  // first half of the slot's planes goes before the barrier and the rest
+  // right after it, as in gemv_res_kernel.
   constexpr int kBefore = (RS == 4 || NB == 2 || (NG == 112 && PC <= 2)) ? 2 : 1;
+  constexpr bool kSplitPlanes = kSlots == 1 && NB == 1 && RS == 1 && P >= 3;
+  constexpr int kFirstPlanes = kSplitPlanes ? (PC + 1) / 2 : PC;
   sload(0, 0, G0);
-  if constexpr (NG == 64 && NB == 1 && RS == 1) __builtin_amdgcn_s_sleep(12);
+  if constexpr (NG <= 64 && NB == 1 && RS == 1) __builtin_amdgcn_s_sleep(12);
 #pragma unroll
   for (int t = 0; t < kSlots; ++t)
-    if (t < kBefore) wfetch(0, t, wa, 0, G0);
+    if (t < kBefore) wfetch(0, t, wa, 0, G0, 0, kFirstPlanes);
 
   // ---- build the tables and group sums of a pass of Gp groups.  Every round
   // computes its chunk (a past-the-end one its clamped copy) and only the
@@ -1282,6 +1289,7 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   __syncthreads();
 #pragma unroll
   for (int t = kBefore; t < kSlots; ++t) wfetch(0, t, wa, 0, G0);
+  if constexpr (kSplitPlanes) wfetch(0, 0, wa, 0, G0, kFirstPlanes, PC);
 
   // ---- lookups of slot t in a pass of Gp groups of one tile, scales from
   // buffer b, added to this lane's partial acc
@@ -1586,6 +1594,20 @@ void gemv_h16_launch(hipStream_t s, const uint4 *b4, const half_t *a, const half
 // (4096x28672: 14.9 / 18.6 / 22.0 against 20.1 / 23.4 / 23.9 us at
 // p = 2 / 3 / 4).  BCQ_H16=0 forces the stream (A/B runs and tests); BCQ_H16=1
 // the resident tables.
+// fp16 stores with 2048 < K <= 4096: the fp16 tables (32 groups, one slot
+// per lane, the first half of the planes requested before the table barrier)
+// against gemv_res_kernel's fp32 tables, same-process A/B, six repeats, us at
+// p = 2 / 3 / 4: 4096x4096 4.56 / 4.63 / 5.38 -> 4.23 / 4.62 / 5.13,
+// 4096x3072 4.39 / 4.39 / 5.10 -> 4.11 / 4.34 / 4.80 with one tile per
+// workgroup; with several tiles per workgroup (8192x4096 to 28672x4096) or
+// rows split over workgroups (1024x4096, 2048x4096) the fp32 tables were
+// 3-18% faster.  So the fp16 tables take exactly the launches of one tile per
+// workgroup on more than half of the compute units.
+bool gemv_h16_small_route(int MT) {
+  const int cus = compute_units();
+  return MT <= cus && 2 * MT > cus;
+}
+
 bool gemv_h16_route(int G, int p) {
   (void)G;
   (void)p;
@@ -1626,6 +1648,29 @@ hipError_t gemv_dispatch(const uint32_t *bits, int M, int K, int p, const void *
         default:
           hipLaunchKernelGGL(gemv_direct_kernel<4>, dim3(MT), dim3(2 * kRThreads), 0, s, b4, a, z, xx,
                              yy, M, G, MT);
+          break;
+      }
+      return hipGetLastError();
+    }
+    // 2048 < K <= 4096 with one row tile per workgroup and every compute unit
+    // busy: fp16 tables of all of K (gemv_h16_small_route)
+    if (nwin == 2 && gemv_h16_small_route(MT) && gemv_h16_route(G, p)) {
+      switch (p) {
+        case 1:
+          hipLaunchKernelGGL((gemv_h16_kernel<1, false, 32, 1>), dim3(MT), dim3(kHThreads), 0, s, b4,
+                             a, z, xx, yy, M, G, MT);
+          break;
+        case 2:
+          hipLaunchKernelGGL((gemv_h16_kernel<2, false, 32, 1>), dim3(MT), dim3(kHThreads), 0, s, b4,
+                             a, z, xx, yy, M, G, MT);
+          break;
+        case 3:
+          hipLaunchKernelGGL((gemv_h16_kernel<3, false, 32, 1>), dim3(MT), dim3(kHThreads), 0, s, b4,
+                             a, z, xx, yy, M, G, MT);
+          break;
+        default:
+          hipLaunchKernelGGL((gemv_h16_kernel<4, false, 32, 1>), dim3(MT), dim3(kHThreads), 0, s, b4,
+                             a, z, xx, yy, M, G, MT);
           break;
       }
       return hipGetLastError();

@@ -33,8 +33,9 @@
  *    Two fp16 routes also round an intermediate once to fp16, each adding at
  *    most 2^-11 of an output's term magnitude sum_k |w_k x_k| to its error:
  *    the summed decode of the matrix cores (see bcq_gemm_skinny), and the
- *    batch-1 tables for 4096 < K <= 28672, whose entries (sums of four
- *    signed activations, formed in fp32) are held in fp16.
+ *    batch-1 tables for 4096 < K <= 28672 (and for 2048 < K <= 4096 when
+ *    the call has 129 to 256 row tiles of 16 rows), whose entries (sums of
+ *    four signed activations, formed in fp32) are held in fp16.
  *  - Shapes: K must be a positive multiple of 128 (group_size must be 128),
  *    M >= 1, 1 <= p <= planes <= 4.
  */

@@ -91,6 +91,17 @@ def magnitudes(w, x, p_req, rows):
     return out
 
 
+def fp16_table_route(M, K, b, dt):
+    """Whether a call holds table entries in fp16 (each a sum of four signed
+    activations rounded once): fp16 batch 1 with 4096 < K <= 28672, or with
+    2048 < K <= 4096 when each of 256 compute units takes at most one of more
+    than 128 row tiles."""
+    if b != 1 or np.dtype(dt) != np.float16:
+        return False
+    G, MT = K // 128, (M + 15) // 16
+    return 32 < G <= 224 or (16 < G <= 32 and 128 < MT <= 256)
+
+
 def request_ok(got, ref, dt, K, mag=None, summed=False):
     """A request's outputs pass at the bar (relative L2), or -- with fewer than
     16 outputs, where one near-cancelling output can set the whole relative
@@ -98,7 +109,8 @@ def request_ok(got, ref, dt, K, mag=None, summed=False):
     fp32 accumulation of exact products (at most K/4 + 16 sequential
     additions, unit roundoff 2^-24) on the exact routes; on the summed fp16
     decode (launches of more than 16 requests at one precision) each decoded
-    weight is also rounded to fp16 (2^-11 of its size); plus one rounding of
+    weight, and on the fp16 batch-1 tables (fp16_table_route) each table
+    entry, is also rounded to fp16 (2^-11 of its size); plus one rounding of
     the output (2^-11 for fp16)."""
     tol = TOL[np.dtype(dt)]
     if rel_l2(got, ref) <= tol:
@@ -751,7 +763,7 @@ def test_random_shapes_every_path():
             bcq.bcq_gemm_skinny(st, p, dev(w.x), Y)
         ref = oracle_y(w, w.x, [p] * b, rows)
         check(Y.cpu().numpy()[:, rows], np.asarray(ref), (case, M, K, P, b, p), [p] * b,
-              b > 16 and dt == np.float16)
+              (b > 16 and dt == np.float16) or fp16_table_route(M, K, b, dt))
         if b > 1:
             Y = torch.empty((b, M), dtype=tdt, device="cuda")
             bcq.bcq_gemv_mixed_p(st, w.p_req, dev(w.x), Y)
@@ -851,11 +863,15 @@ class h16_route:
     (2000, 28672, 3),   # 224 groups: two full passes, rows split over two workgroups
     (5003, 20480, 4),   # 160 groups: two passes, one tile per workgroup, ragged rows
     (64, 43008, 2),     # 336 groups: past two passes, streamed on either route
+    (3000, 4096, 4),    # 32 groups, 188 tiles: one per workgroup (the fp16 tables; "0": fp32)
+    (2500, 3072, 3),    # 24 groups, 157 tiles
+    (4096, 2176, 2),    # 17 groups, 256 tiles
 ])
 @pytest.mark.parametrize("route", ["1", "0"])
 def test_fp16_tables_and_streamed_windows(M, K, P, route):
     """Both batch-1 routes for fp16 K past 4096 (the resident tables in passes
-    of 112 groups past K = 14336), forced, every output at every
+    of 112 groups past K = 14336), and for 2048 < K <= 4096 with one row tile
+    per workgroup the fp16 tables against the fp32 ones, every output at every
     precision: relative L2 within the fp16 bar, and every output within the
     a-priori bound of its arithmetic. The resident route rounds each table
     entry (a sum of four signed activations) once to fp16, which adds at
