@@ -1108,6 +1108,36 @@ __device__ __forceinline__ float h_half_sum(const uint2 bw, uint32_t base) {
   return (s[0] + s[1]) + (s[2] + s[3]);
 }
 
+// The same sum in two parts, for a software pipeline over planes: the 16
+// entries are read into registers first, then added in h_half_sum's order
+// (so the result is the same).
+__device__ __forceinline__ void h_half_read(const uint2 bw, uint32_t base, _Float16 (&e)[16]) {
+  constexpr int S = kHChunkBytes / 2;
+  const uint32_t wd[2] = {bw.x, bw.y};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t ev = (wd[q] << 1) & 0x1E1E1E1Eu;
+    const uint32_t od = (wd[q] >> 3) & 0x1E1E1E1Eu;
+    const int c = q * 8;
+    e[c + 0] = lds_h<0>(base, ev, (c + 0) * S);
+    e[c + 1] = lds_h<0>(base, od, (c + 1) * S);
+    e[c + 2] = lds_h<1>(base, ev, (c + 2) * S);
+    e[c + 3] = lds_h<1>(base, od, (c + 3) * S);
+    e[c + 4] = lds_h<2>(base, ev, (c + 4) * S);
+    e[c + 5] = lds_h<2>(base, od, (c + 5) * S);
+    e[c + 6] = lds_h<3>(base, ev, (c + 6) * S);
+    e[c + 7] = lds_h<3>(base, od, (c + 7) * S);
+  }
+}
+__device__ __forceinline__ float h_half_add(const _Float16 (&e)[16]) {
+  float one = 1.f;
+  asm("" : "+s"(one));
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 16; ++c) s[c & 3] = fmaf((float)e[c], one, s[c & 3]);
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
 // NG: groups of K the tables hold (32: K <= 4096, 64: K <= 8192, 112: K <=
 // 14336).
 // NB = 1: one tile per workgroup (grid = row tiles).  NB = 2: the workgroup
@@ -1246,6 +1276,14 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
   constexpr int kBefore = (RS == 4 || NB == 2 || (NG == 112 && PC <= 2)) ? 2 : 1;
   constexpr bool kSplitPlanes = kSlots == 1 && NB == 1 && RS == 1 && P >= 3;
   constexpr int kFirstPlanes = kSplitPlanes ? (PC + 1) / 2 : PC;
+  // Lookups pipelined over planes (h_half_read / h_half_add) with the 64- and
+  // 112-group tables; with 32 groups the compiler's own interleave was
+  // faster.  Same-process A/B, six repeats, p = 2 / 3 / 4, us: 4096x14336
+  // 8.50 / 10.42 / 12.36 -> 8.37 / 10.44 / 12.11, 4096x10240 7.28 / 8.64 /
+  // 10.07 -> 7.18 / 8.64 / 9.85, 14336x8192 13.91 / 18.12 / 22.99 -> 13.42 /
+  // 17.45 / 22.09; 4096x4096 4.26 / 4.59 / 5.07 -> 4.35 / 4.73 / 5.12.  Not
+  // with 112 groups and several tiles per workgroup, where it spilled at p = 3.
+  constexpr bool kPipe = NG > 32 && !(NG == 112 && NB == 2);
   sload(0, 0, G0);
   if constexpr (NG <= 64 && NB == 1 && RS == 1) __builtin_amdgcn_s_sleep(12);
 #pragma unroll
@@ -1303,12 +1341,28 @@ __global__ __launch_bounds__(kHThreads) void gemv_h16_kernel(
       if (h < 2 * Gp) {
         const int j = h >> 1, half = h & 1;
         const uint32_t base = lds_addr(lut + j * kHGroupStride + h_chunk_offset(16 * half));
-#pragma unroll
-        for (int u = 0; u < PC; ++u) {
-          // a plane index past P (P not a multiple of RS) looks up with scale 0
+        // a plane index past P (P not a multiple of RS) looks up with scale 0
+        auto plane_scale = [&](int u) -> float {
           const int i = RS > 1 ? ph * PC + u : u;
-          const float sc = i < P ? scale(min(i, P - 1), j) : 0.f;
-          acc = fmaf(sc, h_half_sum(w[t][u], base), acc);
+          return i < P ? scale(min(i, P - 1), j) : 0.f;
+        };
+        if constexpr (kPipe) {
+          // plane u + 1's 16 entries are requested before plane u's are
+          // added, so each wavefront keeps up to 16 table reads in flight
+          float sc[PC];
+#pragma unroll
+          for (int u = 0; u < PC; ++u) sc[u] = plane_scale(u);
+          _Float16 eb[2][16];
+          h_half_read(w[t][0], base, eb[0]);
+#pragma unroll
+          for (int u = 0; u < PC; ++u) {
+            if (u + 1 < PC) h_half_read(w[t][u + 1], base, eb[(u + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            acc = fmaf(sc[u], h_half_add(eb[u & 1]), acc);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < PC; ++u) acc = fmaf(plane_scale(u), h_half_sum(w[t][u], base), acc);
         }
         if (half == 0 && (RS == 1 || ph == 0)) acc = fmaf(scale(P, j), gsum[j], acc);
       }
