@@ -23,10 +23,11 @@
 //    hs of a 16-group window of tables (64 columns, two packed words per
 //    plane).  K <= 4096 keeps the fp32 tables of all of K resident while the
 //    workgroup walks several tiles; fp16 stores up to K = 28672 keep fp16
-//    tables resident (in two passes past K = 14336); other K stream windows of
-//    tables through two buffers (with two or more planes, 1024 lanes split the
-//    planes of each window).  gemv_direct_kernel is the table-free form, kept
-//    behind a switch for comparison.
+//    tables resident (in two passes past K = 14336), and so do fp16 stores
+//    with 2048 < K <= 4096 when each workgroup takes one tile; other K stream
+//    windows of tables through two buffers (with two or more planes, 1024
+//    lanes split the planes of each window).  gemv_direct_kernel is the
+//    table-free form, kept behind a switch for comparison.
 //  * LDS banks.  Table c sits at 80-byte stride (16 entries + 16 B pad) so that
 //    the 16-byte writes of 16 consecutive chunks cover distinct banks, and the
 //    four slots of a wavefront read disjoint quarters of the 64 banks.
