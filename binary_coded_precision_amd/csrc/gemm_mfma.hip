@@ -126,6 +126,59 @@ struct MfPrec {
   uint8_t p[kMfMaxBatch];
 };
 
+// One lane's decode operands for a step: its sign words inverted unless alpha
+// < 0 (a set bit then yields +|alpha|), and |alpha| in both fp16 halves.
+template <int P>
+__device__ __forceinline__ void mf_prep(const MfW<P> &o, uint32_t (&wp)[P][4],
+                                        uint32_t (&mag)[P]) {
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const uint32_t a16 = o.a[i];
+    const uint32_t neg = (uint32_t)((int32_t)(a16 << 16) >> 31);
+    mag[i] = (a16 & 0x7FFFu) * 0x10001u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wp[i][q] = ~(o.bits[i][q] ^ neg);
+  }
+}
+
+// Summed decode of 8-column block n: the fp16 weights z + sum_i +-alpha_i of
+// columns 8n..8n+7 of this lane's (row, group), planes added in order, each
+// add rounded to fp16.  Planes i and i+1 share one 64-bit shift: the high
+// word's bits shifted in from the low word land below bit 15, where the mask
+// drops them.
+template <int P>
+__device__ __forceinline__ half8 mf_sum_block(const uint32_t (&wp)[P][4],
+                                              const uint32_t (&mag)[P], uint32_t z2, int n) {
+  const int q = n >> 2;
+  const int u = n & 3;
+  half2v w[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) w[v] = as_h2(z2);
+#pragma unroll
+  for (int i = 0; i < P; i += 2)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      int sh = 15 - (4 * u + v);
+      if (i + 1 < P) {
+        // opaque shift count: with it known, the compiler proves the spilled
+        // bits masked and splits the shift back into two
+        asm("" : "+s"(sh));
+        const uint64_t w2 = ((uint64_t)wp[i + 1][q] << 32 | wp[i][q]) << sh;
+        w[v] += as_h2(((uint32_t)w2 & 0x80008000u) | mag[i]);
+        w[v] += as_h2(((uint32_t)(w2 >> 32) & 0x80008000u) | mag[i + 1]);
+      } else {
+        w[v] += as_h2(((wp[i][q] << sh) & 0x80008000u) | mag[i]);
+      }
+    }
+  half8 a;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    a[2 * v] = w[v][0];
+    a[2 * v + 1] = w[v][1];
+  }
+  return a;
+}
+
 // NT tiles of 16 requests, P planes.  Loads clamp rows past M, tiles past MT,
 // requests past b and groups past G to in-range addresses; the activations of
 // a group past G are staged as zeros, so it adds nothing (its clamped weights
@@ -199,17 +252,8 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
     for (int k = 0; k < NA; ++k) acc[nt][k] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const OpsW &o, int buf) __attribute__((always_inline)) {
-    // per plane: sign words inverted unless alpha < 0 (a clear bit then
-    // yields +|alpha|), and |alpha| in both halves
     uint32_t wp[P][4], mag[P];
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const uint32_t a16 = o.a[i];
-      const uint32_t neg = (uint32_t)((int32_t)(a16 << 16) >> 31);
-      mag[i] = (a16 & 0x7FFFu) * 0x10001u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) wp[i][q] = ~(o.bits[i][q] ^ neg);
-    }
+    mf_prep<P>(o, wp, mag);
     const uint32_t z2 = o.z * 0x10001u;
     const u32x4 *xb = xs[buf];
     auto read_b = [&](int n, half8 (&bo)[NT]) __attribute__((always_inline)) {
@@ -218,35 +262,9 @@ __global__ __launch_bounds__(64 * W) void gemm_mfma_kernel(
         bo[nt] = __builtin_bit_cast(half8, xb[mf_slot(nt * 16 + r, h, n)]);
     };
     if constexpr (SUM) {
-      // weights of block n: z + sum +-alpha per column, planes added in order;
-      // planes i and i+1 share one 64-bit shift, as in the per-plane branch
+      // weights of block n: z + sum +-alpha per column (mf_sum_block)
       auto decode = [&](int n) __attribute__((always_inline)) -> half8 {
-        const int q = n >> 2;
-        const int u = n & 3;
-        half2v w[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) w[v] = as_h2(z2);
-#pragma unroll
-        for (int i = 0; i < P; i += 2)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            int sh = 15 - (4 * u + v);
-            if (i + 1 < P) {
-              asm("" : "+s"(sh));
-              const uint64_t w2 = ((uint64_t)wp[i + 1][q] << 32 | wp[i][q]) << sh;
-              w[v] += as_h2(((uint32_t)w2 & 0x80008000u) | mag[i]);
-              w[v] += as_h2(((uint32_t)(w2 >> 32) & 0x80008000u) | mag[i + 1]);
-            } else {
-              w[v] += as_h2(((wp[i][q] << sh) & 0x80008000u) | mag[i]);
-            }
-          }
-        half8 a;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          a[2 * v] = w[v][0];
-          a[2 * v + 1] = w[v][1];
-        }
-        return a;
+        return mf_sum_block<P>(wp, mag, z2, n);
       };
       // software pipeline: block n+1's activations are read and its weights
       // decoded before block n's products are issued, so the LDS latency and
@@ -505,14 +523,7 @@ template <int P>
 __device__ __forceinline__ void wk_step(floatx4 (&acc)[P + 1], const MfW<P> &o, const u32x4 *xs,
                                         int rq, int gs) {
   uint32_t wp[P][4], mag[P];
-#pragma unroll
-  for (int i = 0; i < P; ++i) {
-    const uint32_t a16 = o.a[i];
-    const uint32_t neg = (uint32_t)((int32_t)(a16 << 16) >> 31);
-    mag[i] = (a16 & 0x7FFFu) * 0x10001u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) wp[i][q] = ~(o.bits[i][q] ^ neg);
-  }
+  mf_prep<P>(o, wp, mag);
   const uint32_t z2 = o.z * 0x10001u;
   const half8 az = __builtin_bit_cast(half8, u32x4{z2, z2, z2, z2});
 #pragma unroll
@@ -688,6 +699,181 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
     tile(k, wa);
     flush(k, 1);
   }
+}
+
+// ---------------------------------------------------------------- whole K, requests streamed
+//
+// 17 to 64 requests at one precision, 2048 < K <= 4096, one row tile per
+// workgroup: its eight wavefronts split K as in the whole-K kernel (lane
+// (r, h) of wavefront w takes group 4w + h).  Each lane decodes its 16 blocks
+// once into the summed fp16 weights z + sum +-alpha (mf_sum_block, 64
+// registers), and the requests' activations pass through one 128 KB LDS
+// stage, 16 requests at a time, in the whole-K stage's layout.  The
+// activations go straight from memory to LDS (global_load_lds_dwordx4, no
+// registers), so the decoded weights fit beside everything else without
+// spilling.  The eight wavefronts' partial products then meet in LDS and are
+// summed in wavefront order.  No partial sums leave the compute unit and there
+// is no second launch; in exchange every compute unit reads all of the
+// activations (b x K fp16) from L2, where the split kernel reads one K slice
+// per 128 rows but writes fp32 partials that a finalize reads back.
+// Wavefront w's groups are step w of the split kernel and the wavefront sums
+// run in slice order, so the outputs equal the split kernel's bit for bit
+// wherever it takes one step per slice (K = 4096, and every 2048 < K < 4096
+// measured).  Staging two 8-request halves in two buffers, so that one half
+// loads while the other is contracted, measured slower (4096x4096, b = 64:
+// 13.50 -> 16.26 us): half of each product's columns went unused and the
+// barriers doubled.
+template <int NT, int P>
+__global__ __launch_bounds__(64 * kWkWaves) void gemm_wkx_kernel(
+    const u32x4 *__restrict__ bits, const half_t *__restrict__ alpha,
+    const half_t *__restrict__ zero, const half_t *__restrict__ X, int ldx, int b,
+    half_t *__restrict__ Y, int ldy, int M, int G, int MT) {
+  constexpr int kReq = 16;
+  constexpr int kStage = kReq * kWkMaxGroups * kMfBlocks;  // 16-byte blocks, 128 KB
+  constexpr int kLoads = kStage / (64 * kWkWaves);          // per lane and request tile
+  static_assert(kLoads == kReq, "one stage load per request");
+  static_assert(kWkWaves * NT * 64 <= kStage, "partials fit the stage");
+  __shared__ u32x4 xs[kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int h = lane >> 4;
+  const int g = wave * kMfGroups + h;  // this lane's group of K
+  const int gc = min(g, G - 1);
+  const int t = blockIdx.x;  // one row tile per workgroup (grid = MT)
+  const int m = min(t * kTileRows + r, M - 1);
+  const size_t plane_blocks = (size_t)MT * G * kTileRows;
+  const size_t MG = (size_t)M * G;
+
+  // Stage request tile q: load j of wavefront w fills slots (8j + w) * 64 +
+  // lane, which hold request j, groups 4w .. 4w+3 (wk_slot), so each load
+  // reads 1 KB of one request's row; a lane reads the block that the slot's
+  // swizzle puts there.  Requests past b re-read request b - 1 and groups past
+  // G re-read group G - 1: neither reaches a stored output (columns past b are
+  // not stored, and the weights of groups past G are zero).  The request row
+  // is uniform, so only a 32-bit byte offset per lane and load remains in
+  // vector registers.
+  const uint32_t xoff = (uint32_t)gc * (kGroup * 2);
+  auto stage_x = [&](int q) __attribute__((always_inline)) {
+    // opaque per stage: the compiler would otherwise hoist the sixteen 64-bit
+    // addresses of every stage to the start and spill them
+    uint32_t xo = xoff;
+    asm volatile("" : "+v"(xo));
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const char *row = reinterpret_cast<const char *>(X + (size_t)min(q * kReq + j, b - 1) * ldx);
+      __builtin_amdgcn_global_load_lds(
+          (const void *)(row + (xo + (uint32_t)((r ^ j) << 4))),
+          (__attribute__((address_space(3))) void *)(xs + (j * kWkWaves + wave) * 64), 16, 0, 0);
+    }
+  };
+
+  // this lane's sign words and scales first (the decode waits for them), then
+  // the first request tile's stage, then the pull-in below
+  MfW<P> wo;
+  {
+    const u32x4 *tb = bits + ((size_t)t * G + gc) * kTileRows + r;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      wo.bits[i] = tb[i * plane_blocks];
+      wo.a[i] = *reinterpret_cast<const unsigned short *>(alpha + i * MG + (size_t)m * G + gc);
+    }
+    wo.z = *reinterpret_cast<const unsigned short *>(zero + (size_t)m * G + gc);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  stage_x(0);
+  __builtin_amdgcn_sched_barrier(0);
+  // Requests 16.. (the later request tiles) are pulled into L2 now, one
+  // 2-byte load per 128-byte line, so that their stages later hit L2 instead
+  // of each missing to HBM in turn.  Workgroups go to the eight XCDs
+  // round-robin, so the workgroups sharing an XCD split its lines: workgroup
+  // i touches part i / 8 of them, a line per thread (a part larger than the
+  // workgroup is pulled in only in part).  The load is unconditional (threads
+  // past the part re-touch its last line): a load under a branch would be
+  // waited for where the branches join.  The value is consumed by an empty
+  // asm at the end and never used.
+  uint32_t touch = 0;
+  if constexpr (NT > 1) {
+    const int parts = max(1, (int)gridDim.x >> 3);
+    const int per_row = G * 2;  // 128-byte lines of a request's K columns
+    const int lines = (b - kReq) * per_row;
+    const int per_part = (lines + parts - 1) / parts;
+    const int l = min((((int)blockIdx.x >> 3) % parts) * per_part + min(tid, per_part - 1),
+                      lines - 1);
+    touch = *reinterpret_cast<const unsigned short *>(X + (size_t)(kReq + l / per_row) * ldx +
+                                                       (size_t)(l % per_row) * 64);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // the tile's weights, decoded once (zero for groups past G)
+  half8 aw[kMfBlocks];
+  {
+    uint32_t wp[P][4], mag[P];
+    mf_prep<P>(wo, wp, mag);
+    const uint32_t z2 = wo.z * 0x10001u;
+#pragma unroll
+    for (int n = 0; n < kMfBlocks; ++n) {
+      aw[n] = mf_sum_block<P>(wp, mag, z2, n);
+      if (g >= G) aw[n] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  floatx4 acc[NT];
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    if (q > 0) stage_x(q);
+    // the stage's loads land in LDS: wait for this wavefront's, then for
+    // every wavefront's
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // every B operand of the request tile is read before the products, so the
+    // LDS latency is paid once rather than before each product
+    half8 bq[kMfBlocks];
+#pragma unroll
+    for (int n = 0; n < kMfBlocks; ++n) bq[n] = __builtin_bit_cast(half8, xs[wk_slot(r, g, n)]);
+    acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < kMfBlocks; ++n)
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[n], bq[n], acc[q], 0, 0, 0);
+    __syncthreads();
+  }
+  // the eight wavefronts' partials meet in the stage: [wave][q][lane]; lane
+  // (c, h) holds rows 4h .. 4h+3 for request 16q + c
+  floatx4 *red = reinterpret_cast<floatx4 *>(xs);
+#pragma unroll
+  for (int q = 0; q < NT; ++q) red[(wave * NT + q) * 64 + lane] = acc[q];
+  __syncthreads();
+#pragma unroll
+  for (int e0 = 0; e0 < NT * 256; e0 += 64 * kWkWaves) {
+    const int e = e0 + tid;
+    if (e < NT * 256) {
+      const int q = e >> 8;
+      const int l = (e >> 2) & 63, v = e & 3;
+      const int c = q * 16 + (l & 15);
+      const int mm = t * kTileRows + 4 * (l >> 4) + v;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWkWaves; ++w) sum += red[(w * NT + q) * 64 + l][v];
+      if (c < b && mm < M) Y[(size_t)c * ldy + mm] = (half_t)sum;
+    }
+  }
+  asm volatile("" ::"v"(touch));
+}
+
+// The streamed whole-K kernel serves uniform-precision launches of two to
+// four request tiles with 16 < G <= 32 on 129 to 256 row tiles (one per
+// compute unit; more than half of them busy).  Same-process A/B against the
+// split kernel, cold, us: 4096x4096 b = 17 / 32 / 48 / 64 (p = 4) 10.67 /
+// 11.95 / 13.49 / 15.27 -> 10.14 / 10.24 / 11.78 / 13.42, b = 64 p = 2 13.44
+// -> 11.60; 4096x3072 b = 64 13.61 -> 12.66; 4096x2176 b = 40 11.31 ->
+// 10.88; 2048x4096 b = 64 12.57 -> 12.30 (a tie), 1024x4096 b = 64 11.37 ->
+// 12.42 (a loss: 64 workgroups).
+bool use_wkx(int M, int K, int n, bool mixed) {
+  const int G = K / kGroup;
+  const int MT = row_tiles(M);
+  return !mixed && n > 16 && n <= kMfMaxBatch && G > kWkMaxGroups / 2 && G <= kWkMaxGroups &&
+         MT > kMfSlots / 2 && MT <= kMfSlots;
 }
 
 // The whole-K kernel serves a launch when it has one request tile and K fits
@@ -868,6 +1054,29 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
       default: BCQ_WK(4); break;
     }
 #undef BCQ_WK
+    return hipGetLastError();
+  }
+  if (use_wkx(M, K, b, p_req != nullptr)) {
+    const dim3 grid(MT), block(64 * kWkWaves);  // MT <= kMfSlots: one tile per workgroup
+#define BCQ_WKX(NTV)                                                                          \
+  switch (p) {                                                                                \
+    case 1: hipLaunchKernelGGL((gemm_wkx_kernel<NTV, 1>), grid, block, 0, s, b4, a, z, X, ldx, \
+                               b, Y, ldy, M, G, MT); break;                                   \
+    case 2: hipLaunchKernelGGL((gemm_wkx_kernel<NTV, 2>), grid, block, 0, s, b4, a, z, X, ldx, \
+                               b, Y, ldy, M, G, MT); break;                                   \
+    case 3: hipLaunchKernelGGL((gemm_wkx_kernel<NTV, 3>), grid, block, 0, s, b4, a, z, X, ldx, \
+                               b, Y, ldy, M, G, MT); break;                                   \
+    default: hipLaunchKernelGGL((gemm_wkx_kernel<NTV, 4>), grid, block, 0, s, b4, a, z, X, ldx, \
+                                b, Y, ldy, M, G, MT); break;                                  \
+  }
+    if (NT == 2) {
+      BCQ_WKX(2)
+    } else if (NT == 3) {
+      BCQ_WKX(3)
+    } else {
+      BCQ_WKX(4)
+    }
+#undef BCQ_WKX
     return hipGetLastError();
   }
   const int W = mf_waves(NT);

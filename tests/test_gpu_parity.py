@@ -570,6 +570,34 @@ def test_mfma_workspace_reused_across_batch_sizes():
             assert rel_l2(got[r], ref[r]) <= 2e-3, (b, p, r)
 
 
+@pytest.mark.parametrize("M,K,b,P", [
+    (4096, 4096, 17, 4), (4096, 4096, 33, 3), (4096, 4096, 64, 4),
+    (2500, 3072, 50, 3),  # 157 row tiles, the last one ragged
+    (4000, 2176, 40, 4),  # 17 groups: lanes past K
+    (3001, 4096, 64, 2),  # 188 row tiles, the last holding one row
+])
+def test_streamed_whole_k_every_output(M, K, b, P):
+    """Launches of 17..64 fp16 requests at one precision with 2048 < K <= 4096
+    on 129..256 row tiles (the streamed whole-K matrix-core kernel): every
+    output of every request at every precision against the oracle, with
+    padded activation and output rows; the padding stays untouched."""
+    w = bcq_synth.make(M, K, P, b=b, dtype=np.float16, seed=M + K + b, outlier_frac=0.01)
+    st = store_of(w)
+    ws = bcq.new_workspace(st, b)
+    Xbig = torch.zeros((b, K + 64), dtype=torch.float16, device="cuda")
+    Xbig[:, :K] = dev(w.x)
+    sentinel = 1234.0
+    for p in range(1, P + 1):
+        say("streamed whole-K", M, K, b, p)
+        Ybig = torch.full((b, M + 24), sentinel, dtype=torch.float16, device="cuda")
+        bcq.bcq_gemm_skinny(st, p, Xbig[:, :K], Ybig[:, :M], workspace=ws)
+        out = Ybig.cpu().numpy().astype(np.float64)
+        assert np.all(out[:, M:] == sentinel), p
+        ref = oracle_y_all(w, w.x, [p] * b)
+        for r in range(b):
+            assert request_ok(out[r, :M], ref[r], np.float16, K, summed=True), (p, r)
+
+
 @pytest.mark.parametrize("shape", ["q_o", "k_v", "gate_up", "down"])
 @pytest.mark.parametrize("b", [16, 64])
 def test_config5_layer_sweep_every_row(shape, b):
