@@ -373,11 +373,15 @@ bcq_status bcq_gemm_skinny(const bcq_store *store, int32_t p, const void *X, int
   char *Yc = static_cast<char *>(Y);
   if (on_matrix_cores(store, b)) {
     log_route("bcq_gemm_skinny", store, b,
-              bcq::mfma_whole_k(store->M, store->K, b < bcq::kMfMaxBatch ? b : bcq::kMfMaxBatch)
-                  ? "matrix cores, whole K"
-                  : "matrix cores, split K");
-    return run_mfma_batches(store, p, nullptr, Xc, b, ldx, Yc, ldy, workspace, bcq::kMfMaxBatch,
-                            stream);
+              bcq::mfma_streamed(store->M, store->K, b)
+                  ? "matrix cores, whole K, requests streamed"
+                  : bcq::mfma_whole_k(store->M, store->K,
+                                      b < bcq::kMfMaxBatch ? b : bcq::kMfMaxBatch)
+                        ? "matrix cores, whole K"
+                        : "matrix cores, split K");
+    // the streamed whole-K kernel takes the whole batch in one launch
+    const int chunk = bcq::mfma_streamed(store->M, store->K, b) ? BCQ_MAX_BATCH : bcq::kMfMaxBatch;
+    return run_mfma_batches(store, p, nullptr, Xc, b, ldx, Yc, ldy, workspace, chunk, stream);
   }
   log_route("bcq_gemm_skinny", store, b, b == 1 ? "batch-1 tables" : "vector-ALU tables");
   int32_t ps[BCQ_MAX_BATCH];

@@ -93,7 +93,7 @@ hipError_t launch_skinny_lut(const uint32_t *bits, int M, int K, int p_max, cons
 // uses the first p_req[q] of them (p_req: host array of b values in 1..p, or
 // nullptr for all p).  Per-request precisions need b <= kMfMaxMixed; otherwise
 // b <= kMfMaxBatch per launch (a call with more runs several launches in
-// order).  ws holds at least mfma_workspace_bytes(M, K, b) bytes for the call's
+// order), or b <= BCQ_MAX_BATCH where mfma_streamed holds.  ws holds at least mfma_workspace_bytes(M, K, b) bytes for the call's
 // whole batch b (nullptr when that is 0: launches that keep K within one
 // workgroup need none).
 constexpr int kMfMaxBatch = 64;
@@ -116,5 +116,9 @@ hipError_t launch_gemm_gate_up(const uint32_t *bits, int M, int K, int p, const 
 // True when a launch of n fp16 requests on (M, K) keeps K within one
 // workgroup (no workspace, no second kernel).
 bool mfma_whole_k(int M, int K, int n);
+// True when a uniform-precision launch of n fp16 requests on (M, K) runs the
+// streamed whole-K kernel, which takes up to BCQ_MAX_BATCH requests in one
+// launch (the weights decoded once for all of them).
+bool mfma_streamed(int M, int K, int n);
 
 }  // namespace bcq

@@ -703,27 +703,27 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
 
 // ---------------------------------------------------------------- whole K, requests streamed
 //
-// 17 to 64 requests at one precision, 2048 < K <= 4096, one row tile per
-// workgroup: its eight wavefronts split K as in the whole-K kernel (lane
-// (r, h) of wavefront w takes group 4w + h).  Each lane decodes its 16 blocks
-// once into the summed fp16 weights z + sum +-alpha (mf_sum_block, 64
+// 17 to 256 requests at one precision in one launch, 2048 < K <= 4096, one row
+// tile per workgroup: its eight wavefronts split K as in the whole-K kernel
+// (lane (r, h) of wavefront w takes group 4w + h).  Each lane decodes its 16
+// blocks once into the summed fp16 weights z + sum +-alpha (mf_sum_block, 64
 // registers), and the requests' activations pass through one 128 KB LDS
 // stage, 16 requests at a time, in the whole-K stage's layout.  The
 // activations go straight from memory to LDS (global_load_lds_dwordx4, no
 // registers), so the decoded weights fit beside everything else without
-// spilling.  The eight wavefronts' partial products then meet in LDS and are
-// summed in wavefront order.  No partial sums leave the compute unit and there
-// is no second launch; in exchange every compute unit reads all of the
-// activations (b x K fp16) from L2, where the split kernel reads one K slice
-// per 128 rows but writes fp32 partials that a finalize reads back.
-// Wavefront w's groups are step w of the split kernel and the wavefront sums
-// run in slice order, so the outputs equal the split kernel's bit for bit
-// wherever it takes one step per slice (K = 4096, and every 2048 < K < 4096
-// measured).  Staging two 8-request halves in two buffers, so that one half
-// loads while the other is contracted, measured slower (4096x4096, b = 64:
-// 13.50 -> 16.26 us): half of each product's columns went unused and the
-// barriers doubled.
-template <int NT, int P>
+// spilling.  After each 16 requests' products the eight wavefronts' partials
+// meet in LDS and are summed in wavefront order while the next 16 requests'
+// activations load.  No partial sums leave the compute unit and there is no
+// second launch; in exchange every compute unit reads all of the activations
+// (b x K fp16) from L2, where the split kernel reads one K slice per 128 rows
+// but writes fp32 partials that a finalize reads back.  Wavefront w's groups
+// are step w of the split kernel and the wavefront sums run in slice order,
+// so the outputs equal the split kernel's bit for bit wherever it takes one
+// step per slice (K = 4096, and every 2048 < K < 4096 measured).  Staging two
+// 8-request halves in two buffers, so that one half loads while the other is
+// contracted, measured slower (4096x4096, b = 64: 13.50 -> 16.26 us): half of
+// each product's columns went unused and the barriers doubled.
+template <int P>
 __global__ __launch_bounds__(64 * kWkWaves) void gemm_wkx_kernel(
     const u32x4 *__restrict__ bits, const half_t *__restrict__ alpha,
     const half_t *__restrict__ zero, const half_t *__restrict__ X, int ldx, int b,
@@ -732,8 +732,8 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wkx_kernel(
   constexpr int kStage = kReq * kWkMaxGroups * kMfBlocks;  // 16-byte blocks, 128 KB
   constexpr int kLoads = kStage / (64 * kWkWaves);          // per lane and request tile
   static_assert(kLoads == kReq, "one stage load per request");
-  static_assert(kWkWaves * NT * 64 <= kStage, "partials fit the stage");
   __shared__ u32x4 xs[kStage];
+  __shared__ floatx4 red[kWkWaves][64];  // one request tile's wavefront partials
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -746,6 +746,7 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wkx_kernel(
   const int m = min(t * kTileRows + r, M - 1);
   const size_t plane_blocks = (size_t)MT * G * kTileRows;
   const size_t MG = (size_t)M * G;
+  const int nq = (b + kReq - 1) / kReq;  // request tiles
 
   // Stage request tile q: load j of wavefront w fills slots (8j + w) * 64 +
   // lane, which hold request j, groups 4w .. 4w+3 (wk_slot), so each load
@@ -795,7 +796,7 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wkx_kernel(
   // waited for where the branches join.  The value is consumed by an empty
   // asm at the end and never used.
   uint32_t touch = 0;
-  if constexpr (NT > 1) {
+  {
     const int parts = max(1, (int)gridDim.x >> 3);
     const int per_row = G * 2;  // 128-byte lines of a request's K columns
     const int lines = (b - kReq) * per_row;
@@ -819,10 +820,12 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wkx_kernel(
       if (g >= G) aw[n] = half8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  floatx4 acc[NT];
-#pragma unroll
-  for (int q = 0; q < NT; ++q) {
-    if (q > 0) stage_x(q);
+  // Request tile q: wait for its stage, contract it, and once every
+  // wavefront is done (the stage is then free) request tile q + 1's stage
+  // and sum tile q's eight wavefront partials in wavefront order.  The
+  // partials area is rewritten only after the next tile's first barrier,
+  // which every thread passes only once its sums are done.
+  for (int q = 0; q < nq; ++q) {
     // the stage's loads land in LDS: wait for this wavefront's, then for
     // every wavefront's
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -832,38 +835,30 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wkx_kernel(
     half8 bq[kMfBlocks];
 #pragma unroll
     for (int n = 0; n < kMfBlocks; ++n) bq[n] = __builtin_bit_cast(half8, xs[wk_slot(r, g, n)]);
-    acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int n = 0; n < kMfBlocks; ++n)
-      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[n], bq[n], acc[q], 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[n], bq[n], acc, 0, 0, 0);
+    // lane (c, h) holds rows 4h .. 4h+3 for request 16q + c
+    red[wave][lane] = acc;
     __syncthreads();
-  }
-  // the eight wavefronts' partials meet in the stage: [wave][q][lane]; lane
-  // (c, h) holds rows 4h .. 4h+3 for request 16q + c
-  floatx4 *red = reinterpret_cast<floatx4 *>(xs);
-#pragma unroll
-  for (int q = 0; q < NT; ++q) red[(wave * NT + q) * 64 + lane] = acc[q];
-  __syncthreads();
-#pragma unroll
-  for (int e0 = 0; e0 < NT * 256; e0 += 64 * kWkWaves) {
-    const int e = e0 + tid;
-    if (e < NT * 256) {
-      const int q = e >> 8;
-      const int l = (e >> 2) & 63, v = e & 3;
-      const int c = q * 16 + (l & 15);
+    if (q + 1 < nq) stage_x(q + 1);
+    if (tid < 256) {
+      const int l = tid >> 2, v = tid & 3;
+      const int c = q * kReq + (l & 15);
       const int mm = t * kTileRows + 4 * (l >> 4) + v;
       float sum = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWkWaves; ++w) sum += red[(w * NT + q) * 64 + l][v];
+      for (int w = 0; w < kWkWaves; ++w) sum += red[w][l][v];
       if (c < b && mm < M) Y[(size_t)c * ldy + mm] = (half_t)sum;
     }
   }
   asm volatile("" ::"v"(touch));
 }
 
-// The streamed whole-K kernel serves uniform-precision launches of two to
-// four request tiles with 16 < G <= 32 on 129 to 256 row tiles (one per
-// compute unit; more than half of them busy).  Same-process A/B against the
+// The streamed whole-K kernel serves uniform-precision calls of 17 to 256
+// requests (one launch each) with 16 < G <= 32 on 129 to 256 row tiles (one
+// per compute unit; more than half of them busy).  Same-process A/B against the
 // split kernel, cold, us: 4096x4096 b = 17 / 32 / 48 / 64 (p = 4) 10.67 /
 // 11.95 / 13.49 / 15.27 -> 10.14 / 10.24 / 11.78 / 13.42, b = 64 p = 2 13.44
 // -> 11.60; 4096x3072 b = 64 13.61 -> 12.66; 4096x2176 b = 40 11.31 ->
@@ -872,7 +867,7 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wkx_kernel(
 bool use_wkx(int M, int K, int n, bool mixed) {
   const int G = K / kGroup;
   const int MT = row_tiles(M);
-  return !mixed && n > 16 && n <= kMfMaxBatch && G > kWkMaxGroups / 2 && G <= kWkMaxGroups &&
+  return !mixed && n > 16 && n <= BCQ_MAX_BATCH && G > kWkMaxGroups / 2 && G <= kWkMaxGroups &&
          MT > kMfSlots / 2 && MT <= kMfSlots;
 }
 
@@ -969,6 +964,7 @@ void launch_mf_nt(int NT, bool sum, dim3 grid, hipStream_t s, const MfArgs &g) {
 }  // namespace
 
 bool mfma_whole_k(int M, int K, int n) { return use_wk(M, K, n); }
+bool mfma_streamed(int M, int K, int n) { return use_wkx(M, K, n, false); }
 
 size_t mfma_workspace_bytes(int M, int K, int b) {
   // the launches of one call run in order and reuse the workspace; a call
@@ -1058,25 +1054,16 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
   }
   if (use_wkx(M, K, b, p_req != nullptr)) {
     const dim3 grid(MT), block(64 * kWkWaves);  // MT <= kMfSlots: one tile per workgroup
-#define BCQ_WKX(NTV)                                                                          \
-  switch (p) {                                                                                \
-    case 1: hipLaunchKernelGGL((gemm_wkx_kernel<NTV, 1>), grid, block, 0, s, b4, a, z, X, ldx, \
-                               b, Y, ldy, M, G, MT); break;                                   \
-    case 2: hipLaunchKernelGGL((gemm_wkx_kernel<NTV, 2>), grid, block, 0, s, b4, a, z, X, ldx, \
-                               b, Y, ldy, M, G, MT); break;                                   \
-    case 3: hipLaunchKernelGGL((gemm_wkx_kernel<NTV, 3>), grid, block, 0, s, b4, a, z, X, ldx, \
-                               b, Y, ldy, M, G, MT); break;                                   \
-    default: hipLaunchKernelGGL((gemm_wkx_kernel<NTV, 4>), grid, block, 0, s, b4, a, z, X, ldx, \
-                                b, Y, ldy, M, G, MT); break;                                  \
-  }
-    if (NT == 2) {
-      BCQ_WKX(2)
-    } else if (NT == 3) {
-      BCQ_WKX(3)
-    } else {
-      BCQ_WKX(4)
+    switch (p) {
+      case 1: hipLaunchKernelGGL((gemm_wkx_kernel<1>), grid, block, 0, s, b4, a, z, X, ldx, b, Y,
+                                 ldy, M, G, MT); break;
+      case 2: hipLaunchKernelGGL((gemm_wkx_kernel<2>), grid, block, 0, s, b4, a, z, X, ldx, b, Y,
+                                 ldy, M, G, MT); break;
+      case 3: hipLaunchKernelGGL((gemm_wkx_kernel<3>), grid, block, 0, s, b4, a, z, X, ldx, b, Y,
+                                 ldy, M, G, MT); break;
+      default: hipLaunchKernelGGL((gemm_wkx_kernel<4>), grid, block, 0, s, b4, a, z, X, ldx, b,
+                                  Y, ldy, M, G, MT); break;
     }
-#undef BCQ_WKX
     return hipGetLastError();
   }
   const int W = mf_waves(NT);

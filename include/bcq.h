@@ -215,19 +215,21 @@ bcq_status bcq_gemm_gate_up(const bcq_store *store, const int32_t *p_host, const
  * ALUs with sign-combination tables shared by up to 8 requests per launch
  * (exact fp32 sums of the stored values).  Other fp16 batches of 2, and those
  * of 3 and more,
- * decode tiles of W to fp16 once per launch of up to 64 requests and contract
- * them with X on the matrix cores (fp32 accumulation; in launches of up to 16
+ * decode tiles of W to fp16 once per launch of up to 64 requests (of the whole
+ * batch, up to BCQ_MAX_BATCH, in the calls at one precision with
+ * 2048 < K <= 4096 on 2049 to 4096 rows) and contract them with X on the
+ * matrix cores (fp32 accumulation; in launches of up to 16
  * requests, and in per-request-precision launches of up to 32, each plane's
  * +-alpha is an exact fp16 operand; in larger launches at one precision the
  * decoded weight z + sum +-alpha is rounded to fp16).  Launches of up to 16 requests with
  * K <= 4096 keep K within one workgroup, except K <= 2048 on more than 256
- * tiles of 16 rows (M > 4096); so do launches of 17 to 64 requests with
- * 2048 < K <= 4096 on 2049 to 4096 rows.  Other launches split K over
+ * tiles of 16 rows (M > 4096); so do calls of 17 to BCQ_MAX_BATCH requests
+ * with 2048 < K <= 4096 on 2049 to 4096 rows.  Other launches split K over
  * workgroups and use bcq_workspace_bytes(store, b) bytes of device workspace
  * (4-byte aligned) for the K slices' partial sums: contents need no
  * initialisation and are clobbered by the call, so calls that may run at the
  * same time need separate workspaces.  That size depends on (M, K, b) only,
- * so it also covers the 17..64-request shapes just named, whose
+ * so it also covers the 17..256-request shapes just named, whose
  * per-request-precision calls split K; calls at one precision there leave the
  * workspace untouched.  workspace may be NULL when that size is 0; a smaller
  * workspace gives BCQ_ERR_INVALID_ARG.

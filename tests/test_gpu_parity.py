@@ -575,12 +575,15 @@ def test_mfma_workspace_reused_across_batch_sizes():
     (2500, 3072, 50, 3),  # 157 row tiles, the last one ragged
     (4000, 2176, 40, 4),  # 17 groups: lanes past K
     (3001, 4096, 64, 2),  # 188 row tiles, the last holding one row
+    (3000, 3072, 130, 3),  # past 64 requests: one launch for the whole batch
+    (4096, 4096, 256, 2),  # the largest batch
 ])
 def test_streamed_whole_k_every_output(M, K, b, P):
-    """Launches of 17..64 fp16 requests at one precision with 2048 < K <= 4096
-    on 129..256 row tiles (the streamed whole-K matrix-core kernel): every
-    output of every request at every precision against the oracle, with
-    padded activation and output rows; the padding stays untouched."""
+    """Calls of 17..256 fp16 requests at one precision with 2048 < K <= 4096
+    on 129..256 row tiles (the streamed whole-K matrix-core kernel, one launch
+    per call): every output of every request at every precision against the
+    oracle, with padded activation and output rows; the padding stays
+    untouched."""
     w = bcq_synth.make(M, K, P, b=b, dtype=np.float16, seed=M + K + b, outlier_frac=0.01)
     st = store_of(w)
     ws = bcq.new_workspace(st, b)
