@@ -711,9 +711,13 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
 // stage, 16 requests at a time, in the whole-K stage's layout.  The
 // activations go straight from memory to LDS (global_load_lds_dwordx4, no
 // registers), so the decoded weights fit beside everything else without
-// spilling.  After each 16 requests' products the eight wavefronts' partials
-// meet in LDS and are summed in wavefront order while the next 16 requests'
-// activations load.  No partial sums leave the compute unit and there is no
+// spilling.  Up to 64 requests (NT request tiles) the tiles' partials stay in
+// registers and the eight wavefronts' partials meet once, in the stage, after
+// the last tile; past 64 (NT = 0) the request tiles run in a loop, and after
+// each tile's products its partials meet in a small LDS array and are summed
+// while the next tile's activations load (one launch for the whole call: the
+// weights are decoded once).  Either way the partials are summed in wavefront
+// order.  No partial sums leave the compute unit and there is no
 // second launch; in exchange every compute unit reads all of the activations
 // (b x K fp16) from L2, where the split kernel reads one K slice per 128 rows
 // but writes fp32 partials that a finalize reads back.  Wavefront w's groups
@@ -723,7 +727,7 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wk_kernel(
 // 8-request halves in two buffers, so that one half loads while the other is
 // contracted, measured slower (4096x4096, b = 64: 13.50 -> 16.26 us): half of
 // each product's columns went unused and the barriers doubled.
-template <int P>
+template <int P, int NT>
 __global__ __launch_bounds__(64 * kWkWaves) void gemm_wkx_kernel(
     const u32x4 *__restrict__ bits, const half_t *__restrict__ alpha,
     const half_t *__restrict__ zero, const half_t *__restrict__ X, int ldx, int b,
@@ -732,6 +736,7 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wkx_kernel(
   constexpr int kStage = kReq * kWkMaxGroups * kMfBlocks;  // 16-byte blocks, 128 KB
   constexpr int kLoads = kStage / (64 * kWkWaves);          // per lane and request tile
   static_assert(kLoads == kReq, "one stage load per request");
+  static_assert(kWkWaves * NT * 64 <= kStage, "partials fit the stage");
   __shared__ u32x4 xs[kStage];
   __shared__ floatx4 red[kWkWaves][64];  // one request tile's wavefront partials
 
@@ -746,7 +751,7 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wkx_kernel(
   const int m = min(t * kTileRows + r, M - 1);
   const size_t plane_blocks = (size_t)MT * G * kTileRows;
   const size_t MG = (size_t)M * G;
-  const int nq = (b + kReq - 1) / kReq;  // request tiles
+  const int nq = NT > 0 ? NT : (b + kReq - 1) / kReq;  // request tiles
 
   // Stage request tile q: load j of wavefront w fills slots (8j + w) * 64 +
   // lane, which hold request j, groups 4w .. 4w+3 (wk_slot), so each load
@@ -820,37 +825,77 @@ __global__ __launch_bounds__(64 * kWkWaves) void gemm_wkx_kernel(
       if (g >= G) aw[n] = half8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  // Request tile q: wait for its stage, contract it, and once every
-  // wavefront is done (the stage is then free) request tile q + 1's stage
-  // and sum tile q's eight wavefront partials in wavefront order.  The
-  // partials area is rewritten only after the next tile's first barrier,
-  // which every thread passes only once its sums are done.
-  for (int q = 0; q < nq; ++q) {
-    // the stage's loads land in LDS: wait for this wavefront's, then for
-    // every wavefront's
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (NT > 0) {
+    // NT request tiles (up to 64 requests): the tiles' partials stay in
+    // registers, and the eight wavefronts' partials meet once, in the stage,
+    // after the last tile
+    floatx4 acc[NT];
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      if (q > 0) stage_x(q);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      half8 bq[kMfBlocks];
+#pragma unroll
+      for (int n = 0; n < kMfBlocks; ++n) bq[n] = __builtin_bit_cast(half8, xs[wk_slot(r, g, n)]);
+      acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int n = 0; n < kMfBlocks; ++n)
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[n], bq[n], acc[q], 0, 0, 0);
+      __syncthreads();
+    }
+    // [wave][q][lane]; lane (c, h) holds rows 4h .. 4h+3 for request 16q + c
+    floatx4 *part = reinterpret_cast<floatx4 *>(xs);
+#pragma unroll
+    for (int q = 0; q < NT; ++q) part[(wave * NT + q) * 64 + lane] = acc[q];
     __syncthreads();
-    // every B operand of the request tile is read before the products, so the
-    // LDS latency is paid once rather than before each product
-    half8 bq[kMfBlocks];
 #pragma unroll
-    for (int n = 0; n < kMfBlocks; ++n) bq[n] = __builtin_bit_cast(half8, xs[wk_slot(r, g, n)]);
-    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int e0 = 0; e0 < NT * 256; e0 += 64 * kWkWaves) {
+      const int e = e0 + tid;
+      if (e < NT * 256) {
+        const int q = e >> 8;
+        const int l = (e >> 2) & 63, v = e & 3;
+        const int c = q * kReq + (l & 15);
+        const int mm = t * kTileRows + 4 * (l >> 4) + v;
+        float sum = 0.f;
 #pragma unroll
-    for (int n = 0; n < kMfBlocks; ++n)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[n], bq[n], acc, 0, 0, 0);
-    // lane (c, h) holds rows 4h .. 4h+3 for request 16q + c
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (q + 1 < nq) stage_x(q + 1);
-    if (tid < 256) {
-      const int l = tid >> 2, v = tid & 3;
-      const int c = q * kReq + (l & 15);
-      const int mm = t * kTileRows + 4 * (l >> 4) + v;
-      float sum = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWkWaves; ++w) sum += red[w][l][v];
-      if (c < b && mm < M) Y[(size_t)c * ldy + mm] = (half_t)sum;
+        for (int w = 0; w < kWkWaves; ++w) sum += part[(w * NT + q) * 64 + l][v];
+        if (c < b && mm < M) Y[(size_t)c * ldy + mm] = (half_t)sum;
+      }
+    }
+  } else {
+    // Request tile q: wait for its stage, contract it, and once every
+    // wavefront is done (the stage is then free) request tile q + 1's stage
+    // and sum tile q's eight wavefront partials in wavefront order.  The
+    // partials area is rewritten only after the next tile's first barrier,
+    // which every thread passes only once its sums are done.
+    for (int q = 0; q < nq; ++q) {
+      // the stage's loads land in LDS: wait for this wavefront's, then for
+      // every wavefront's
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      // every B operand of the request tile is read before the products, so the
+      // LDS latency is paid once rather than before each product
+      half8 bq[kMfBlocks];
+  #pragma unroll
+      for (int n = 0; n < kMfBlocks; ++n) bq[n] = __builtin_bit_cast(half8, xs[wk_slot(r, g, n)]);
+      floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int n = 0; n < kMfBlocks; ++n)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[n], bq[n], acc, 0, 0, 0);
+      // lane (c, h) holds rows 4h .. 4h+3 for request 16q + c
+      red[wave][lane] = acc;
+      __syncthreads();
+      if (q + 1 < nq) stage_x(q + 1);
+      if (tid < 256) {
+        const int l = tid >> 2, v = tid & 3;
+        const int c = q * kReq + (l & 15);
+        const int mm = t * kTileRows + 4 * (l >> 4) + v;
+        float sum = 0.f;
+  #pragma unroll
+        for (int w = 0; w < kWkWaves; ++w) sum += red[w][l][v];
+        if (c < b && mm < M) Y[(size_t)c * ldy + mm] = (half_t)sum;
+      }
     }
   }
   asm volatile("" ::"v"(touch));
@@ -1053,17 +1098,28 @@ hipError_t launch_gemm_mfma(const uint32_t *bits, int M, int K, int p, const voi
     return hipGetLastError();
   }
   if (use_wkx(M, K, b, p_req != nullptr)) {
+    // up to 64 requests: the request tiles unrolled, partials summed once;
+    // more: a loop over request tiles, each tile's partials summed in turn
     const dim3 grid(MT), block(64 * kWkWaves);  // MT <= kMfSlots: one tile per workgroup
+    const int nt = b <= kMfMaxBatch ? NT : 0;
+#define BCQ_WKX(PV)                                                                          \
+  switch (nt) {                                                                              \
+    case 2: hipLaunchKernelGGL((gemm_wkx_kernel<PV, 2>), grid, block, 0, s, b4, a, z, X, ldx, \
+                               b, Y, ldy, M, G, MT); break;                                  \
+    case 3: hipLaunchKernelGGL((gemm_wkx_kernel<PV, 3>), grid, block, 0, s, b4, a, z, X, ldx, \
+                               b, Y, ldy, M, G, MT); break;                                  \
+    case 4: hipLaunchKernelGGL((gemm_wkx_kernel<PV, 4>), grid, block, 0, s, b4, a, z, X, ldx, \
+                               b, Y, ldy, M, G, MT); break;                                  \
+    default: hipLaunchKernelGGL((gemm_wkx_kernel<PV, 0>), grid, block, 0, s, b4, a, z, X, ldx, \
+                                b, Y, ldy, M, G, MT); break;                                 \
+  }
     switch (p) {
-      case 1: hipLaunchKernelGGL((gemm_wkx_kernel<1>), grid, block, 0, s, b4, a, z, X, ldx, b, Y,
-                                 ldy, M, G, MT); break;
-      case 2: hipLaunchKernelGGL((gemm_wkx_kernel<2>), grid, block, 0, s, b4, a, z, X, ldx, b, Y,
-                                 ldy, M, G, MT); break;
-      case 3: hipLaunchKernelGGL((gemm_wkx_kernel<3>), grid, block, 0, s, b4, a, z, X, ldx, b, Y,
-                                 ldy, M, G, MT); break;
-      default: hipLaunchKernelGGL((gemm_wkx_kernel<4>), grid, block, 0, s, b4, a, z, X, ldx, b,
-                                  Y, ldy, M, G, MT); break;
+      case 1: BCQ_WKX(1); break;
+      case 2: BCQ_WKX(2); break;
+      case 3: BCQ_WKX(3); break;
+      default: BCQ_WKX(4); break;
     }
+#undef BCQ_WKX
     return hipGetLastError();
   }
   const int W = mf_waves(NT);
