@@ -23,7 +23,7 @@ initialisation, 20 rounds):
    scales of precision p + 1 (all of them, and the offset) are refit by least
    squares.  Each precision keeps its own table.
 
-Readings where the pages leave a step open (each also listed in the design doc):
+Readings where the pages leave a step open:
   * sign(0) = +1 (a residual of exactly zero gets a +1 plane entry).
   * Greedy initialisation with an offset: the offset starts at the group mean
     and the greedy planes fit the centred weights.
