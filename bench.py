@@ -647,7 +647,8 @@ def cpu_baseline(w, budget_s: float):
         return reps, nbytes, time.perf_counter() - t0
 
     reps1, b1, t1 = run(lambda p: oracle.gemv(w.signs, w.alpha, w.zero, w.x[0], p), budget_s / 2)
-    # the GPU machine gives one GPU's job 16 cores whatever the host reports
+    # at most 16 threads: the core share of one GPU's job on the measured host, whatever
+    # os.cpu_count() reports
     nthreads = max(1, min(16, os.cpu_count() or 1))
     bounds = np.linspace(0, w.M, nthreads + 1).astype(int)
     parts = [(np.ascontiguousarray(w.signs[:, lo:hi]), np.ascontiguousarray(w.alpha[:, lo:hi]),
